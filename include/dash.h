@@ -1,0 +1,150 @@
+/*
+ * dash.h -- C ABI of the MI355X (gfx950) DashAttention forward library (libdash.so).
+ *
+ * The method (arXiv 2605.18753, "DashAttention: Differentiable and Adaptive Sparse
+ * Hierarchical Attention"), as summarised on gist.science ("Technische Zusammenfassung",
+ * "Methodik"), the aixai.ru blog ("Трёхстадийная архитектура") and the liuzhao09 reading
+ * note (section 2, "核心方法"):
+ *   Stage 0  every complete 64-token chunk of keys is summarised by a scaled dot-product
+ *            attention of a learned per-head query (head_cls) over the chunk's keys;
+ *   Stage 1  each query scores the chunk summaries and alpha-entmax(gamma * scores) gives a
+ *            sparse block distribution; the distributions of the query heads that share a
+ *            KV head are averaged into one shared support, packed as a bit mask in 64-bit
+ *            words;
+ *   Stage 2  token-level softmax attention over the active chunks only, with the Stage 1
+ *            block weight entering the token logits as a log-prior, plus the query's own
+ *            (diagonal) chunk, which has no summary yet.
+ * The interface -- queries, keys, values, a per-head classification vector head_cls,
+ * chunk_size, estimate_diagonal, enable_gqa and an optional active_blocks mask -- follows
+ * the aiexpert.news article on the authors' release (paragraph on the Triton package).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers unless stated; tensors are dense, row-major,
+ *     with the shapes given below; they must be 16-byte aligned.  The caller owns all
+ *     memory; the library never allocates device memory and keeps no state besides the
+ *     loaded kernels and a thread-local error string.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without waiting.  Arguments are validated on the host first; on any
+ *     failure nothing is launched and a negative dash_status is returned, with a message
+ *     in dash_last_error().  Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - kv(h) = h / (Hq / Hkv): consecutive query heads share a KV head (enable_gqa).
+ *   - Only complete chunks are summarised.  Row t routes over chunks c < t / C and always
+ *     attends causally inside its own chunk with log-prior 0 (estimate_diagonal = 0).
+ */
+#ifndef DASH_H_
+#define DASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad alpha/gamma/scale, T <= 0 */
+  DASH_ERR_SHAPE = -2,       /* head counts inconsistent, sizes too large */
+  DASH_ERR_DTYPE = -3,       /* unknown dtype */
+  DASH_ERR_UNSUPPORTED = -4, /* valid per the method, not built here (D, C, G, flags) */
+  DASH_ERR_WORKSPACE = -5,   /* workspace pointer null or smaller than required */
+  DASH_ERR_HIP = -6          /* a HIP runtime call or launch failed */
+} dash_status;
+
+typedef enum { DASH_BF16 = 0, DASH_FP32 = 1 } dash_dtype;
+
+typedef struct dash_params {
+  int32_t B;          /* batch */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* key/value heads; Hq % Hkv == 0 */
+  int32_t T;          /* prefill: sequence length; decode/append: cache capacity T_max */
+  int32_t D;          /* head dim: 64 or 128 */
+  int32_t chunk_size; /* tokens per chunk: 64 (the only size the pages use) */
+  float alpha;        /* entmax alpha, finite and > 1; 1.5 at inference */
+  float gamma;        /* Stage 1 logit factor (the "Stage 1 factor"), finite > 0 */
+  float sm_scale;     /* logit scale of Stages 0-2; <= 0 selects 1/sqrt(D) */
+  int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
+  int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
+  int32_t estimate_diagonal; /* must be 0: the diagonal chunk is always kept at prior 1 */
+} dash_params;
+
+/* Version of this ABI (major * 100 + minor). */
+int dash_abi_version(void);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* dash_last_error(void);
+
+/* ---------------------------------------------------------------------------------
+ * Causal prefill (all three stages).
+ *   q        [B, Hq, T, D]   dtype
+ *   k, v     [B, Hkv, T, D]  dtype
+ *   head_cls [Hkv, D]        dtype   (one classifier query per KV head)
+ *   out      [B, Hq, T, D]   dtype   written
+ * Optional outputs (NULL = not wanted):
+ *   active_blocks [B, Hkv, T, W] uint64, W = ceil(ceil(T/C) / 64): bit (c % 64) of word
+ *                 c / 64 is set iff the head-averaged weight of chunk c for row t is > 0
+ *                 (LSB first).  Bits for c >= t / C are 0.
+ *   block_weights [B, Hkv, T, ceil(T/C)] float32: the head-averaged entmax weights,
+ *                 0 where inactive (debug/analysis; costs a full clear).
+ *   summary_out   [B, Hkv, ceil(T/C), D] float32: Stage 0 summaries of every complete
+ *                 chunk (a partial last chunk is left untouched); lets decode continue.
+ * workspace: device buffer of at least dash_prefill_workspace_size() bytes, 256-byte
+ * aligned, not shared with a concurrent call.
+ * ------------------------------------------------------------------------------- */
+int dash_prefill_workspace_size(const dash_params* p, size_t* bytes);
+int dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
+                 const void* head_cls, void* out, uint64_t* active_blocks,
+                 float* block_weights, float* summary_out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * One incremental decoding step (one new token per sequence).
+ *   p->T          cache capacity T_max
+ *   q             [B, Hq, D]            dtype, the new token's queries
+ *   k_cache, v_cache [B, Hkv, T_max, D] dtype, holding seq_lens[b] valid tokens, the new
+ *                 token included (the caller writes it at index seq_lens[b] - 1 first)
+ *   seq_lens      [B] int32 (device): 1 <= seq_lens[b] <= T_max
+ *   summary_cache [B, Hkv, ceil(T_max/C), D] float32 holding the summaries of every
+ *                 chunk c < (seq_lens[b] - 1) / C (see dash_append_chunk)
+ *   out           [B, Hq, D] dtype written
+ *   active_blocks optional [B, Hkv, W] uint64, W = ceil(ceil(T_max/C) / 64)
+ * The query sits at t = seq_lens[b] - 1: decode row t equals prefill row t of the same
+ * sequence.  A sequence whose seq_lens entry is out of range gets NaN outputs and no
+ * memory outside its cache rows is touched.
+ * ------------------------------------------------------------------------------- */
+int dash_decode_workspace_size(const dash_params* p, size_t* bytes);
+int dash_decode(const dash_params* p, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* seq_lens, const float* summary_cache,
+                void* out, uint64_t* active_blocks, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Chunk-summary cache append.  A summary, once its chunk is complete, is frozen and
+ * cached (gist.science, "Stufe 0", efficiency remark): for each b this summarises every
+ * chunk c with n_summarized[b] <= c < seq_lens[b] / C into summary_cache and then sets
+ * n_summarized[b] = max(n_summarized[b], seq_lens[b] / C).  Call it after a decode step
+ * whose token completed a chunk, and once to build the cache of a prompt.
+ *   k_cache [B, Hkv, T_max, D] dtype; head_cls [Hkv, D] dtype;
+ *   seq_lens [B] int32 (device); summary_cache [B, Hkv, ceil(T_max/C), D] float32;
+ *   n_summarized [B] int32 (device, in/out).
+ * ------------------------------------------------------------------------------- */
+int dash_append_chunk(const dash_params* p, const void* k_cache, const void* head_cls,
+                      const int32_t* seq_lens, float* summary_cache,
+                      int32_t* n_summarized, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Dense causal softmax attention with the same layout (the comparator the pages time
+ * against: FlashAttention-3 in their Table 5).  Uses p->B, Hq, Hkv, T, D, sm_scale,
+ * enable_gqa, dtype (bf16 only).
+ *   q [B, Hq, T, D], k, v [B, Hkv, T, D], out [B, Hq, T, D].
+ * ------------------------------------------------------------------------------- */
+int dash_dense_causal_workspace_size(const dash_params* p, size_t* bytes);
+int dash_dense_causal(const dash_params* p, const void* q, const void* k, const void* v,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H_ */

@@ -1,0 +1,397 @@
+// C ABI of libdash: argument validation, workspace planning and kernel dispatch.
+//
+// Validation is plain host C++ and runs before any HIP call, so every error path can be
+// exercised without a GPU.  The library owns no device memory: callers pass workspaces
+// sized by the *_workspace_size() queries.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dash.h"
+#include "dash_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DASH_OK;
+}
+
+constexpr int kMaxT = dash::kChunk * (dash::kMaxRouted + 1);
+
+struct Dims {
+  int B, Hq, Hkv, T, D, G, nc, nfull, W;
+  float scale, alpha, gamma;
+  int dtype;
+  size_t es;
+};
+
+int check_params(const dash_params* p, Dims* d, bool need_bf16 = false) {
+  if (!p) return fail(DASH_ERR_INVALID_ARG, "params is NULL");
+  if (p->dtype != DASH_BF16 && p->dtype != DASH_FP32)
+    return fail(DASH_ERR_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0)
+    return fail(DASH_ERR_INVALID_ARG, "B, Hq, Hkv must be positive (got %d, %d, %d)", p->B,
+                p->Hq, p->Hkv);
+  if (p->T <= 0) return fail(DASH_ERR_INVALID_ARG, "T must be positive (got %d)", p->T);
+  if (p->Hq % p->Hkv != 0)
+    return fail(DASH_ERR_SHAPE, "Hq (%d) is not a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!p->enable_gqa && p->Hq != p->Hkv)
+    return fail(DASH_ERR_SHAPE, "Hq != Hkv needs enable_gqa");
+  const int G = p->Hq / p->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(DASH_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", G);
+  if (p->D != 64 && p->D != 128)
+    return fail(DASH_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", p->D);
+  if (p->chunk_size != dash::kChunk)
+    return fail(DASH_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", p->chunk_size);
+  if (!(p->alpha > 1.0f) || !std::isfinite(p->alpha))
+    return fail(DASH_ERR_INVALID_ARG, "alpha must be finite and > 1");
+  if (!(p->gamma > 0.0f) || !std::isfinite(p->gamma))
+    return fail(DASH_ERR_INVALID_ARG, "gamma must be finite and > 0");
+  if (!std::isfinite(p->sm_scale)) return fail(DASH_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (p->estimate_diagonal != 0)
+    return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is not built");
+  if (p->T > kMaxT)
+    return fail(DASH_ERR_UNSUPPORTED, "T=%d exceeds %d (at most %d routed chunks per row)", p->T,
+                kMaxT, dash::kMaxRouted);
+  if (need_bf16 && p->dtype != DASH_BF16) return fail(DASH_ERR_DTYPE, "this entry point is bf16 only");
+  d->B = p->B;
+  d->Hq = p->Hq;
+  d->Hkv = p->Hkv;
+  d->T = p->T;
+  d->D = p->D;
+  d->G = G;
+  d->nc = (p->T + dash::kChunk - 1) / dash::kChunk;
+  d->nfull = p->T / dash::kChunk;
+  d->W = (d->nc + 63) / 64;
+  d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt((float)p->D);
+  d->alpha = p->alpha;
+  d->gamma = p->gamma;
+  d->dtype = p->dtype;
+  d->es = p->dtype == DASH_BF16 ? 2 : 4;
+  return DASH_OK;
+}
+
+int check_ptr(const void* ptr, const char* name, bool required = true) {
+  if (!ptr) return required ? fail(DASH_ERR_INVALID_ARG, "%s is NULL", name) : DASH_OK;
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+    return fail(DASH_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return DASH_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- prefill workspace
+struct PrefillLayout {
+  size_t summ, vt, mask, wbar, ctr, total;
+};
+
+PrefillLayout prefill_layout(const Dims& d) {
+  PrefillLayout L;
+  size_t off = 0;
+  L.summ = off;
+  off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
+  L.vt = off;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * d.nc * d.D * 64 * 2) : 0;
+  L.mask = off;
+  off += align256((size_t)d.B * d.Hkv * d.T * d.W * 8);
+  L.wbar = off;
+  off += align256((size_t)d.B * d.Hkv * d.T * d.nc * 4);
+  L.ctr = off;
+  off += 256;
+  L.total = off;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t mask, wbar, total;
+};
+
+DecodeLayout decode_layout(const Dims& d) {
+  DecodeLayout L;
+  size_t off = 0;
+  L.mask = off;
+  off += align256((size_t)d.B * d.Hkv * d.W * 8);
+  L.wbar = off;
+  off += align256((size_t)d.B * d.Hkv * d.nc * 4);
+  L.total = off;
+  return L;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return DASH_OK;
+  if (!ws) return fail(DASH_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(DASH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (have < need)
+    return fail(DASH_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
+  return DASH_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DASH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+__global__ void k_fill_f32(float* p, size_t n, float v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks == 0) return hipSuccess;
+  k_fill_f32<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dash_abi_version(void) { return 100; }
+
+const char* dash_last_error(void) { return g_err.c_str(); }
+
+int dash_prefill_workspace_size(const dash_params* p, size_t* bytes) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  if (!bytes) return fail(DASH_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = prefill_layout(d).total;
+  return ok();
+}
+
+int dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
+                 const void* head_cls, void* out, uint64_t* active_blocks,
+                 float* block_weights, float* summary_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(k, "k")) return rc;
+  if (int rc = check_ptr(v, "v")) return rc;
+  if (int rc = check_ptr(head_cls, "head_cls")) return rc;
+  if (int rc = check_ptr(out, "out")) return rc;
+  if (int rc = check_ptr(active_blocks, "active_blocks", false)) return rc;
+  if (int rc = check_ptr(block_weights, "block_weights", false)) return rc;
+  if (int rc = check_ptr(summary_out, "summary_out", false)) return rc;
+  const PrefillLayout L = prefill_layout(d);
+  if (int rc = check_ws(workspace, workspace_bytes, L.total)) return rc;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* summ = summary_out ? summary_out : reinterpret_cast<float*>(ws + L.summ);
+  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(ws + L.mask);
+  float* wbar = block_weights ? block_weights : reinterpret_cast<float*>(ws + L.wbar);
+  hipError_t e;
+
+  if (block_weights) {
+    if ((e = fill_f32(block_weights, (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess)
+      return hip_fail(e, "clearing block_weights");
+  }
+  if ((e = dash::launch_stage0(k, head_cls, summ, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull, nullptr,
+                               nullptr, d.scale, d.dtype, s)) != hipSuccess)
+    return hip_fail(e, "stage 0 launch");
+
+  dash::RouteArgs ra{};
+  ra.q = q;
+  ra.summ = summ;
+  ra.mask = mask;
+  ra.wbar = wbar;
+  ra.seq_lens = nullptr;
+  ra.B = d.B;
+  ra.Hq = d.Hq;
+  ra.Hkv = d.Hkv;
+  ra.D = d.D;
+  ra.Tq = d.T;
+  ra.rows = d.T;
+  ra.nc_alloc = d.nc;
+  ra.W = d.W;
+  ra.wbar_ld = d.nc;
+  ra.tcap = d.T;
+  ra.alpha = d.alpha;
+  ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
+  ra.dtype = d.dtype;
+  if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "stage 1 launch");
+
+  dash::AttendArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.vt = nullptr;
+  aa.mask = mask;
+  aa.wbar = wbar;
+  aa.out = out;
+  aa.seq_lens = nullptr;
+  aa.B = d.B;
+  aa.Hq = d.Hq;
+  aa.Hkv = d.Hkv;
+  aa.D = d.D;
+  aa.Tq = d.T;
+  aa.Tk = d.T;
+  aa.rows = d.T;
+  aa.W = d.W;
+  aa.wbar_ld = d.nc;
+  aa.nc = d.nc;
+  aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.dtype = d.dtype;
+  aa.dense = 0;
+  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "stage 2 launch");
+  return ok();
+}
+
+int dash_decode_workspace_size(const dash_params* p, size_t* bytes) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  if (!bytes) return fail(DASH_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decode_layout(d).total;
+  return ok();
+}
+
+int dash_decode(const dash_params* p, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, const float* summary_cache, void* out,
+                uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(k_cache, "k_cache")) return rc;
+  if (int rc = check_ptr(v_cache, "v_cache")) return rc;
+  if (!seq_lens) return fail(DASH_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (int rc = check_ptr(summary_cache, "summary_cache")) return rc;
+  if (int rc = check_ptr(out, "out")) return rc;
+  if (int rc = check_ptr(active_blocks, "active_blocks", false)) return rc;
+  const DecodeLayout L = decode_layout(d);
+  if (int rc = check_ws(workspace, workspace_bytes, L.total)) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint64_t* mask = active_blocks ? active_blocks : reinterpret_cast<uint64_t*>(ws + L.mask);
+  float* wbar = reinterpret_cast<float*>(ws + L.wbar);
+  hipError_t e;
+
+  dash::RouteArgs ra{};
+  ra.q = q;
+  ra.summ = summary_cache;
+  ra.mask = mask;
+  ra.wbar = wbar;
+  ra.seq_lens = seq_lens;
+  ra.B = d.B;
+  ra.Hq = d.Hq;
+  ra.Hkv = d.Hkv;
+  ra.D = d.D;
+  ra.Tq = 1;
+  ra.rows = 1;
+  ra.nc_alloc = d.nc;
+  ra.W = d.W;
+  ra.wbar_ld = d.nc;
+  ra.tcap = d.T;
+  ra.alpha = d.alpha;
+  ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
+  ra.dtype = d.dtype;
+  if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "decode route launch");
+
+  dash::AttendArgs aa{};
+  aa.q = q;
+  aa.k = k_cache;
+  aa.v = v_cache;
+  aa.mask = mask;
+  aa.wbar = wbar;
+  aa.out = out;
+  aa.seq_lens = seq_lens;
+  aa.B = d.B;
+  aa.Hq = d.Hq;
+  aa.Hkv = d.Hkv;
+  aa.D = d.D;
+  aa.Tq = 1;
+  aa.Tk = d.T;
+  aa.rows = 1;
+  aa.W = d.W;
+  aa.wbar_ld = d.nc;
+  aa.nc = d.nc;
+  aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.dtype = d.dtype;
+  aa.dense = 0;
+  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "decode attend launch");
+  return ok();
+}
+
+int dash_append_chunk(const dash_params* p, const void* k_cache, const void* head_cls,
+                      const int32_t* seq_lens, float* summary_cache, int32_t* n_summarized,
+                      void* stream) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  if (int rc = check_ptr(k_cache, "k_cache")) return rc;
+  if (int rc = check_ptr(head_cls, "head_cls")) return rc;
+  if (!seq_lens) return fail(DASH_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (int rc = check_ptr(summary_cache, "summary_cache")) return rc;
+  if (!n_summarized) return fail(DASH_ERR_INVALID_ARG, "n_summarized is NULL");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = dash::launch_stage0(k_cache, head_cls, summary_cache, d.B, d.Hkv, d.T, d.D, d.nc,
+                               d.nfull, n_summarized, seq_lens, d.scale, d.dtype, s)) != hipSuccess)
+    return hip_fail(e, "append launch");
+  if ((e = dash::launch_update_nsum(n_summarized, seq_lens, d.B, s)) != hipSuccess)
+    return hip_fail(e, "append bookkeeping launch");
+  return ok();
+}
+
+int dash_dense_causal_workspace_size(const dash_params* p, size_t* bytes) {
+  Dims d;
+  if (int rc = check_params(p, &d, true)) return rc;
+  if (!bytes) return fail(DASH_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = align256((size_t)d.B * d.Hkv * d.nc * d.D * 64 * 2) + 256;
+  return ok();
+}
+
+int dash_dense_causal(const dash_params* p, const void* q, const void* k, const void* v,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  if (int rc = check_params(p, &d, true)) return rc;
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(k, "k")) return rc;
+  if (int rc = check_ptr(v, "v")) return rc;
+  if (int rc = check_ptr(out, "out")) return rc;
+  size_t need = 0;
+  dash_dense_causal_workspace_size(p, &need);
+  if (int rc = check_ws(workspace, workspace_bytes, need)) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  dash::AttendArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.out = out;
+  aa.B = d.B;
+  aa.Hq = d.Hq;
+  aa.Hkv = d.Hkv;
+  aa.D = d.D;
+  aa.Tq = d.T;
+  aa.Tk = d.T;
+  aa.rows = d.T;
+  aa.W = d.W;
+  aa.wbar_ld = d.nc;
+  aa.nc = d.nc;
+  aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.dtype = d.dtype;
+  aa.dense = 1;
+  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "dense launch");
+  return ok();
+}
+
+}  // extern "C"

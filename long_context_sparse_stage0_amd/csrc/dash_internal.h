@@ -1,0 +1,88 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dash {
+
+constexpr int kChunk = 64;          // tokens per chunk (the pages' only chunk size)
+constexpr int kMaxRouted = 2048;    // routed chunks per row held in registers (32 per lane)
+constexpr int kMaxRoutedRegs = kMaxRouted / 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ device helpers
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ launch-side API
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+
+struct RouteArgs {
+  const void* q;          // [B, Hq, Tq, D]
+  const float* summ;      // [B, Hkv, nc_alloc, D]
+  uint64_t* mask;         // [B, Hkv, rows, W]
+  float* wbar;            // [B, Hkv, rows, wbar_ld] (written at set bits)
+  const int32_t* seq_lens;  // decode: query row = seq_lens[b] - 1; prefill: nullptr
+  int B, Hq, Hkv, D, Tq, rows, nc_alloc, W, wbar_ld;
+  int tcap;               // prefill: T; decode: cache capacity (a query row must be < tcap)
+  float alpha, zscale;    // zscale = (alpha - 1) * gamma * sm_scale
+  int dtype;
+};
+
+struct AttendArgs {
+  const void* q;          // [B, Hq, Tq, D]
+  const void* k;          // [B, Hkv, Tk, D]
+  const void* v;          // [B, Hkv, Tk, D]
+  const void* vt;         // bf16 chunk-transposed V [B, Hkv, nc, D, 64] (MFMA path)
+  const uint64_t* mask;   // [B, Hkv, rows, W]
+  const float* wbar;      // [B, Hkv, rows, wbar_ld]
+  void* out;              // [B, Hq, Tq, D]
+  const int32_t* seq_lens;
+  int B, Hq, Hkv, D, Tq, Tk, rows, W, wbar_ld, nc;
+  float scale_log2;       // sm_scale * log2(e)
+  int dtype;
+  int dense;              // 1: every chunk c < i_t active with prior 1 (comparator)
+};
+
+hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, int B, int Hkv,
+                         int T_stride, int D, int nc_alloc, int n_full,
+                         const int32_t* lo_b, const int32_t* seq_lens, float scale,
+                         int dtype, hipStream_t s);
+hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
+                              hipStream_t s);
+hipError_t launch_vtranspose(const void* v, void* vt, int B, int Hkv, int T, int D, int nc,
+                             hipStream_t s);
+hipError_t launch_route_valu(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_mfma(const RouteArgs& a, hipStream_t s);
+hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s);
+
+}  // namespace dash

@@ -1,0 +1,123 @@
+// alpha-entmax threshold solver shared by the Stage 1 kernels.
+//
+// alpha-entmax (Peters, Niculae and Martins 2019; used for chunk routing in arXiv
+// 2605.18753, gist.science "Stufe 1: Entmax-Chunk-Routing"):
+//   p_c = [y_c - tau]_+^(1/(alpha-1)),  y = (alpha-1) * gamma * s * <q, k_bar_c>,
+//   tau fixed by sum_c p_c = 1.
+// F(tau) = sum_c [y_c - tau]_+^(1/(alpha-1)) - 1 is convex and decreasing, and
+// tau* lies in [max y - 1, max y - n^(1-alpha)].
+//
+// Solver (own design): start at the left end tau_0 = max y - 1 (F >= 0) and step right,
+// never past tau*, so the current support S = {y > tau} always contains the true one.
+// Each pass reduces, over S, the count, sum d, sum d^2 (or the needed powers) and the
+// smallest d = y - tau; from these:
+//   alpha = 2  : the root of the linear piece, delta = (sum d - 1)/|S|; exact and final
+//                if delta < min d, otherwise a Newton step (which it equals).
+//   alpha = 1.5: the smaller root of |S| delta^2 - 2 delta sum d + sum d^2 - 1 = 0 is the
+//                exact answer if it stays below min d (the support does not change);
+//                otherwise tau* > tau + min d, and the step is max(Newton, min d).
+//   other alpha: safeguarded Newton steps until the step is below fp32 resolution.
+// Every step is a valid lower bound (Newton from the left on a convex function, or a
+// point where F is still positive), so the iteration is monotone and each pass that does
+// not finish drops at least one element.
+#pragma once
+#include "dash_internal.h"
+
+namespace dash {
+
+enum { kAlphaGeneral = 0, kAlpha15 = 1, kAlpha2 = 2 };
+
+__device__ __forceinline__ float pow_pos(float d, float e) {  // d > 0
+  return fast_exp2(e * fast_log2(d));
+}
+
+// Cross-lane reduction hooks: the generic kernel reduces over a whole wave; the MFMA
+// kernel supplies its own combination over lanes and waves.
+struct WaveReduce {
+  __device__ __forceinline__ float sum(float v) const { return wave_sum(v); }
+  __device__ __forceinline__ float min(float v) const { return wave_min(v); }
+  __device__ __forceinline__ float max(float v) const { return wave_max(v); }
+};
+
+// y[NR]: this lane's scores ((alpha-1)-scaled), -inf for absent entries.
+// Returns tau; *zsum receives sum_c [y_c - tau]_+^(1/(alpha-1)) (the normaliser).
+template <int MODE, int NR, class Red>
+__device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, const Red& red,
+                                  float* zsum) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) m = fmaxf(m, y[r]);
+  m = red.max(m);
+  float tau = m - 1.0f;
+  const float inv = 1.0f / (alpha - 1.0f);
+  const float hi = m - ((MODE == kAlpha15) ? rsqrtf((float)n)
+                                            : (MODE == kAlpha2 ? 1.0f / (float)n
+                                                               : pow_pos((float)n, 1.0f - alpha)));
+  for (int it = 0; it < 96; ++it) {
+    float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float d = y[r] - tau;
+      if (d > 0.f) {
+        cnt += 1.f;
+        mn = fminf(mn, d);
+        if (MODE == kAlpha15) {
+          s1 += d;
+          s2 = fmaf(d, d, s2);
+        } else if (MODE == kAlpha2) {
+          s1 += d;
+        } else {
+          const float dp1 = pow_pos(d, inv - 1.0f);  // d^(p-1)
+          s1 += dp1;                                 // for F'
+          s2 = fmaf(dp1, d, s2);                     // d^p, for F
+        }
+      }
+    }
+    cnt = red.sum(cnt);
+    s1 = red.sum(s1);
+    if (MODE != kAlpha2) s2 = red.sum(s2);
+    mn = red.min(mn);
+    if (MODE == kAlpha2) {
+      const float delta = (s1 - 1.0f) / cnt;
+      if (delta < mn) {
+        tau += delta;
+        break;
+      }
+      tau = fminf(tau + fmaxf(delta, mn), hi);
+    } else if (MODE == kAlpha15) {
+      const float F = s2 - 1.0f;
+      const float disc = fmaf(s1, s1, -cnt * F);
+      if (disc >= 0.f) {
+        const float delta = (s1 - sqrtf(disc)) / cnt;
+        if (delta < mn) {
+          tau += fmaxf(delta, 0.f);
+          break;
+        }
+      }
+      tau = fminf(tau + fmaxf(F / (2.0f * s1), mn), hi);
+    } else {
+      const float F = s2 - 1.0f;
+      const float step = F / (inv * s1);
+      tau = fminf(tau + fmaxf(step, 0.f), hi);
+      if (step <= 3e-7f * fmaxf(1.0f, fabsf(tau))) break;
+    }
+  }
+  float z = 0.f;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float d = y[r] - tau;
+    if (d > 0.f) z += (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
+  }
+  *zsum = red.sum(z);
+  return tau;
+}
+
+template <int MODE>
+__device__ __forceinline__ float entmax_weight(float y, float tau, float inv, float rz) {
+  const float d = y - tau;
+  if (!(d > 0.f)) return 0.f;
+  const float p = (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
+  return p * rz;
+}
+
+}  // namespace dash

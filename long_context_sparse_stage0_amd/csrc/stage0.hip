@@ -1,0 +1,164 @@
+// Stage 0: chunk summaries, and the chunk-transposed copy of V used by the MFMA Stage 2.
+//
+// Method (gist.science summary of arXiv 2605.18753, "Stufe 0: Lokale
+// Chunk-Zusammenfassung"; aixai.ru blog, "Трёхстадийная архитектура"): a learned query
+// attends by scaled dot-product attention over the 64 keys of a chunk; the attention-
+// weighted key is the chunk's summary.  Once a chunk is complete its summary is frozen.
+//
+// Kernel shape: one 64-lane wave per (b, kv head, chunk).  A chunk of K is one
+// contiguous 64 x D block (16 KiB at D = 128 bf16), read row by row so that each row is
+// one fully coalesced 256-byte wave load; lane l owns columns [l*E, l*E + E), E = D/64.
+// The 64 partial dot products of a lane are reduced across lanes through a padded LDS
+// tile (lane j ends up with logit a_j), softmax runs across lanes, and the weighted sum
+// of the rows (still in registers) is accumulated per lane in fp32.  HBM-bound: K is
+// read once, fp32 summaries are written once.
+#include "dash_internal.h"
+
+namespace dash {
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
+                                               const TIn* __restrict__ head_cls,
+                                               float* __restrict__ summ, int Hkv,
+                                               int T_stride, int nc_alloc, int n_full,
+                                               const int32_t* __restrict__ lo_b,
+                                               const int32_t* __restrict__ seq_lens,
+                                               float scale_log2) {
+  constexpr int E = D / 64;
+  __shared__ float red[64][65];
+  __shared__ float pis[64];
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  int lo = 0, hi = n_full;
+  if (seq_lens != nullptr) {
+    int sl = seq_lens[b];
+    sl = sl < 0 ? 0 : (sl > T_stride ? T_stride : sl);
+    hi = sl / kChunk;
+    lo = lo_b ? lo_b[b] : 0;
+    if (lo < 0) lo = 0;
+  }
+  float h[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) h[e] = to_f32(head_cls[kvh * D + lane * E + e]) * scale_log2;
+
+  for (int c = lo + blockIdx.x; c < hi; c += gridDim.x) {
+    const TIn* kc = k + ((size_t)(b * Hkv + kvh) * T_stride + (size_t)c * kChunk) * D;
+    float kr[64][E];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kr[j][e] = to_f32(kc[j * D + lane * E + e]);
+        part += h[e] * kr[j][e];
+      }
+      red[j][lane] = part;
+    }
+    __syncthreads();
+    float a = 0.f;  // logit of key `lane`, in log2 units
+    for (int i = 0; i < 64; ++i) a += red[lane][i];
+    const float m = wave_max(a);
+    const float p = fast_exp2(a - m);
+    const float s = wave_sum(p);
+    pis[lane] = p / s;
+    __syncthreads();
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const float pj = pis[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += pj * kr[j][e];
+    }
+    float* o = summ + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = acc[e];
+    __syncthreads();
+  }
+}
+
+__global__ void k_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    int n = seq_lens[b] / kChunk;
+    if (n > n_summarized[b]) n_summarized[b] = n;
+  }
+}
+
+// V [B, Hkv, T, D] -> vt [B, Hkv, nc, D, 64]: each chunk becomes a D x 64 tile whose rows
+// are 64 consecutive keys of one column; rows of a partial last chunk are zero-filled.
+template <int D>
+__global__ __launch_bounds__(256) void k_vtranspose(const uint16_t* __restrict__ v,
+                                                    uint16_t* __restrict__ vt, int Hkv, int T,
+                                                    int nc) {
+  __shared__ uint16_t tile[64][D + 2];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const uint16_t* src = v + ((size_t)(b * Hkv + kvh) * T + (size_t)c * kChunk) * D;
+  constexpr int SEGS = 64 * D / 8;
+  for (int seg = tid; seg < SEGS; seg += 256) {
+    const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (c * kChunk + row < T) val = *reinterpret_cast<const uint4*>(src + row * D + col);
+    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&val);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[row][col + i] = pv[i];
+  }
+  __syncthreads();
+  uint16_t* dst = vt + ((size_t)(b * Hkv + kvh) * nc + c) * (size_t)D * 64;
+  for (int seg = tid; seg < D * 8; seg += 256) {
+    const int d = seg / 8, j0 = (seg % 8) * 8;
+    uint4 val;
+    uint16_t* pv = reinterpret_cast<uint16_t*>(&val);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = tile[j0 + i][d];
+    *reinterpret_cast<uint4*>(dst + d * 64 + j0) = val;
+  }
+}
+
+hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, int B, int Hkv,
+                         int T_stride, int D, int nc_alloc, int n_full,
+                         const int32_t* lo_b, const int32_t* seq_lens, float scale,
+                         int dtype, hipStream_t s) {
+  const float sl2 = scale * 1.4426950408889634f;
+  int gx = seq_lens ? 64 : n_full;
+  if (gx < 1) gx = 1;
+  dim3 grid(gx, Hkv, B);
+  if (dtype == 0) {
+    if (D == 128)
+      k_stage0<bf16, 128><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, Hkv,
+                                              T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
+    else
+      k_stage0<bf16, 64><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, Hkv,
+                                             T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
+  } else {
+    if (D == 128)
+      k_stage0<float, 128><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
+                                               Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
+                                               sl2);
+    else
+      k_stage0<float, 64><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
+                                              Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
+                                              sl2);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
+                              hipStream_t s) {
+  k_update_nsum<<<(B + 63) / 64, 64, 0, s>>>(n_summarized, seq_lens, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_vtranspose(const void* v, void* vt, int B, int Hkv, int T, int D, int nc,
+                             hipStream_t s) {
+  dim3 grid(nc, Hkv, B);
+  if (D == 128)
+    k_vtranspose<128><<<grid, 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vt, Hkv, T, nc);
+  else
+    k_vtranspose<64><<<grid, 256, 0, s>>>((const uint16_t*)v, (uint16_t*)vt, Hkv, T, nc);
+  return hipGetLastError();
+}
+
+}  // namespace dash

@@ -1,0 +1,66 @@
+"""Helpers shared by the GPU parity tests: upload seeded inputs, run the oracle, and
+compare with the tolerances of the method's parity bar:
+  out           max-abs <= 2e-2 (bf16) / 1e-4 (fp32)
+  block weights max-abs <= 1e-3
+  active mask   bit-exact, except bits whose oracle group margin |max_h (y - tau)| <= 1e-4
+"""
+import sys
+
+import numpy as np
+
+OUT_TOL = {"bf16": 2e-2, "fp32": 1e-4}
+W_TOL = 1e-3
+MARGIN = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+    return t.cuda()
+
+
+def unpack_words(words, nc):
+    """int64 words [..., W] -> bool [..., nc] with bit c % 64 of word c // 64 (LSB first)."""
+    w = np.ascontiguousarray(words).view(np.uint64)
+    bits = ((w[..., :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+    return bits.reshape(*w.shape[:-1], -1)[..., :nc]
+
+
+def compare_mask(gpu_bits, oracle_mask, oracle_margin, rows):
+    """gpu_bits/oracle_* indexed [..., r, c]; only routed chunks c < t // 64 are compared;
+    every bit beyond must be 0 on the GPU."""
+    bad = 0
+    ambiguous = 0
+    for r, t in enumerate(rows):
+        it = int(t) // 64
+        g = gpu_bits[..., r, :]
+        assert not g[..., it:].any(), f"row {t}: bits set at or beyond the own chunk"
+        if it == 0:
+            continue
+        om = oracle_mask[..., r, :it]
+        mg = oracle_margin[..., r, :it]
+        diff = g[..., :it] != om
+        near = np.abs(mg) <= MARGIN
+        ambiguous += int((diff & near).sum())
+        bad += int((diff & ~near).sum())
+    assert bad == 0, f"{bad} mask bits differ outside the 1e-4 margin ({ambiguous} inside)"
+    return ambiguous
+
+
+def compare_out(gpu, ref, dtype, what="out"):
+    err = float(np.nanmax(np.abs(gpu.astype(np.float64) - ref)))
+    assert np.isfinite(gpu).all(), f"{what}: non-finite values"
+    assert err <= OUT_TOL[dtype], f"{what}: max-abs error {err:.3e} > {OUT_TOL[dtype]}"
+    return err
+
+
+def compare_weights(gpu_w, ref_w):
+    err = float(np.abs(gpu_w.astype(np.float64) - ref_w).max()) if gpu_w.size else 0.0
+    assert err <= W_TOL, f"block weights: max-abs error {err:.3e} > {W_TOL}"
+    return err
