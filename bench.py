@@ -1,0 +1,315 @@
+#!/usr/bin/env python
+"""Benchmark of the DashAttention forward pass on one MI355X.
+
+Prints ONE JSON line on stdout:
+  value      prefill tokens/s on the 128K workload (B=1, 32 query / 2 KV heads, D=128,
+             bf16, alpha=1.5, planted needles calibrated to ~75% zero routing weight);
+             one step = one full causal prefill (Stage 0 + Stage 1 + Stage 2), inputs
+             resident in HBM;
+  roofline   Stage 2 (the dominant kernel) against the bf16 dense MFMA peak, with
+             algorithmic flops  sum_{b,kvh,t} G * 4 D * (64 * popcount(mask_t) + t % 64 + 1);
+  decode     the 64K decode workload (B=16, 256 steps, summary appended when a chunk fills):
+             us/step against the HBM roofline of its algorithmic bytes;
+  dense      a dense causal flash-style kernel on the same inputs (the pages' comparator);
+  cpu_baseline  the float64 oracle timed on host cores over a bounded sample of rows.
+Progress lines go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s @128K + decode us/token @64K, bf16; % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stage2_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def popcount64(x):
+    """Popcount of int64 tensors (two 32-bit halves, SWAR)."""
+    import torch
+    out = torch.zeros_like(x)
+    for half in (x & 0xFFFFFFFF, (x >> 32) & 0xFFFFFFFF):
+        v = half - ((half >> 1) & 0x55555555)
+        v = (v & 0x33333333) + ((v >> 2) & 0x33333333)
+        v = (v + (v >> 4)) & 0x0F0F0F0F
+        out += (v * 0x01010101 & 0xFFFFFFFF) >> 24
+    return out
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def bench_prefill(args, w, dash, torch):
+    from long_context_sparse_stage0_amd import synth
+    t0 = time.time()
+    x = synth.prefill_inputs(w)
+    log(f"generated {w.name} inputs in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    q, k, v, hc = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev)
+                   for n in ("q", "k", "v", "head_cls"))
+    B, Hq, T, D = q.shape
+    Hkv, G = w.Hkv, w.G
+    nc = -(-T // 64)
+    W = -(-nc // 64)
+    out = torch.empty_like(q)
+    ab = torch.empty((B, Hkv, T, W), dtype=torch.int64, device=dev)
+    p = dash.make_params(B, Hq, Hkv, T, D, alpha=w.alpha, gamma=w.gamma, enable_gqa=True,
+                         dtype=torch.bfloat16)
+    ws = dash.alloc_workspace(dash.workspace_size("prefill", p), dev)
+    kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=True, workspace=ws)
+
+    # one untimed pass returning the mask, for the sparsity and the algorithmic flops
+    dash.prefill(q, k, v, hc, out=out, **kw)
+    dash.prefill_stage(1, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                       enable_gqa=True, active_blocks=ab)
+    torch.cuda.synchronize()
+    pc = popcount64(ab).sum(dim=-1)                       # [B, Hkv, T] active chunks per row
+    t_idx = torch.arange(T, device=dev)
+    routed = (t_idx // 64).to(torch.float64)
+    active = pc.to(torch.float64)
+    zero_frac = 1.0 - float(active.sum() / (routed.sum() * B * Hkv))
+    diag = (t_idx % 64 + 1).to(torch.float64)
+    flops2 = float(G * 4 * D * (64.0 * active.sum() + B * Hkv * diag.sum()))
+    # executed work of the union walk: R rows per workgroup share the union of their masks
+    R = min(64, 256 // G) if G >= 4 else 64
+    abr = ab.view(B, Hkv, T // R, R, W) if T % R == 0 else None
+    union_flops = None
+    if abr is not None:
+        u = abr[:, :, :, 0].clone()
+        for r in range(1, R):
+            u |= abr[:, :, :, r]
+        upc = popcount64(u).sum(dim=-1).to(torch.float64)  # [B, Hkv, T/R]
+        union_flops = float(R * G * 4 * D * 64.0 * upc.sum() + G * 4 * D * B * Hkv * 64.0 * T)
+    flops_dense = float(B * Hq * 4 * D * T * (T + 1) / 2)
+    log(f"zero-weight fraction {zero_frac:.4f}; stage-2 algorithmic flops {flops2:.3e}")
+    del pc, active
+
+    def step(evs=None):
+        for s in range(3):
+            dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                               enable_gqa=True)
+            if evs is not None:
+                evs[s + 1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    st = [float(np.mean([ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(args.steps)]))
+          for s in range(3)]
+    log(f"prefill {ms:.2f} ms/step; stages {st[0]:.3f} / {st[1]:.3f} / {st[2]:.3f} ms")
+    tokens_s = B * T / (ms / 1e3)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        src = os.path.join(ROOT, "long_context_sparse_stage0_amd", "csrc", "attend_mfma.hip")
+        if tf.get("source_sha256_16") == source_hash(src) and tf.get("workload") == w.name:
+            traffic = tf.get("bytes_per_launch")
+    achieved = flops2 / (st[2] / 1e3) / 1e12
+    roof = {"bound": "mfma", "kernel": "k_attend_mfma (Stage 2)", "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic, "algorithmic_flops_per_launch": flops2,
+            "executed_union_flops_per_launch": union_flops,
+            "kernel_ms": st[2]}
+    res = dict(ms=ms, tokens_s=tokens_s, stages_ms=st, roofline=roof, zero_frac=zero_frac,
+               flops2=flops2, flops_dense=flops_dense, x=x)
+
+    if not args.no_dense:
+        pd = dash.make_params(B, Hq, Hkv, T, D, enable_gqa=True, dtype=torch.bfloat16)
+        wsd = dash.alloc_workspace(dash.workspace_size("dense", pd), dev)
+        dash.dense_causal(q, k, v, enable_gqa=True, out=out, workspace=wsd)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nd = max(1, min(args.steps, 3))
+        e0.record()
+        for _ in range(nd):
+            dash.dense_causal(q, k, v, enable_gqa=True, out=out, workspace=wsd)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / nd
+        res["dense"] = {"ms_per_call": dms, "tflops": flops_dense / (dms / 1e3) / 1e12,
+                        "frac_of_peak": flops_dense / (dms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "speedup_sparse_over_dense": dms / ms,
+                        "speedup_stage2_over_dense": dms / st[2]}
+        log(f"dense causal {dms:.2f} ms ({res['dense']['tflops']:.0f} TFLOP/s)")
+        del wsd
+    del q, k, v, out, ws, ab
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, w, dash, torch):
+    from long_context_sparse_stage0_amd import synth
+    t0 = time.time()
+    x = synth.decode_inputs(w)
+    log(f"generated {w.name} inputs in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    kc = torch.from_numpy(x["k_cache"]).to(torch.bfloat16).to(dev)
+    vc = torch.from_numpy(x["v_cache"]).to(torch.bfloat16).to(dev)
+    hc = torch.from_numpy(x["head_cls"]).to(torch.bfloat16).to(dev)
+    qs = torch.from_numpy(x["q_steps"]).to(torch.bfloat16).to(dev)
+    del x
+    B, Hkv, TT, D = kc.shape
+    Hq = qs.shape[2]
+    S = min(args.decode_steps, w.steps)
+    nc = -(-TT // 64)
+    W = -(-nc // 64)
+    summ = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device=dev)
+    nsum = torch.zeros(B, dtype=torch.int32, device=dev)
+    lens_all = (w.T + 1 + torch.arange(S, dtype=torch.int32, device=dev))[:, None].repeat(1, B).contiguous()
+    init_len = torch.full((B,), w.T, dtype=torch.int32, device=dev)
+    dash.append_chunk(kc, hc, init_len, summ, nsum, Hq=Hq, enable_gqa=True)
+    p = dash.make_params(B, Hq, Hkv, TT, D, alpha=w.alpha, enable_gqa=True, dtype=torch.bfloat16)
+    ws = dash.alloc_workspace(dash.workspace_size("decode", p), dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ab = torch.empty((B, Hkv, W), dtype=torch.int64, device=dev)
+
+    def run(n, with_mask=False):
+        act = 0.0
+        for s in range(n):
+            L = w.T + 1 + s
+            r = dash.decode(qs[s], kc, vc, lens_all[s], summ, alpha=w.alpha, enable_gqa=True,
+                            out=out, workspace=ws, return_active_blocks=with_mask)
+            if with_mask:
+                act += float(popcount64(r[1]).sum())
+            if L % 64 == 0:
+                dash.append_chunk(kc, hc, lens_all[s], summ, nsum, Hq=Hq, enable_gqa=True)
+        return act
+
+    # untimed pass for the algorithmic bytes
+    act = run(S, with_mask=True)
+    torch.cuda.synchronize()
+    nsum.fill_(w.T // 64)
+    # bytes: summaries of routed chunks (fp32), active K/V chunks, the diagonal tokens, q, o
+    bytes_total = 0.0
+    for s in range(S):
+        t = w.T + s
+        it = t // 64
+        bytes_total += B * Hkv * (it * D * 4 + (t % 64 + 1) * D * 2 * 2) + 2 * B * Hq * D * 2
+    bytes_total += act * 64 * D * 2 * 2
+    for _ in range(args.warmup):
+        run(min(S, 8))
+    torch.cuda.synchronize()
+    nsum.fill_(w.T // 64)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    run(S)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = e0.elapsed_time(e1) * 1e3 / S
+    gbs = bytes_total / S / (us * 1e-6) / 1e9
+    frac_active = act / (B * Hkv * sum((w.T + s) // 64 for s in range(S)))
+    log(f"decode {us:.1f} us/step ({(t1 - t0) * 1e6 / S:.1f} wall), {gbs:.0f} GB/s, "
+        f"active fraction {frac_active:.3f}")
+    del kc, vc, qs, summ, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "us_per_step": us, "tokens_per_s": B / (us * 1e-6),
+            "steps": S, "algorithmic_bytes_per_step": bytes_total / S,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS},
+            "active_fraction": frac_active}
+
+
+def cpu_baseline(args, w, x):
+    """The float64 oracle on a bounded, uniformly sampled set of rows; extrapolated to the
+    whole sequence (Stage 0 over every chunk + mean row cost x T)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import dash_oracle as O
+    rng = np.random.default_rng(12345)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        summ = O.chunk_summaries(x["k"], x["head_cls"], 1.0 / math.sqrt(w.D))
+        t_s0 = time.perf_counter() - t0
+        rows = rng.integers(0, w.T, size=2)
+        t0 = time.perf_counter()
+        O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, rows=rows, summaries=summ)
+        t_probe = time.perf_counter() - t0
+        n = int(max(4, min(256, args.cpu_seconds / max(t_probe / 2, 1e-3))))
+        rows = rng.integers(0, w.T, size=n)
+        t0 = time.perf_counter()
+        O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, rows=rows, summaries=summ)
+        t_rows = time.perf_counter() - t0
+    t_full = t_s0 + t_rows / n * w.T
+    log(f"oracle: stage 0 {t_s0:.1f}s, {n} rows {t_rows:.1f}s -> {t_full:.0f}s for the sequence")
+    return {"value": w.B * w.T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} uniformly sampled rows of the {w.name} workload (all heads) plus "
+                      f"Stage 0 over every chunk, extrapolated to all {w.T} rows; "
+                      f"{t_s0 + t_rows:.1f}s of CPU time, 1 BLAS thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--workload", default="prefill_128k_gqa32x2")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_stage0_amd import dash
+    from long_context_sparse_stage0_amd.workloads import ALL, DECODE_64K_B16
+    dash.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = ALL[args.workload]
+    pre = bench_prefill(args, w, dash, torch)
+    dec = None if args.no_decode else bench_decode(args, DECODE_64K_B16, dash, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, w, pre["x"])
+
+    line = {
+        "metric": METRIC, "value": pre["tokens_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "alpha": w.alpha, "needle_amp": w.needle_amp,
+                   "zero_weight_fraction": pre["zero_frac"]},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "stages_ms": {"stage0_summaries_and_vT": pre["stages_ms"][0],
+                      "stage1_route": pre["stages_ms"][1], "stage2_attend": pre["stages_ms"][2]},
+        "dense": pre.get("dense"),
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

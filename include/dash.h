@@ -98,6 +98,15 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
                  float* block_weights, float* summary_out, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Profiling aid: run one stage of dash_prefill alone (stage 0: summaries and the
+ * chunk-transposed V; 1: routing; 2: sparse attention), reading the intermediates that a
+ * complete dash_prefill call with the same arguments and workspace left behind.  Used to
+ * time each kernel separately; results equal those of the full call. */
+int dash_prefill_stage(const dash_params* p, int stage, const void* q, const void* k,
+                       const void* v, const void* head_cls, void* out,
+                       uint64_t* active_blocks, float* block_weights, float* summary_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * One incremental decoding step (one new token per sequence).
  *   p->T          cache capacity T_max

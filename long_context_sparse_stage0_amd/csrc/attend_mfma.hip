@@ -1,0 +1,345 @@
+// Stage 2 on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16): prior-induced sparse softmax
+// attention over the active chunks of a bit-packed mask, flash-style online softmax.
+//
+// Method: gist.science summary of arXiv 2605.18753, "Stufe 2: Prior-induzierte spärliche
+// Softmax" (softmax(z + log g), g = 0 where the routing weight is 0, FlashAttention-style
+// kernel iterating over the active chunks of a bit-packed mask and adding the routing bias
+// to the logits; the query's own chunk is a separate branch); aixai.ru blog,
+// "Трёхстадийная архитектура" (the mask is walked in one pass, with no per-query index
+// materialisation).  All G query heads of a KV head share the mask and the weights.
+//
+// Work unit: one workgroup per (b, kv head, R consecutive rows inside one 64-row block),
+// i.e. R x G query vectors (256 for G >= 4), 32 per wave.  The workgroup walks the union
+// of its rows' mask words in increasing chunk order (a visit list built in LDS), then the
+// diagonal chunk; per visit, each row gets bias log2(w_bar) where its own bit is set and
+// -inf where it is not, so the union walk computes exactly the per-row result.
+//
+// MFMA mapping (16x16x32, wave64; lane l, k-slot (l/16, i)):
+//   S^T = K Q^T  : A = K rows, B = Q^T.  The 16 rows of a key tile are permuted so that
+//                  after two tiles ("halves") of a 32-key span, lane l holds the scores of
+//                  keys 32p + 8(l/16) + [0, 8) for its query column l%16.
+//   O^T += V^T P^T: B = P^T straight from those registers (k-slot i <-> key 8(l/16)+i),
+//                  A = V^T rows read as one 16-byte LDS load from a chunk-transposed copy
+//                  of V ([chunk][d][64 keys]) that Stage 0's companion kernel writes.
+// Softmax runs in base 2 (the logit scale carries log2 e); the running max starts at a
+// large finite negative value so a query whose row is masked for a whole chunk stays NaN-
+// free.  K/V tiles are register-prefetched one visit ahead into the other of two LDS
+// buffers; rows are padded by 16 bytes so every 16-byte LDS read is bank-conflict free.
+#include "dash_internal.h"
+
+namespace dash {
+
+namespace {
+
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+}  // namespace
+
+template <int D, int NW, bool DENSE>
+__global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 32;          // k-steps of the QK^T contraction
+  constexpr int NDT = D / 16;         // 16-wide d tiles of the output
+  constexpr int KP = D * 2 + 16;      // K row pitch in LDS (bytes)
+  constexpr int VP = 64 * 2 + 16;     // V^T row pitch in LDS (bytes)
+  constexpr int KBYTES = 64 * KP, VBYTES = D * VP;
+  constexpr int KSEG = 64 * D / 8, VSEG = D * 8;       // 16-byte segments per tile
+  constexpr int KPT = (KSEG + NT - 1) / NT, VPT = (VSEG + NT - 1) / NT;
+  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][VBYTES];
+  __shared__ uint64_t rowbits[64][MAXW];
+  __shared__ uint16_t visit[kMaxRouted + 2];
+  __shared__ int woff[MAXW + 1];
+
+  const int G = a.Hq / a.Hkv;
+  const int R = NW * 32 / G;                 // rows per workgroup (<= 64, divides 64)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  // heavy tiles (late rows) first: the hardware dispatches workgroups roughly in order
+  const int tile = gridDim.x - 1 - blockIdx.x;
+  const int BH = a.B * a.Hkv;
+  const int rt = tile / BH, bk = tile % BH;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int row0 = rt * R;
+  const int it = row0 / kChunk;              // diagonal chunk, shared by all R rows
+  const int T = a.Tq;
+  (void)tiles_per_bk;
+
+  // ---- per-row mask words and the union walk
+  const int W = a.W;
+  const int nw_route = (it + 63) / 64;       // words that can hold routed chunks
+  if (!DENSE) {
+    for (int idx = tid; idx < R * nw_route; idx += NT) {
+      const int r = idx / nw_route, w = idx % nw_route;
+      const int t = row0 + r;
+      rowbits[r][w] = (t < T) ? a.mask[((size_t)bk * a.rows + t) * W + w] : 0ull;
+    }
+  }
+  __syncthreads();
+  if (tid < nw_route) {
+    uint64_t u = 0;
+    if (DENSE) {
+      const int n = min(64, it - 64 * tid);
+      u = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    } else {
+      for (int r = 0; r < R; ++r) u |= rowbits[r][tid];
+    }
+    woff[tid + 1] = __popcll(u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    woff[0] = 0;
+    for (int w = 0; w < nw_route; ++w) woff[w + 1] += woff[w];
+  }
+  __syncthreads();
+  if (tid < nw_route) {
+    uint64_t u = 0;
+    if (DENSE) {
+      const int n = min(64, it - 64 * tid);
+      u = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    } else {
+      for (int r = 0; r < R; ++r) u |= rowbits[r][tid];
+    }
+    int o = woff[tid];
+    while (u) {
+      visit[o++] = (uint16_t)(64 * tid + __builtin_ctzll(u));
+      u &= u - 1;
+    }
+  }
+  if (tid == 0) visit[woff[nw_route]] = (uint16_t)it;
+  __syncthreads();
+  const int nvis = woff[nw_route] + 1;
+
+  // ---- this lane's two query columns
+  const int l16 = lane & 15, lg = lane >> 4;
+  int qrow[2], qh[2];
+  bool qok[2];
+  bf16x8 qop[2][KS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int n = 32 * wv + 16 * qt + l16;
+    const int r = n / G, g = n % G;
+    qrow[qt] = r;
+    qh[qt] = kvh * G + g;
+    const int t = row0 + r;
+    qok[qt] = t < T;
+    const bf16* qp = (const bf16*)a.q + ((size_t)(b * a.Hq + qh[qt]) * T + (qok[qt] ? t : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
+      if (!qok[qt]) v = bf16x8{};
+      qop[qt][ks] = v;
+    }
+  }
+
+  // ---- global -> register prefetch of one chunk's K and V^T tiles
+  const bf16* kbase = (const bf16*)a.k + (size_t)bk * a.Tk * D;
+  const bf16* vtbase = (const bf16*)a.vt + (size_t)bk * a.nc * D * 64;
+  uint4 kreg[KPT], vreg[VPT];
+  auto prefetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int seg = tid + i * NT;
+      if (seg < KSEG) {
+        const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
+        const int key = c * kChunk + row;
+        kreg[i] = key < a.Tk ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col)
+                             : make_uint4(0, 0, 0, 0);
+      }
+    }
+    const bf16* vsrc = vtbase + (size_t)c * D * 64;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int seg = tid + i * NT;
+      if (seg < VSEG) vreg[i] = *reinterpret_cast<const uint4*>(vsrc + seg * 8);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int seg = tid + i * NT;
+      if (seg < KSEG) {
+        const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
+        *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + col * 2]) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int seg = tid + i * NT;
+      if (seg < VSEG) {
+        const int row = seg / 8, col = (seg % 8) * 8;
+        *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + col * 2]) = vreg[i];
+      }
+    }
+  };
+  // routing bias of this lane's two rows for chunk c (base 2)
+  auto load_bias = [&](int c, float* bias) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float bv = 0.f;
+      if (!DENSE && c != it) {
+        const int r = qrow[qt];
+        const bool on = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
+        bv = on ? fast_log2(a.wbar[((size_t)bk * a.rows + row0 + r) * a.wbar_ld + c]) : -INFINITY;
+      }
+      bias[qt] = bv;
+    }
+  };
+
+  floatx4 o[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {kNegBig, kNegBig}, lsum[2] = {0.f, 0.f};
+  const float sl2 = a.scale_log2;
+  const int tloc[2] = {(row0 + qrow[0]) & 63, (row0 + qrow[1]) & 63};
+
+  prefetch(visit[0]);
+  float bias_next[2];
+  load_bias(visit[0], bias_next);
+
+  for (int vi = 0; vi < nvis; ++vi) {
+    const int c = visit[vi];
+    const int buf = vi & 1;
+    stash(buf);
+    float bias[2] = {bias_next[0], bias_next[1]};
+    __syncthreads();
+    if (vi + 1 < nvis) {
+      const int cn = visit[vi + 1];
+      prefetch(cn);
+      load_bias(cn, bias_next);
+    }
+    const bool diag = (c == it);
+    const uint8_t* kl = lds_k[buf];
+    const uint8_t* vl = lds_v[buf];
+
+    // S^T for 64 keys: tile kt = 2 p + half
+    floatx4 s[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int p = kt >> 1, half = kt & 1;
+      const int key = 32 * p + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
+      s[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      s[1][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + key * KP + (32 * ks + 8 * lg) * 2);
+        s[0][kt] = mfma16(ka, qop[0][ks], s[0][kt]);
+        s[1][kt] = mfma16(ka, qop[1][ks], s[1][kt]);
+      }
+    }
+
+    // online softmax per query column; build P^T operands
+    bf16x8 pop[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float x[16];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = fmaf(s[qt][kt][j], sl2, bias[qt]);
+          if (diag) {
+            const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
+            if (key > tloc[qt]) v = -INFINITY;
+          }
+          x[4 * kt + j] = v;
+        }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = xor16_max(mx);
+      const float mn = fmaxf(m[qt], mx);
+      const float corr = fast_exp2(m[qt] - mn);
+      m[qt] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = fast_exp2(x[i] - mn);
+        ps += x[i];
+      }
+      lsum[qt] = fmaf(lsum[qt], corr, ps);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        bf16x8 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = (bf16)x[8 * p + j];          // half 0: keys 32p + 8 lg + j
+          v[4 + j] = (bf16)x[8 * p + 4 + j];  // half 1: keys 32p + 8 lg + 4 + j
+        }
+        pop[qt][p] = v;
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const bf16x8 va =
+            *reinterpret_cast<const bf16x8*>(vl + (16 * dt + l16) * VP + (32 * p + 8 * lg) * 2);
+        o[0][dt] = mfma16(va, pop[0][p], o[0][dt]);
+        o[1][dt] = mfma16(va, pop[1][p], o[1][dt]);
+      }
+    }
+  }
+
+  // ---- normalise and write
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l = xor16_sum(lsum[qt]);
+    const float rl = 1.0f / l;
+    if (!qok[qt]) continue;
+    bf16* op = (bf16*)a.out + ((size_t)(b * a.Hq + qh[qt]) * T + row0 + qrow[qt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (bf16)(o[qt][dt][j] * rl);
+      *reinterpret_cast<bf16x4*>(op + 16 * dt + 4 * lg) = v;
+    }
+  }
+}
+
+template <int D, bool DENSE>
+static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int NW = G >= 4 ? 8 : 2 * G;  // 32 query vectors per wave
+  const int R = NW * 32 / G;
+  const int tiles = (a.Tq + R - 1) / R;
+  dim3 grid(tiles * a.B * a.Hkv);
+  switch (NW) {
+    case 8: k_attend_mfma<D, 8, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
+    case 4: k_attend_mfma<D, 4, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
+    default: k_attend_mfma<D, 2, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s) {
+  (void)work_counter;
+  if (a.dense)
+    return a.D == 128 ? launch_attend_mfma_t<128, true>(a, s) : launch_attend_mfma_t<64, true>(a, s);
+  return a.D == 128 ? launch_attend_mfma_t<128, false>(a, s) : launch_attend_mfma_t<64, false>(a, s);
+}
+
+}  // namespace dash

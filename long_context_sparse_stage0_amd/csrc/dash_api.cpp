@@ -177,10 +177,10 @@ int dash_prefill_workspace_size(const dash_params* p, size_t* bytes) {
   return ok();
 }
 
-int dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
-                 const void* head_cls, void* out, uint64_t* active_blocks,
-                 float* block_weights, float* summary_out, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+static int prefill_impl(const dash_params* p, int stages, const void* q, const void* k,
+                        const void* v, const void* head_cls, void* out,
+                        uint64_t* active_blocks, float* block_weights, float* summary_out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
   if (int rc = check_ptr(q, "q")) return rc;
@@ -201,13 +201,19 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
   float* wbar = block_weights ? block_weights : reinterpret_cast<float*>(ws + L.wbar);
   hipError_t e;
 
-  if (block_weights) {
+  if (stages & 1) {
+    if ((e = dash::launch_stage0(k, head_cls, summ, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull,
+                                 nullptr, nullptr, d.scale, d.dtype, s)) != hipSuccess)
+      return hip_fail(e, "stage 0 launch");
+    if (d.dtype == DASH_BF16) {
+      if ((e = dash::launch_vtranspose(v, ws + L.vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
+        return hip_fail(e, "V transpose launch");
+    }
+  }
+  if ((stages & 2) && block_weights) {
     if ((e = fill_f32(block_weights, (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess)
       return hip_fail(e, "clearing block_weights");
   }
-  if ((e = dash::launch_stage0(k, head_cls, summ, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull, nullptr,
-                               nullptr, d.scale, d.dtype, s)) != hipSuccess)
-    return hip_fail(e, "stage 0 launch");
 
   dash::RouteArgs ra{};
   ra.q = q;
@@ -228,7 +234,10 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
   ra.alpha = d.alpha;
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
   ra.dtype = d.dtype;
-  if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "stage 1 launch");
+  if (stages & 2) {
+    if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "stage 1 launch");
+  }
+  if (!(stages & 4)) return ok();
 
   dash::AttendArgs aa{};
   aa.q = q;
@@ -252,8 +261,31 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
   aa.scale_log2 = d.scale * 1.4426950408889634f;
   aa.dtype = d.dtype;
   aa.dense = 0;
-  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "stage 2 launch");
+  if (d.dtype == DASH_BF16) {
+    aa.vt = ws + L.vt;
+    if ((e = dash::launch_attend_mfma(aa, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "stage 2 launch");
+  } else {
+    if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "stage 2 launch");
+  }
   return ok();
+}
+
+int dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
+                 const void* head_cls, void* out, uint64_t* active_blocks,
+                 float* block_weights, float* summary_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return prefill_impl(p, 7, q, k, v, head_cls, out, active_blocks, block_weights, summary_out,
+                      workspace, workspace_bytes, stream);
+}
+
+int dash_prefill_stage(const dash_params* p, int stage, const void* q, const void* k,
+                       const void* v, const void* head_cls, void* out,
+                       uint64_t* active_blocks, float* block_weights, float* summary_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 2) return fail(DASH_ERR_INVALID_ARG, "stage must be 0, 1 or 2");
+  return prefill_impl(p, 1 << stage, q, k, v, head_cls, out, active_blocks, block_weights,
+                      summary_out, workspace, workspace_bytes, stream);
 }
 
 int dash_decode_workspace_size(const dash_params* p, size_t* bytes) {
@@ -390,7 +422,11 @@ int dash_dense_causal(const dash_params* p, const void* q, const void* k, const 
   aa.scale_log2 = d.scale * 1.4426950408889634f;
   aa.dtype = d.dtype;
   aa.dense = 1;
-  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "dense launch");
+  void* vt = workspace;
+  if ((e = dash::launch_vtranspose(v, vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
+    return hip_fail(e, "V transpose launch");
+  aa.vt = vt;
+  if ((e = dash::launch_attend_mfma(aa, nullptr, s)) != hipSuccess) return hip_fail(e, "dense launch");
   return ok();
 }
 

@@ -28,7 +28,7 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 
 EXPORTS = [
     "dash_abi_version", "dash_last_error",
-    "dash_prefill_workspace_size", "dash_prefill",
+    "dash_prefill_workspace_size", "dash_prefill", "dash_prefill_stage",
     "dash_decode_workspace_size", "dash_decode",
     "dash_append_chunk",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.dash_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_prefill.restype = ctypes.c_int
+    lib.dash_prefill_stage.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_prefill_stage.restype = ctypes.c_int
     lib.dash_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_decode.restype = ctypes.c_int
     lib.dash_append_chunk.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -153,6 +155,20 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
                                workspace.numel(), _stream(stream)))
     extras = [x for x in (ab, bw, sm) if x is not None]
     return (out, *extras) if extras else out
+
+
+def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=1.0,
+                  sm_scale=None, enable_gqa=False, active_blocks=None, block_weights=None,
+                  summaries=None, stream=None):
+    """Run one prefill stage (0, 1 or 2) from the intermediates a full `prefill` call with
+    the same tensors and workspace left behind (profiling aid)."""
+    B, Hq, T, D = q.shape
+    p = make_params(B, Hq, k.shape[1], T, D, alpha=alpha, gamma=gamma, sm_scale=sm_scale,
+                    enable_gqa=enable_gqa, dtype=q.dtype)
+    _check(load().dash_prefill_stage(ctypes.byref(p), int(stage), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(head_cls), _ptr(out), _ptr(active_blocks),
+                                     _ptr(block_weights), _ptr(summaries), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
 
 
 def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha=1.5,
