@@ -98,7 +98,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillLayout {
-  size_t summ, vt, mask, wbar, ctr, total;
+  size_t summ, ssplit, vt, mask, wbar, ctr, total;
 };
 
 PrefillLayout prefill_layout(const Dims& d) {
@@ -106,6 +106,8 @@ PrefillLayout prefill_layout(const Dims& d) {
   size_t off = 0;
   L.summ = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
+  L.ssplit = off;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * d.nc * 2 * d.D * 2) : 0;
   L.vt = off;
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * d.nc * d.D * 64 * 2) : 0;
   L.mask = off;
@@ -202,7 +204,8 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   hipError_t e;
 
   if (stages & 1) {
-    if ((e = dash::launch_stage0(k, head_cls, summ, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull,
+    void* ss = d.dtype == DASH_BF16 ? (void*)(ws + L.ssplit) : nullptr;
+    if ((e = dash::launch_stage0(k, head_cls, summ, ss, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull,
                                  nullptr, nullptr, d.scale, d.dtype, s)) != hipSuccess)
       return hip_fail(e, "stage 0 launch");
     if (d.dtype == DASH_BF16) {
@@ -235,7 +238,11 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
   ra.dtype = d.dtype;
   if (stages & 2) {
-    if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "stage 1 launch");
+    if (d.dtype == DASH_BF16)
+      e = dash::launch_route_mfma(ra, ws + L.ssplit, s);
+    else
+      e = dash::launch_route_valu(ra, s);
+    if (e != hipSuccess) return hip_fail(e, "stage 1 launch");
   }
   if (!(stages & 4)) return ok();
 
@@ -375,7 +382,7 @@ int dash_append_chunk(const dash_params* p, const void* k_cache, const void* hea
   if (!n_summarized) return fail(DASH_ERR_INVALID_ARG, "n_summarized is NULL");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if ((e = dash::launch_stage0(k_cache, head_cls, summary_cache, d.B, d.Hkv, d.T, d.D, d.nc,
+  if ((e = dash::launch_stage0(k_cache, head_cls, summary_cache, nullptr, d.B, d.Hkv, d.T, d.D, d.nc,
                                d.nfull, n_summarized, seq_lens, d.scale, d.dtype, s)) != hipSuccess)
     return hip_fail(e, "append launch");
   if ((e = dash::launch_update_nsum(n_summarized, seq_lens, d.B, s)) != hipSuccess)

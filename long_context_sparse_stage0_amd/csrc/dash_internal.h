@@ -72,8 +72,10 @@ struct AttendArgs {
   int dense;              // 1: every chunk c < i_t active with prior 1 (comparator)
 };
 
-hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, int B, int Hkv,
-                         int T_stride, int D, int nc_alloc, int n_full,
+// summ_split (nullable, bf16 inputs only): [B, Hkv, nc_alloc, 2, D] bf16 hi and lo planes of
+// the fp32 summaries (hi = bf16(x), lo = bf16(x - hi)) for the MFMA router.
+hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
+                         int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,
                          int dtype, hipStream_t s);
 hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
@@ -81,7 +83,7 @@ hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, in
 hipError_t launch_vtranspose(const void* v, void* vt, int B, int Hkv, int T, int D, int nc,
                              hipStream_t s);
 hipError_t launch_route_valu(const RouteArgs& a, hipStream_t s);
-hipError_t launch_route_mfma(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s);
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s);
 

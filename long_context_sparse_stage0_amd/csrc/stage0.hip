@@ -19,7 +19,8 @@ namespace dash {
 template <typename TIn, int D>
 __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
                                                const TIn* __restrict__ head_cls,
-                                               float* __restrict__ summ, int Hkv,
+                                               float* __restrict__ summ,
+                                               bf16* __restrict__ ssplit, int Hkv,
                                                int T_stride, int nc_alloc, int n_full,
                                                const int32_t* __restrict__ lo_b,
                                                const int32_t* __restrict__ seq_lens,
@@ -74,6 +75,15 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
     float* o = summ + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * D + lane * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = acc[e];
+    if (ssplit != nullptr) {
+      bf16* sp = ssplit + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * 2 * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bf16 hi = (bf16)acc[e];
+        sp[e] = hi;
+        sp[D + e] = (bf16)(acc[e] - (float)hi);
+      }
+    }
     __syncthreads();
   }
 }
@@ -117,29 +127,30 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t* __restrict__
   }
 }
 
-hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, int B, int Hkv,
-                         int T_stride, int D, int nc_alloc, int n_full,
+hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
+                         int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,
                          int dtype, hipStream_t s) {
+  bf16* ss = (bf16*)summ_split;
   const float sl2 = scale * 1.4426950408889634f;
   int gx = seq_lens ? 64 : n_full;
   if (gx < 1) gx = 1;
   dim3 grid(gx, Hkv, B);
   if (dtype == 0) {
     if (D == 128)
-      k_stage0<bf16, 128><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, Hkv,
+      k_stage0<bf16, 128><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, ss, Hkv,
                                               T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
     else
-      k_stage0<bf16, 64><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, Hkv,
+      k_stage0<bf16, 64><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, ss, Hkv,
                                              T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
   } else {
     if (D == 128)
       k_stage0<float, 128><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
-                                               Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
+                                               nullptr, Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
                                                sl2);
     else
       k_stage0<float, 64><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
-                                              Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
+                                              nullptr, Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
                                               sl2);
   }
   return hipGetLastError();

@@ -59,7 +59,7 @@ class Workload:
 # Amplitude of the needle shift for the 128K workload, chosen by
 # oracle/calibrate_needles.py so that about 75% of causal (row, kv-head, chunk) pairs
 # receive zero routing weight.  The 64K decode and sweep workloads reuse it.
-CALIBRATED_AMP = 0.5
+CALIBRATED_AMP = 0.328125
 
 PREFILL_1K_FP32 = Workload(
     name="prefill_1k_fp32", kind="prefill", B=1, Hq=2, Hkv=2, T=1024, D=64,
