@@ -121,7 +121,7 @@ PrefillLayout prefill_layout(const Dims& d) {
 }
 
 struct DecodeLayout {
-  size_t mask, wbar, total;
+  size_t mask, wbar, pml, po, total;
 };
 
 DecodeLayout decode_layout(const Dims& d) {
@@ -131,6 +131,11 @@ DecodeLayout decode_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.W * 8);
   L.wbar = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * 4);
+  const size_t nseg = (size_t)dash::decode_nseg_max(d.nc);
+  L.pml = off;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 32 * 4) : 0;
+  L.po = off;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 16 * d.D * 4) : 0;
   L.total = off;
   return L;
 }
@@ -343,7 +348,8 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   ra.alpha = d.alpha;
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
   ra.dtype = d.dtype;
-  if ((e = dash::launch_route_valu(ra, s)) != hipSuccess) return hip_fail(e, "decode route launch");
+  e = d.dtype == DASH_BF16 ? dash::launch_decode_route(ra, s) : dash::launch_route_valu(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "decode route launch");
 
   dash::AttendArgs aa{};
   aa.q = q;
@@ -366,7 +372,12 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   aa.scale_log2 = d.scale * 1.4426950408889634f;
   aa.dtype = d.dtype;
   aa.dense = 0;
-  if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "decode attend launch");
+  if (d.dtype == DASH_BF16)
+    e = dash::launch_decode_attend(aa, reinterpret_cast<float*>(ws + L.pml),
+                                   reinterpret_cast<float*>(ws + L.po), s);
+  else
+    e = dash::launch_attend_valu(aa, s);
+  if (e != hipSuccess) return hip_fail(e, "decode attend launch");
   return ok();
 }
 

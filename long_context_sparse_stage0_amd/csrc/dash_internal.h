@@ -87,4 +87,11 @@ hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStre
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s);
 
+// decode (bf16): route one row per (b, kv head); split-K attend over the active chunks
+// into per-segment partials pml [B*Hkv][nseg][32] (max, sum) and po [B*Hkv][nseg][16][D],
+// then a log-sum-exp combine into a.out.
+int decode_nseg_max(int nc);
+hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_decode_attend(const AttendArgs& a, float* pml, float* po, hipStream_t s);
+
 }  // namespace dash

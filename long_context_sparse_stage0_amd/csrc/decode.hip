@@ -1,0 +1,370 @@
+// Incremental decoding: one new query row per sequence against the K/V cache and the
+// chunk-summary cache (arXiv 2605.18753 as summarised on gist.science: "Stufe 0" -- a
+// complete chunk's summary is frozen and cached; the kernels support incremental decoding
+// with a chunk-representation cache, "Hauptbeiträge").  Decode row t equals prefill row t.
+//
+// Three kernels per step, all on the caller's stream:
+//   k_decode_route   one 16-wave workgroup per (b, kv head): the G heads' scores against
+//                    every routed summary on MFMA (fp32 summaries split into bf16 hi + lo
+//                    in registers), staged in LDS so that wave g solves head g's entmax
+//                    threshold with wave-only reductions; then a fixed-order sum over the
+//                    heads, a ballot per 64 chunks for the mask word and w_bar at set bits.
+//   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
+//                    chunk form a list; each workgroup takes 16 consecutive items, each of
+//                    its 4 waves a quarter of them.  S^T = K Q^T with K rows loaded straight
+//                    from global as MFMA operands, V staged through wave-private LDS in
+//                    [d][key] order for the V^T P^T product; the waves' (max, sum, O)
+//                    partials are merged in LDS and written once per workgroup.
+//   k_decode_combine log-sum-exp merge of the segment partials, one workgroup per (b, head).
+// Decoding is HBM-bound: the active K/V chunks (32 KiB each at D = 128) dominate the bytes.
+#include "route_common.h"
+
+namespace dash {
+
+namespace {
+
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float xg_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xg_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+constexpr int kSeg = 16;        // list items per attend workgroup
+constexpr int kAttWaves = 4;
+constexpr float kNegBig = -1.0e30f;
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ route
+template <int D, int MODE>
+__global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
+  constexpr int NW = 16, KS = D / 32, NR = kMaxRoutedRegs;
+  constexpr int ld = kMaxRouted + 16;            // covers 16 * ceil(routed / 16) columns
+  __shared__ __attribute__((aligned(16))) float sc[16 * ld];  // [head][chunk] scores, then weights
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int bk = blockIdx.x, b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int t = a.seq_lens[b] - 1;
+  const bool valid = t >= 0 && t < a.tcap;
+  const int it = valid ? t / kChunk : 0;
+
+  // scores: S^T tile = 16 chunks x 16 head columns (columns >= G are zero queries)
+  bf16x8 qop[KS];
+  {
+    const bool qok = l16 < G;
+    const bf16* qp = (const bf16*)a.q + ((size_t)b * a.Hq + kvh * G + (qok ? l16 : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
+      qop[ks] = qok ? v : bf16x8{};
+    }
+  }
+  const float* sb = a.summ + (size_t)bk * a.nc_alloc * D;
+  const int ntile = (it + 15) / 16;
+  for (int ct = wv; ct < ntile; ct += NW) {
+    const int crow = 16 * ct + l16;
+    const bool cok = crow < it;
+    const float* srow = sb + (size_t)(cok ? crow : 0) * D;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 x0 = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
+      const float4 x1 = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16 h = (bf16)xs[i];
+        hi[i] = h;
+        lo[i] = (bf16)(xs[i] - (float)h);
+      }
+      if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
+      acc = mfma16(hi, qop[ks], acc);
+      acc = mfma16(lo, qop[ks], acc);
+    }
+    *reinterpret_cast<float4*>(&sc[l16 * ld + 16 * ct + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+  __syncthreads();
+
+  // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...
+  if (wv < G && it > 0) {
+    float y[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = lane + 64 * r;
+      y[r] = c < it ? a.zscale * sc[wv * ld + c] : -INFINITY;
+    }
+    float z;
+    const float tau = entmax_threshold<MODE, NR>(y, it, a.alpha, WaveReduce(), &z);
+    const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = lane + 64 * r;
+      if (c < it) sc[wv * ld + c] = entmax_weight<MODE>(y[r], tau, inv, rz);
+    }
+  }
+  __syncthreads();
+
+  // GQA average in head order, mask words by ballot, w_bar at set bits
+  const float rG = 1.0f / (float)G;
+  for (int w = wv; w < a.W; w += NW) {
+    const int c = 64 * w + lane;
+    float s = 0.f;
+    if (c < it)
+      for (int g = 0; g < G; ++g) s += sc[g * ld + c];
+    const float wb = s * rG;
+    const bool on = c < it && wb > 0.f;
+    const uint64_t bits = __ballot(on);
+    if (on) a.wbar[(size_t)bk * a.wbar_ld + c] = wb;
+    if (lane == 0) a.mask[(size_t)bk * a.W + w] = bits;
+  }
+}
+
+// ------------------------------------------------------------------------------ attend
+template <int D>
+__global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, float* __restrict__ pml,
+                                                                  float* __restrict__ po, int nseg_max) {
+  constexpr int KS = D / 32, NDT = D / 16;
+  constexpr int VP = 64 + 8;                      // V^T row pitch (bf16 elements)
+  constexpr int SEGS = 64 * D / 8;                // 16-byte segments per V tile
+  __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][D * VP];
+  __shared__ int items[kSeg];
+  __shared__ int nitems_s, nact_s;
+  __shared__ float mrg_ml[kAttWaves][2][16];
+
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int seg = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int t = a.seq_lens[b] - 1;
+  if (t < 0 || t >= a.Tk) return;                 // the combine kernel writes NaN
+  const int it = t / kChunk;
+  const uint64_t* mw = a.mask + (size_t)bk * a.W;
+
+  if (tid == 0) {
+    // items: set bits of the mask in chunk order, then the diagonal chunk
+    int nact = 0;
+    for (int w = 0; w < a.W; ++w) nact += __popcll(mw[w]);
+    const int lo = seg * kSeg, hi = min(lo + kSeg, nact + 1);
+    int n = 0, rank = 0;
+    for (int w = 0; w < a.W && rank < hi; ++w) {
+      uint64_t bits = mw[w];
+      const int pc = __popcll(bits);
+      if (rank + pc <= lo) { rank += pc; continue; }
+      while (bits && rank < hi) {
+        const int c = 64 * w + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (rank >= lo) items[n++] = c;
+        ++rank;
+      }
+    }
+    if (nact >= lo && nact < hi) items[n++] = it;  // the diagonal is the last item
+    nitems_s = n;
+    nact_s = nact;
+  }
+  __syncthreads();
+  const int nitems = nitems_s;
+  if (nitems == 0) return;
+
+  // query columns: the G heads of this kv head (columns >= G are zero)
+  bf16x8 qop[KS];
+  {
+    const bool qok = l16 < G;
+    const bf16* qp = (const bf16*)a.q + ((size_t)b * a.Hq + kvh * G + (qok ? l16 : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
+      qop[ks] = qok ? v : bf16x8{};
+    }
+  }
+  const bf16* kb = (const bf16*)a.k + (size_t)bk * a.Tk * D;
+  const bf16* vb = (const bf16*)a.v + (size_t)bk * a.Tk * D;
+  bf16* vl = vts[wv];
+  const float sl2 = a.scale_log2;
+  float m = kNegBig, lsum = 0.f;
+  floatx4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ii = wv; ii < nitems; ii += kAttWaves) {
+    const int c = items[ii];
+    const bool diag = c == it;
+    const int kmax = diag ? t : c * kChunk + 63;   // last valid key of this chunk
+    // V tile -> LDS as [d][key]
+#pragma unroll 4
+    for (int i = 0; i < SEGS / 64; ++i) {
+      const int sgi = i * 64 + lane;
+      const int key = sgi / (D / 8), db = (sgi % (D / 8)) * 8;
+      const int kabs = c * kChunk + key;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (kabs <= kmax) val = *reinterpret_cast<const uint4*>(vb + (size_t)kabs * D + db);
+      const bf16* pv = reinterpret_cast<const bf16*>(&val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vl[(db + e) * VP + key] = pv[e];
+    }
+    // S^T = K Q^T, key tiles permuted so lane l ends with keys 32p + 8 lg + [0, 8)
+    floatx4 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
+      const int kabs = c * kChunk + key;
+      const bool kok = kabs <= kmax;
+      const bf16* kr = kb + (size_t)(kok ? kabs : 0) * D;
+      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + 32 * ks + 8 * lg);
+        if (!kok) ka = bf16x8{};
+        s[kt] = mfma16(ka, qop[ks], s[kt]);
+      }
+    }
+    const float bias = diag ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]);
+    float x[16];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
+        x[4 * kt + j] = (c * kChunk + key <= kmax) ? fmaf(s[kt][j], sl2, bias) : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = xg_max(mx);
+    const float mn = fmaxf(m, mx);
+    const float corr = fast_exp2(m - mn);
+    m = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = fast_exp2(x[i] - mn);
+      ps += x[i];
+    }
+    lsum = fmaf(lsum, corr, ps);
+    bf16x8 pop[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pop[p][j] = (bf16)x[8 * p + j];
+        pop[p][4 + j] = (bf16)x[8 * p + 4 + j];
+      }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] *= corr;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (16 * dt + l16) * VP + 32 * p + 8 * lg);
+        o[dt] = mfma16(va, pop[p], o[dt]);
+      }
+    }
+  }
+  // merge the waves' partials: (m, l) per query column, then O rescaled and summed in LDS
+  lsum = xg_sum(lsum);
+  if (lg == 0) {
+    mrg_ml[wv][0][l16] = m;
+    mrg_ml[wv][1][l16] = lsum;
+  }
+  __syncthreads();
+  float mt = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kAttWaves; ++w) mt = fmaxf(mt, mrg_ml[w][0][l16]);
+  const float f = fast_exp2(m - mt);
+  float* ob = reinterpret_cast<float*>(&vts[0][0]);          // reuse: [D][16] floats
+  __syncthreads();
+  for (int w = 0; w < kAttWaves; ++w) {
+    if (wv == w) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 16 * dt + 4 * lg + j;
+          const float v = o[dt][j] * f;
+          ob[d * 16 + l16] = (w == 0) ? v : ob[d * 16 + l16] + v;
+        }
+    }
+    __syncthreads();
+  }
+  const size_t pidx = (size_t)bk * nseg_max + seg;
+  if (tid < 16) {
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) lt += mrg_ml[w][1][tid] * fast_exp2(mrg_ml[w][0][tid] - mt);
+    pml[pidx * 32 + tid] = mt;
+    pml[pidx * 32 + 16 + tid] = lt;
+  }
+  for (int i = tid; i < 16 * D; i += kAttWaves * 64) {
+    const int q = i / D, d = i % D;
+    po[(pidx * 16 + q) * D + d] = ob[d * 16 + q];
+  }
+}
+
+// ------------------------------------------------------------------------------ combine
+template <typename TOut, int D>
+__global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
+                                                      const float* __restrict__ po, int nseg_max) {
+  const int bh = blockIdx.x, b = bh / a.Hq, h = bh % a.Hq;
+  const int G = a.Hq / a.Hkv, kvh = h / G, q = h % G;
+  const int bk = b * a.Hkv + kvh;
+  const int d = threadIdx.x;
+  TOut* op = (TOut*)a.out + (size_t)bh * D;
+  const int t = a.seq_lens[b] - 1;
+  if (t < 0 || t >= a.Tk) {
+    op[d] = from_f32<TOut>(__builtin_nanf(""));
+    return;
+  }
+  int nact = 0;
+  for (int w = 0; w < a.W; ++w) nact += __popcll(a.mask[(size_t)bk * a.W + w]);
+  const int nseg = (nact + 1 + kSeg - 1) / kSeg;
+  float mt = kNegBig;
+  for (int s = 0; s < nseg; ++s) mt = fmaxf(mt, pml[((size_t)bk * nseg_max + s) * 32 + q]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    const size_t pi = (size_t)bk * nseg_max + s;
+    const float f = fast_exp2(pml[pi * 32 + q] - mt);
+    l += pml[pi * 32 + 16 + q] * f;
+    acc += po[(pi * 16 + q) * D + d] * f;
+  }
+  op[d] = from_f32<TOut>(acc / l);
+}
+
+// ------------------------------------------------------------------------------ launchers
+int decode_nseg_max(int nc) { return (nc + 1 + kSeg - 1) / kSeg; }
+
+hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
+  const size_t lds = 0;
+  dim3 grid(a.B * a.Hkv);
+  if (a.D == 128) {
+    if (a.alpha == 1.5f) k_decode_route<128, kAlpha15><<<grid, 1024, lds, s>>>(a);
+    else if (a.alpha == 2.0f) k_decode_route<128, kAlpha2><<<grid, 1024, lds, s>>>(a);
+    else k_decode_route<128, kAlphaGeneral><<<grid, 1024, lds, s>>>(a);
+  } else {
+    if (a.alpha == 1.5f) k_decode_route<64, kAlpha15><<<grid, 1024, lds, s>>>(a);
+    else if (a.alpha == 2.0f) k_decode_route<64, kAlpha2><<<grid, 1024, lds, s>>>(a);
+    else k_decode_route<64, kAlphaGeneral><<<grid, 1024, lds, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attend(const AttendArgs& a, float* pml, float* po, hipStream_t s) {
+  const int nseg = decode_nseg_max(a.nc);
+  dim3 grid(nseg, a.B * a.Hkv);
+  if (a.D == 128) k_decode_attend<128><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg);
+  else k_decode_attend<64><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(a.B * a.Hq);
+  if (a.D == 128) k_decode_combine<bf16, 128><<<g2, 128, 0, s>>>(a, pml, po, nseg);
+  else k_decode_combine<bf16, 64><<<g2, 64, 0, s>>>(a, pml, po, nseg);
+  return hipGetLastError();
+}
+
+}  // namespace dash

@@ -7,10 +7,11 @@
 // blog, "Трёхстадийная архитектура" (active chunks packed in 64-bit words).  The entmax
 // definition is that of Peters, Niculae and Martins (2019).
 //
-// Work unit: one workgroup (8 waves) per (b, kv head, R = 32/G rows of one 64-row block):
-// 32 query vectors that all route over the same chunks c < i_t.  Chunk tiles of 16 are
-// dealt to the waves round-robin (tile w, w+8, ...), and every score stays in registers
-// (16 tiles x 2 query tiles x 4 = 128 values per lane at 2048 chunks).
+// Work unit: one workgroup (8 or 16 waves) per (b, kv head, R = 32/G rows of one 64-row
+// block): 32 query vectors that all route over the same chunks c < i_t.  Chunk tiles of 16
+// are dealt to the waves round-robin (tile w, w + NW, ...), and every score stays in
+// registers (at most 8 tiles x 2 query tiles x 4 = 64 values per lane; 16 waves cover
+// 2048 chunks).
 //
 // Scores: S^T = K_bar Q^T on v_mfma_f32_16x16x32_bf16.  Q is bf16 exactly; the fp32
 // summaries are split once (by Stage 0) into bf16 hi + lo planes and both products are
@@ -63,9 +64,9 @@ __device__ __forceinline__ float xg_max(float v) {
 
 }  // namespace
 
-template <int D, int MT, int MODE>
-__global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit) {
-  constexpr int NW = 8, KS = D / 32, NQ = 4;  // NQ reduced quantities per pass
+template <int D, int NW, int MT, int MODE>
+__global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit) {
+  constexpr int NT = NW * 64, KS = D / 32, NQ = 4;  // NQ reduced quantities per pass
   constexpr int MAXW = (kMaxRouted + 63) / 64 + 1;
   __shared__ float part[2][2][NQ][16][NW];
   __shared__ unsigned long long mbits[32][MAXW];
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
   const int T = a.Tq;
   const int W = a.W;
 
-  for (int i = tid; i < 32 * MAXW; i += 512) (&mbits[0][0])[i] = 0ull;
+  for (int i = tid; i < 32 * MAXW; i += NT) (&mbits[0][0])[i] = 0ull;
 
   // queries of this lane: column l16 of query tiles 0 and 1
   bf16x8 qop[2][KS];
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
   for (int j = 0; j < MT; ++j) {
     const int ct = wv + NW * j;
     floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (ct < ntile) {
+    if (ct < ntile) {  // wave-uniform
       const int crow = 16 * ct + l16;
       const bool cok = crow < it;
       const bf16* srow = sp + (size_t)(cok ? crow : 0) * 2 * D;
@@ -131,6 +132,10 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
     }
   }
 
+  // tiles owned by this wave: wv, wv + 8, ... below ntile (wave-uniform, so the per-tile
+  // blocks below are skipped by scalar branches)
+  const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
+
   // ---- threshold solver for the 32 queries
   float tau[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f}, zs[2] = {1.f, 1.f};
   bool done[2] = {true, true};
@@ -142,9 +147,12 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
     for (int qt = 0; qt < 2; ++qt) {
       float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
+      for (int j = 0; j < MT; ++j) {
+        if (j < nj) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, y[j][qt][jj]);
+          for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, y[j][qt][jj]);
+        }
+      }
       m = xg_max(m);
       if (lg == 0) part[buf][qt][0][l16][wv] = m;
     }
@@ -166,25 +174,27 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
       for (int qt = 0; qt < 2; ++qt) {
         float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
 #pragma unroll
-        for (int j = 0; j < MT; ++j)
+        for (int j = 0; j < MT; ++j) {
+          if (j >= nj) continue;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const float d = y[j][qt][jj] - tau[qt];
-            if (d > 0.f) {
-              cnt += 1.f;
-              mn = fminf(mn, d);
-              if (MODE == kAlpha15) {
-                s1 += d;
-                s2 = fmaf(d, d, s2);
-              } else if (MODE == kAlpha2) {
-                s1 += d;
-              } else {
-                const float dp1 = pow_pos(d, inv - 1.0f);
-                s1 += dp1;
-                s2 = fmaf(dp1, d, s2);
-              }
+            const bool in = d > 0.f;
+            const float dp = fmaxf(d, 0.f);
+            cnt += in ? 1.f : 0.f;
+            mn = fminf(mn, in ? d : INFINITY);
+            if (MODE == kAlpha15) {
+              s1 += dp;
+              s2 = fmaf(dp, dp, s2);
+            } else if (MODE == kAlpha2) {
+              s1 += dp;
+            } else if (in) {
+              const float dp1 = pow_pos(d, inv - 1.0f);
+              s1 += dp1;
+              s2 = fmaf(dp1, d, s2);
             }
           }
+        }
         cnt = xg_sum(cnt);
         s1 = xg_sum(s1);
         s2 = xg_sum(s2);
@@ -243,12 +253,14 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
     for (int qt = 0; qt < 2; ++qt) {
       float z = 0.f;
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
+      for (int j = 0; j < MT; ++j) {
+        if (j >= nj) continue;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float d = y[j][qt][jj] - tau[qt];
           if (d > 0.f) z += (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
         }
+      }
       z = xg_sum(z);
       if (lg == 0) part[buf][qt][0][l16][wv] = z;
     }
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         const int ct = wv + NW * j;
-        if (ct >= ntile) continue;
+        if (j >= nj) continue;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float p = entmax_weight<MODE>(y[j][qt][jj], tau[qt], inv, rz);
@@ -288,32 +300,31 @@ __global__ __launch_bounds__(512) void k_route_mfma(RouteArgs a, const bf16* __r
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < R * W; idx += 512) {
+  for (int idx = tid; idx < R * W; idx += NT) {
     const int r = idx / W, w = idx % W;
     if (row0 + r < T) a.mask[((size_t)bk * a.rows + row0 + r) * W + w] = (w < MAXW) ? mbits[r][w] : 0ull;
   }
 }
 
-template <int D, int MT>
+template <int D, int NW, int MT>
 static void launch_mt(const RouteArgs& a, const bf16* ss, dim3 grid, hipStream_t s) {
   if (a.alpha == 1.5f)
-    k_route_mfma<D, MT, kAlpha15><<<grid, 512, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss);
   else if (a.alpha == 2.0f)
-    k_route_mfma<D, MT, kAlpha2><<<grid, 512, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss);
   else
-    k_route_mfma<D, MT, kAlphaGeneral><<<grid, 512, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss);
 }
 
 template <int D>
 static void launch_d(const RouteArgs& a, const bf16* ss, dim3 grid, hipStream_t s) {
   const int max_it = (a.Tq - 1) / kChunk;
   const int tiles = (max_it + 15) / 16;
-  const int mt = (tiles + 7) / 8;
-  if (mt <= 1) launch_mt<D, 1>(a, ss, grid, s);
-  else if (mt <= 2) launch_mt<D, 2>(a, ss, grid, s);
-  else if (mt <= 4) launch_mt<D, 4>(a, ss, grid, s);
-  else if (mt <= 8) launch_mt<D, 8>(a, ss, grid, s);
-  else launch_mt<D, 16>(a, ss, grid, s);
+  if (tiles <= 8) launch_mt<D, 8, 1>(a, ss, grid, s);
+  else if (tiles <= 16) launch_mt<D, 8, 2>(a, ss, grid, s);
+  else if (tiles <= 32) launch_mt<D, 8, 4>(a, ss, grid, s);
+  else if (tiles <= 64) launch_mt<D, 8, 8>(a, ss, grid, s);
+  else launch_mt<D, 16, 8>(a, ss, grid, s);
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s) {

@@ -157,3 +157,33 @@ def test_decode_fp32_and_invalid_len(dash):
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.isnan(o[0]).all() and np.isfinite(o[1]).all()
+
+
+def test_decode_steps_with_append(dash):
+    """Decode 100 consecutive steps from a 600-token prompt (GQA 4), appending each chunk
+    as it fills; every step equals the oracle's prefill row of the full sequence."""
+    w = Workload(name="dec_steps", kind="prefill", B=2, Hq=8, Hkv=2, T=700, D=128,
+                 dtype="bf16", seed=33, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say("[parity] decode 100 steps with appends, GQA 4")
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    B, Hkv, T, D = 2, 2, 700, 128
+    nc = -(-T // 64)
+    summ = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(B, dtype=torch.int32, device="cuda")
+    L0 = 600
+    dash.append_chunk(k, hc, torch.full((B,), L0, dtype=torch.int32, device="cuda"), summ, nsum,
+                      Hq=8, enable_gqa=True)
+    outs = []
+    for s in range(T - L0):
+        L = L0 + s + 1
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        q = to_dev(x["q"][:, :, L - 1], "bf16").contiguous()
+        outs.append(dash.decode(q, k, v, lens, summ, enable_gqa=True).float().cpu().numpy())
+        if L % 64 == 0:
+            dash.append_chunk(k, hc, lens, summ, nsum, Hq=8, enable_gqa=True)
+    torch.cuda.synchronize()
+    rows = np.arange(L0, T)
+    ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], rows=rows)
+    g = np.stack(outs, axis=2)                       # [B, Hq, steps, D]
+    compare_out(g, ref["out"], "bf16", what="decode steps")
