@@ -128,15 +128,38 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
 }
 
 // ------------------------------------------------------------------------------ attend
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// V^T operand of the 16x16x32 MFMA for d rows d0 + (l % 16) and keys k0 + [0, 8), read from
+// a row-major [key][d] LDS tile with two transposing loads (ds_read_b64_tr_b16): within a
+// 16-lane group, source lane r = 4k + q points at V[k0 + k][d0 + 4q] and output lane i
+// receives V[k0 + k][d0 + i] for k = 0..3.
+__device__ __forceinline__ bf16x8 vt_operand(const bf16* tile, int pitch, int k0, int d0, int l16) {
+  const int k = l16 >> 2, q = l16 & 3;
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const bf16* p0 = tile + (k0 + k) * pitch + d0 + 4 * q;
+  const bf16* p1 = p0 + 4 * pitch;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+  // concatenate as whole vectors: element-wise bf16 re-packing of these results was
+  // miscompiled (halves duplicated) by this toolchain
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, float* __restrict__ pml,
                                                                   float* __restrict__ po, int nseg_max) {
   constexpr int KS = D / 32, NDT = D / 16;
-  constexpr int VP = 64 + 8;                      // V^T row pitch (bf16 elements)
-  constexpr int SEGS = 64 * D / 8;                // 16-byte segments per V tile
-  __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][D * VP];
+  constexpr int VP = D + 16;                      // V row pitch in LDS (bf16 elements)
+  constexpr int SEGR = D / 8;                     // 16-byte segments per V row
+  constexpr int VL = 64 * SEGR / 64;              // segments per lane per tile
+  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
+  __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][64 * VP];
+  __shared__ uint64_t wl[MAXW];
+  __shared__ int wpre[MAXW + 1];
   __shared__ int items[kSeg];
-  __shared__ int nitems_s, nact_s;
   __shared__ float mrg_ml[kAttWaves][2][16];
 
   const int G = a.Hq / a.Hkv;
@@ -147,34 +170,41 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
   const int t = a.seq_lens[b] - 1;
   if (t < 0 || t >= a.Tk) return;                 // the combine kernel writes NaN
   const int it = t / kChunk;
-  const uint64_t* mw = a.mask + (size_t)bk * a.W;
+  const int W = a.W;
 
-  if (tid == 0) {
-    // items: set bits of the mask in chunk order, then the diagonal chunk
-    int nact = 0;
-    for (int w = 0; w < a.W; ++w) nact += __popcll(mw[w]);
-    const int lo = seg * kSeg, hi = min(lo + kSeg, nact + 1);
-    int n = 0, rank = 0;
-    for (int w = 0; w < a.W && rank < hi; ++w) {
-      uint64_t bits = mw[w];
-      const int pc = __popcll(bits);
-      if (rank + pc <= lo) { rank += pc; continue; }
-      while (bits && rank < hi) {
-        const int c = 64 * w + __builtin_ctzll(bits);
-        bits &= bits - 1;
-        if (rank >= lo) items[n++] = c;
-        ++rank;
-      }
+  // ---- the list: set mask bits in chunk order, then the diagonal chunk
+  if (tid < W) wl[tid] = a.mask[(size_t)bk * W + tid];
+  __syncthreads();
+  if (wv == 0) {  // inclusive scan of the words' popcounts
+    int v = lane < W ? __popcll(wl[lane]) : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o, 64);
+      if (lane >= o) v += u;
     }
-    if (nact >= lo && nact < hi) items[n++] = it;  // the diagonal is the last item
-    nitems_s = n;
-    nact_s = nact;
+    if (lane < W) wpre[lane + 1] = v;
+    if (lane == 0) wpre[0] = 0;
   }
   __syncthreads();
-  const int nitems = nitems_s;
-  if (nitems == 0) return;
+  const int nact = wpre[W];
+  const int lo = seg * kSeg, hi = min(lo + kSeg, nact + 1);
+  const int nitems = hi - lo;
+  if (nitems <= 0) return;
+  if (tid < nitems) {
+    const int r = lo + tid;
+    int c = it;
+    if (r < nact) {
+      int w = 0;
+      while (wpre[w + 1] <= r) ++w;
+      uint64_t bits = wl[w];
+      for (int k = r - wpre[w]; k > 0; --k) bits &= bits - 1;
+      c = 64 * w + __builtin_ctzll(bits);
+    }
+    items[tid] = c;
+  }
+  __syncthreads();
 
-  // query columns: the G heads of this kv head (columns >= G are zero)
+  // ---- query columns: the G heads of this kv head (columns >= G are zero)
   bf16x8 qop[KS];
   {
     const bool qok = l16 < G;
@@ -194,39 +224,60 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ii = wv; ii < nitems; ii += kAttWaves) {
-    const int c = items[ii];
-    const bool diag = c == it;
-    const int kmax = diag ? t : c * kChunk + 63;   // last valid key of this chunk
-    // V tile -> LDS as [d][key]
-#pragma unroll 4
-    for (int i = 0; i < SEGS / 64; ++i) {
-      const int sgi = i * 64 + lane;
-      const int key = sgi / (D / 8), db = (sgi % (D / 8)) * 8;
-      const int kabs = c * kChunk + key;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (kabs <= kmax) val = *reinterpret_cast<const uint4*>(vb + (size_t)kabs * D + db);
-      const bf16* pv = reinterpret_cast<const bf16*>(&val);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vl[(db + e) * VP + key] = pv[e];
-    }
-    // S^T = K Q^T, key tiles permuted so lane l ends with keys 32p + 8 lg + [0, 8)
-    floatx4 s[4];
+  // registers for one item: K operands (A of S^T) and this lane's V segments
+  bf16x8 kop[4][KS];
+  uint4 vseg[VL];
+  auto load_item = [&](int c) {
+    const int kmax = (c == it) ? t : c * kChunk + 63;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
       const int kabs = c * kChunk + key;
       const bool kok = kabs <= kmax;
       const bf16* kr = kb + (size_t)(kok ? kabs : 0) * D;
-      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr + 32 * ks + 8 * lg);
-        if (!kok) ka = bf16x8{};
-        s[kt] = mfma16(ka, qop[ks], s[kt]);
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(kr + 32 * ks + 8 * lg);
+        kop[kt][ks] = kok ? v : bf16x8{};
       }
     }
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int sg = i * 64 + lane;
+      const int key = sg / SEGR, db = (sg % SEGR) * 8;
+      const int kabs = c * kChunk + key;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kabs <= kmax) v = *reinterpret_cast<const uint4*>(vb + (size_t)kabs * D + db);
+      vseg[i] = v;
+    }
+  };
+
+  if (wv < nitems) load_item(items[wv]);
+  for (int ii = wv; ii < nitems; ii += kAttWaves) {
+    const int c = items[ii];
+    const bool diag = c == it;
+    const int kmax = diag ? t : c * kChunk + 63;
+    // V rows -> LDS (row-major, padded)
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int sg = i * 64 + lane;
+      const int key = sg / SEGR, db = (sg % SEGR) * 8;
+      *reinterpret_cast<uint4*>(vl + key * VP + db) = vseg[i];
+    }
+    // wait for these stores before the transposing LDS reads below: unlike ordinary LDS
+    // reads they are not ordered behind the wave's outstanding LDS writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // S^T = K Q^T
+    floatx4 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[kt] = mfma16(kop[kt][ks], qop[ks], s[kt]);
+    }
     const float bias = diag ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]);
+    // next item's loads overlap the softmax and the PV product
+    if (ii + kAttWaves < nitems) load_item(items[ii + kAttWaves]);
     float x[16];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -261,11 +312,10 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
     for (int dt = 0; dt < NDT; ++dt) {
       o[dt] *= corr;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (16 * dt + l16) * VP + 32 * p + 8 * lg);
-        o[dt] = mfma16(va, pop[p], o[dt]);
-      }
+      for (int p = 0; p < 2; ++p)
+        o[dt] = mfma16(vt_operand(vl, VP, 32 * p + 8 * lg, 16 * dt, l16), pop[p], o[dt]);
     }
+    asm volatile("" ::: "memory");  // the next item's stores stay after these reads
   }
   // merge the waves' partials: (m, l) per query column, then O rescaled and summed in LDS
   lsum = xg_sum(lsum);
@@ -279,7 +329,6 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
   for (int w = 0; w < kAttWaves; ++w) mt = fmaxf(mt, mrg_ml[w][0][l16]);
   const float f = fast_exp2(m - mt);
   float* ob = reinterpret_cast<float*>(&vts[0][0]);          // reuse: [D][16] floats
-  __syncthreads();
   for (int w = 0; w < kAttWaves; ++w) {
     if (wv == w) {
 #pragma unroll
@@ -308,31 +357,54 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
 }
 
 // ------------------------------------------------------------------------------ combine
+// one workgroup of D threads per (b, head); the segment maxima and sums are reduced in
+// parallel, then each thread merges its column of the partial outputs.
 template <typename TOut, int D>
 __global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
                                                       const float* __restrict__ po, int nseg_max) {
+  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
+  __shared__ float fs[256];
+  __shared__ float red[D / 64 > 0 ? D / 64 : 1];
+  __shared__ int cnt[MAXW];
   const int bh = blockIdx.x, b = bh / a.Hq, h = bh % a.Hq;
   const int G = a.Hq / a.Hkv, kvh = h / G, q = h % G;
   const int bk = b * a.Hkv + kvh;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   TOut* op = (TOut*)a.out + (size_t)bh * D;
   const int t = a.seq_lens[b] - 1;
   if (t < 0 || t >= a.Tk) {
     op[d] = from_f32<TOut>(__builtin_nanf(""));
     return;
   }
+  for (int w = d; w < a.W; w += D) cnt[w] = __popcll(a.mask[(size_t)bk * a.W + w]);
+  __syncthreads();
   int nact = 0;
-  for (int w = 0; w < a.W; ++w) nact += __popcll(a.mask[(size_t)bk * a.W + w]);
-  const int nseg = (nact + 1 + kSeg - 1) / kSeg;
-  float mt = kNegBig;
-  for (int s = 0; s < nseg; ++s) mt = fmaxf(mt, pml[((size_t)bk * nseg_max + s) * 32 + q]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < nseg; ++s) {
+  for (int w = 0; w < a.W; ++w) nact += cnt[w];
+  const int nseg = (nact + 1 + kSeg - 1) / kSeg;   // <= 256 for 2048 routed chunks
+  // max over segments
+  float mloc = kNegBig;
+  for (int s = d; s < nseg; s += D) mloc = fmaxf(mloc, pml[((size_t)bk * nseg_max + s) * 32 + q]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wv] = mloc;
+  __syncthreads();
+  float mt = red[0];
+  for (int w = 1; w < D / 64; ++w) mt = fmaxf(mt, red[w]);
+  __syncthreads();
+  // per-segment factors and the total sum
+  float lloc = 0.f;
+  for (int s = d; s < nseg; s += D) {
     const size_t pi = (size_t)bk * nseg_max + s;
     const float f = fast_exp2(pml[pi * 32 + q] - mt);
-    l += pml[pi * 32 + 16 + q] * f;
-    acc += po[(pi * 16 + q) * D + d] * f;
+    fs[s] = f;
+    lloc += pml[pi * 32 + 16 + q] * f;
   }
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[wv] = lloc;
+  __syncthreads();
+  float l = 0.f;
+  for (int w = 0; w < D / 64; ++w) l += red[w];
+  float acc = 0.f;
+  for (int s = 0; s < nseg; ++s) acc += po[(((size_t)bk * nseg_max + s) * 16 + q) * D + d] * fs[s];
   op[d] = from_f32<TOut>(acc / l);
 }
 
