@@ -26,6 +26,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast", "-munsafe-fp-atomics",
+    # never let the compiler move per-thread arrays into LDS behind our back: an array it
+    # cannot keep in registers should show up as scratch in the resource report instead
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
   constexpr int VP = 64 * 2 + 16;     // V^T row pitch in LDS (bytes)
   constexpr int KBYTES = 64 * KP, VBYTES = D * VP;
   constexpr int KSEG = 64 * D / 8, VSEG = D * 8;       // 16-byte segments per tile
-  constexpr int KPT = (KSEG + NT - 1) / NT, VPT = (VSEG + NT - 1) / NT;
+  constexpr int KPT = KSEG / NT, VPT = VSEG / NT;
+  static_assert(KSEG % NT == 0 && VSEG % NT == 0, "tile loads must cover every thread evenly");
   constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
@@ -155,36 +156,31 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int seg = tid + i * NT;
-      if (seg < KSEG) {
-        const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
-        const int key = c * kChunk + row;
-        kreg[i] = key < a.Tk ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col)
-                             : make_uint4(0, 0, 0, 0);
-      }
+      const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
+      const int key = c * kChunk + row;
+      kreg[i] = key < a.Tk ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col)
+                           : make_uint4(0, 0, 0, 0);
     }
     const bf16* vsrc = vtbase + (size_t)c * D * 64;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int seg = tid + i * NT;
-      if (seg < VSEG) vreg[i] = *reinterpret_cast<const uint4*>(vsrc + seg * 8);
+      // bounds-checked select, as for K (a plain assignment here was demoted to scratch)
+      vreg[i] = c < a.nc ? *reinterpret_cast<const uint4*>(vsrc + (tid + i * NT) * 8)
+                         : make_uint4(0, 0, 0, 0);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int seg = tid + i * NT;
-      if (seg < KSEG) {
-        const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + col * 2]) = kreg[i];
-      }
+      const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + col * 2]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int seg = tid + i * NT;
-      if (seg < VSEG) {
-        const int row = seg / 8, col = (seg % 8) * 8;
-        *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + col * 2]) = vreg[i];
-      }
+      const int row = seg / 8, col = (seg % 8) * 8;
+      *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + col * 2]) = vreg[i];
     }
   };
   // routing bias of this lane's two rows for chunk c (base 2)
@@ -249,29 +245,28 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
     bf16x8 pop[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
+      // raw scores (keys past the row masked on the diagonal); the logit max follows from
+      // the raw max because the scale is positive and the bias is constant per column
       float x[16];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = fmaf(s[qt][kt][j], sl2, bias[qt]);
-          if (diag) {
-            const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
-            if (key > tloc[qt]) v = -INFINITY;
-          }
-          x[4 * kt + j] = v;
+          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
+          x[4 * kt + j] = (diag && key > tloc[qt]) ? -INFINITY : s[qt][kt][j];
         }
-      float mx = x[0];
+      float mr = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      mx = xor16_max(mx);
-      const float mn = fmaxf(m[qt], mx);
+      for (int i = 4; i < 16; i += 4) mr = fmaxf(mr, fmaxf(fmaxf(x[i], x[i + 1]), fmaxf(x[i + 2], x[i + 3])));
+      mr = xor16_max(mr);
+      const float mn = fmaxf(m[qt], fmaf(mr, sl2, bias[qt]));
       const float corr = fast_exp2(m[qt] - mn);
       m[qt] = mn;
+      const float off = bias[qt] - mn;
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[i] = fast_exp2(x[i] - mn);
+        x[i] = fast_exp2(fmaf(x[i], sl2, off));
         ps += x[i];
       }
       lsum[qt] = fmaf(lsum[qt], corr, ps);
