@@ -24,7 +24,16 @@
 // Softmax runs in base 2 (the logit scale carries log2 e); the running max starts at a
 // large finite negative value so a query whose row is masked for a whole chunk stays NaN-
 // free.  K/V tiles are register-prefetched one visit ahead into the other of two LDS
-// buffers; rows are padded by 16 bytes so every 16-byte LDS read is bank-conflict free.
+// buffers.
+//
+// LDS layout: a 16-byte LDS access by a full wave is served in two half-wave passes, and a
+// pass is conflict free when its 32 lanes hit 32 distinct 16-byte slots modulo 512 bytes
+// (measured on gfx950: padding rows by 16 bytes, which suffices for 8-lane groups, leaves
+// the operand reads below 2-way conflicted).  Rows are therefore unpadded and the 16-byte
+// chunks of a row are XOR-swizzled by row bits (kswz, vswz) chosen so that the MFMA
+// operand reads and the tile stores both touch 32 distinct slots per half-wave.
+#include <type_traits>
+
 #include "dash_internal.h"
 
 namespace dash {
@@ -32,29 +41,48 @@ namespace dash {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
+constexpr float kSlack = 8.0f;      // log2 of the largest unnormalised probability kept
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+// max over lanes l, l^16, l^32, l^48 with the gfx950 row-swap moves (no LDS round trip):
+// permlane16_swap(v, v) gives each lane the values of rows {2i, 2i+1} of its row pair,
+// permlane32_swap(v, v) those of the lower and the upper half-wave
+__device__ __forceinline__ float rowgroup_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
   v += __shfl_xor(v, 16, 64);
   return v + __shfl_xor(v, 32, 64);
 }
 
+// Swizzle of the 16-byte chunk index inside a K row (D/8 chunks per row).  A half-wave's
+// operand read covers 16 keys {8i + j : i < 4, j < 4} (+ const) times two chunks; keys that
+// share a 512-byte slot line (same key mod 32/(D/8)) get distinct even masks.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  if (D == 128) return 2 * (((key >> 1) & 1) | (((key >> 3) & 3) << 1));
+  return 2 * ((key >> 3) & 3);
+}
+// Swizzle of the 16-byte chunk index inside a V^T row (64 keys = 8 chunks per row): the
+// operand read covers 16 consecutive rows times two chunks.
+__device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 3); }
+
 }  // namespace
 
-template <int D, int NW, bool DENSE>
-__global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
+template <int D, int NW, int RMAX, bool DENSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   constexpr int NT = NW * 64;
   constexpr int KS = D / 32;          // k-steps of the QK^T contraction
   constexpr int NDT = D / 16;         // 16-wide d tiles of the output
-  constexpr int KP = D * 2 + 16;      // K row pitch in LDS (bytes)
-  constexpr int VP = 64 * 2 + 16;     // V^T row pitch in LDS (bytes)
+  constexpr int KP = D * 2;           // K row pitch in LDS (bytes), chunks swizzled
+  constexpr int VP = 64 * 2;          // V^T row pitch in LDS (bytes), chunks swizzled
   constexpr int KBYTES = 64 * KP, VBYTES = D * VP;
   constexpr int KSEG = 64 * D / 8, VSEG = D * 8;       // 16-byte segments per tile
   constexpr int KPT = KSEG / NT, VPT = VSEG / NT;
@@ -63,7 +91,7 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][VBYTES];
-  __shared__ uint64_t rowbits[64][MAXW];
+  __shared__ uint64_t rowbits[RMAX][MAXW];
   __shared__ uint16_t visit[kMaxRouted + 2];
   __shared__ int woff[MAXW + 1];
 
@@ -148,7 +176,9 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
     }
   }
 
-  // ---- global -> register prefetch of one chunk's K and V^T tiles
+  // ---- global -> register prefetch of one chunk's K and V^T tiles.  Both loads are
+  // written as bounds-checked selects: as plain assignments the compiler keeps the arrays
+  // in scratch memory.
   const bf16* kbase = (const bf16*)a.k + (size_t)bk * a.Tk * D;
   const bf16* vtbase = (const bf16*)a.vt + (size_t)bk * a.nc * D * 64;
   uint4 kreg[KPT], vreg[VPT];
@@ -163,37 +193,37 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
     }
     const bf16* vsrc = vtbase + (size_t)c * D * 64;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      // bounds-checked select, as for K (a plain assignment here was demoted to scratch)
+    for (int i = 0; i < VPT; ++i)
       vreg[i] = c < a.nc ? *reinterpret_cast<const uint4*>(vsrc + (tid + i * NT) * 8)
                          : make_uint4(0, 0, 0, 0);
-    }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int seg = tid + i * NT;
-      const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + col * 2]) = kreg[i];
+      const int row = seg / (D / 8), ch = seg % (D / 8);
+      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + (ch ^ kswz<D>(row)) * 16]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int seg = tid + i * NT;
-      const int row = seg / 8, col = (seg % 8) * 8;
-      *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + col * 2]) = vreg[i];
+      const int row = seg / 8, ch = seg % 8;
+      *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + (ch ^ vswz(row)) * 16]) = vreg[i];
     }
   };
-  // routing bias of this lane's two rows for chunk c (base 2)
-  auto load_bias = [&](int c, float* bias) {
+  // routing weight and mask bit of this lane's two rows for routed chunk c; the weight is
+  // loaded one visit ahead and only turned into a bias (log2 w, or -inf where the row's bit
+  // is clear) when the visit starts, so no wait on it stalls the tile prefetch
+  float wnext[2] = {1.f, 1.f};
+  bool onnext[2] = {true, true};
+  auto fetch_weight = [&](int c) {
+    if (DENSE) return;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float bv = 0.f;
-      if (!DENSE && c != it) {
-        const int r = qrow[qt];
-        const bool on = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
-        bv = on ? fast_log2(a.wbar[((size_t)bk * a.rows + row0 + r) * a.wbar_ld + c]) : -INFINITY;
-      }
-      bias[qt] = bv;
+      const int r = qrow[qt];
+      onnext[qt] = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
+      const int t = min(row0 + r, a.rows - 1);
+      wnext[qt] = a.wbar[((size_t)bk * a.rows + t) * a.wbar_ld + c];
     }
   };
 
@@ -202,42 +232,46 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // m: the reference maximum of each query column (base-2 logits).  It is only raised when
+  // a chunk's maximum exceeds it by more than kSlack, so most chunks skip the rescale of
+  // O and l; probabilities relative to it stay below 2^kSlack.
   float m[2] = {kNegBig, kNegBig}, lsum[2] = {0.f, 0.f};
   const float sl2 = a.scale_log2;
   const int tloc[2] = {(row0 + qrow[0]) & 63, (row0 + qrow[1]) & 63};
 
-  prefetch(visit[0]);
-  float bias_next[2];
-  load_bias(visit[0], bias_next);
-
-  for (int vi = 0; vi < nvis; ++vi) {
-    const int c = visit[vi];
+  // one visit of chunk visit[vi]; DIAG: the query block's own chunk (always the last visit)
+  auto visit_chunk = [&](int vi, auto diag_tag) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
     const int buf = vi & 1;
     stash(buf);
-    float bias[2] = {bias_next[0], bias_next[1]};
+    float bias[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      bias[qt] = (DIAG || DENSE) ? 0.f : (onnext[qt] ? fast_log2(wnext[qt]) : -INFINITY);
     __syncthreads();
-    if (vi + 1 < nvis) {
+    if (!DIAG) {
       const int cn = visit[vi + 1];
       prefetch(cn);
-      load_bias(cn, bias_next);
+      if (cn != it) fetch_weight(cn);
     }
-    const bool diag = (c == it);
     const uint8_t* kl = lds_k[buf];
     const uint8_t* vl = lds_v[buf];
 
     // S^T for 64 keys: tile kt = 2 p + half
-    floatx4 s[2][4];
+    floatx4 sc[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int p = kt >> 1, half = kt & 1;
       const int key = 32 * p + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
-      s[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      s[1][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int ksw = kswz<D>(key);        // p and half do not change the swizzle
+      sc[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sc[1][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + key * KP + (32 * ks + 8 * lg) * 2);
-        s[0][kt] = mfma16(ka, qop[0][ks], s[0][kt]);
-        s[1][kt] = mfma16(ka, qop[1][ks], s[1][kt]);
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(kl + key * KP + ((4 * ks + lg) ^ ksw) * 16);
+        sc[0][kt] = mfma16(ka, qop[0][ks], sc[0][kt]);
+        sc[1][kt] = mfma16(ka, qop[1][ks], sc[1][kt]);
       }
     }
 
@@ -253,25 +287,29 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
-          x[4 * kt + j] = (diag && key > tloc[qt]) ? -INFINITY : s[qt][kt][j];
+          x[4 * kt + j] = (DIAG && key > tloc[qt]) ? -INFINITY : sc[qt][kt][j];
         }
-      float mr = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      float mr = fmaxf(fmaxf(x[0], x[1]), x[2]);
 #pragma unroll
-      for (int i = 4; i < 16; i += 4) mr = fmaxf(mr, fmaxf(fmaxf(x[i], x[i + 1]), fmaxf(x[i + 2], x[i + 3])));
-      mr = xor16_max(mr);
-      const float mn = fmaxf(m[qt], fmaf(mr, sl2, bias[qt]));
-      const float corr = fast_exp2(m[qt] - mn);
-      m[qt] = mn;
-      const float off = bias[qt] - mn;
+      for (int i = 3; i < 15; i += 2) mr = fmaxf(fmaxf(mr, x[i]), x[i + 1]);
+      mr = rowgroup_max(fmaxf(mr, x[15]));
+      const float cand = fmaf(mr, sl2, bias[qt]);
+      if (__builtin_amdgcn_ballot_w64(cand > m[qt] + kSlack) != 0ull) {
+        const float mn = fmaxf(m[qt], cand);
+        const float corr = fast_exp2(m[qt] - mn);
+        m[qt] = mn;
+        lsum[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
+      }
+      const float off = bias[qt] - m[qt];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x[i] = fast_exp2(fmaf(x[i], sl2, off));
         ps += x[i];
       }
-      lsum[qt] = fmaf(lsum[qt], corr, ps);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
+      lsum[qt] += ps;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         bf16x8 v;
@@ -289,13 +327,18 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(vl + (16 * dt + l16) * VP + (32 * p + 8 * lg) * 2);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+            vl + (16 * dt + l16) * VP + ((4 * p + lg) ^ vswz(l16)) * 16);
         o[0][dt] = mfma16(va, pop[0][p], o[0][dt]);
         o[1][dt] = mfma16(va, pop[1][p], o[1][dt]);
       }
     }
-  }
+  };
+
+  prefetch(visit[0]);
+  if (visit[0] != it) fetch_weight(visit[0]);
+  for (int vi = 0; vi + 1 < nvis; ++vi) visit_chunk(vi, std::false_type{});
+  visit_chunk(nvis - 1, std::true_type{});
 
   // ---- normalise and write
 #pragma unroll
@@ -315,17 +358,21 @@ __global__ __launch_bounds__(NW * 64) void k_attend_mfma(AttendArgs a, int tiles
   }
 }
 
+// Shape: 32 query vectors per wave and up to eight waves (two per SIMD, one workgroup per
+// CU), keeping a workgroup inside one 64-row block.  (Four-wave workgroups, two per CU, were
+// measured slower on the 128K workload: the halved K/V tile reuse outweighs the
+// desynchronised barriers.)
 template <int D, bool DENSE>
 static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int NW = G >= 4 ? 8 : 2 * G;  // 32 query vectors per wave
+  const int NW = G >= 4 ? 8 : 2 * G;
   const int R = NW * 32 / G;
   const int tiles = (a.Tq + R - 1) / R;
   dim3 grid(tiles * a.B * a.Hkv);
   switch (NW) {
-    case 8: k_attend_mfma<D, 8, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
-    case 4: k_attend_mfma<D, 4, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
-    default: k_attend_mfma<D, 2, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
+    case 8: k_attend_mfma<D, 8, 64, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
+    case 4: k_attend_mfma<D, 4, 64, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
+    default: k_attend_mfma<D, 2, 64, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
   }
   return hipGetLastError();
 }
