@@ -41,7 +41,12 @@ namespace dash {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
-constexpr float kSlack = 8.0f;      // log2 of the largest unnormalised probability kept
+// A lane's 16 unnormalised probabilities of a chunk may sum to at most 2^8 before the
+// column's reference max is raised; a larger sum, an overflow or a NaN triggers the rescale.
+constexpr float kSumCap = 256.0f;
+// dword 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, offsets in
+// bytes, bounds checked against the record count)
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -176,26 +181,35 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     }
   }
 
-  // ---- global -> register prefetch of one chunk's K and V^T tiles.  Both loads are
-  // written as bounds-checked selects: as plain assignments the compiler keeps the arrays
-  // in scratch memory.
+  // ---- global -> register prefetch of one chunk's K and V^T tiles through buffer
+  // descriptors rebased per chunk (scalar arithmetic only; each thread's byte offsets are
+  // fixed).  A K descriptor's range ends at the last key, so rows past the end of the
+  // sequence read as zeros; they only occur in the diagonal chunk, where they are masked.
   const bf16* kbase = (const bf16*)a.k + (size_t)bk * a.Tk * D;
   const bf16* vtbase = (const bf16*)a.vt + (size_t)bk * a.nc * D * 64;
-  uint4 kreg[KPT], vreg[VPT];
-  auto prefetch = [&](int c) {
+  int koff[KPT], voff[VPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int seg = tid + i * NT;
-      const int row = seg / (D / 8), col = (seg % (D / 8)) * 8;
-      const int key = c * kChunk + row;
-      kreg[i] = key < a.Tk ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col)
-                           : make_uint4(0, 0, 0, 0);
-    }
-    const bf16* vsrc = vtbase + (size_t)c * D * 64;
+  for (int i = 0; i < KPT; ++i) {
+    const int seg = tid + i * NT;
+    koff[i] = (seg / (D / 8) * D + (seg % (D / 8)) * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) voff[i] = (tid + i * NT) * 16;
+  uint4 kreg[KPT], vreg[VPT];
+  auto prefetch = [&](int c_any) {
+    const int c = __builtin_amdgcn_readfirstlane(c_any);
+    const int keys_left = a.Tk - c * kChunk;            // > 0 for every visited chunk
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)c * kChunk * D), (short)0, min(keys_left, kChunk) * D * 2,
+        kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vtbase + (size_t)c * D * 64), (short)0, D * 64 * 2, kBufferRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      vreg[i] = c < a.nc ? *reinterpret_cast<const uint4*>(vsrc + (tid + i * NT) * 8)
-                         : make_uint4(0, 0, 0, 0);
+      vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -232,9 +246,9 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // m: the reference maximum of each query column (base-2 logits).  It is only raised when
-  // a chunk's maximum exceeds it by more than kSlack, so most chunks skip the rescale of
-  // O and l; probabilities relative to it stay below 2^kSlack.
+  // m: the reference maximum of each query column (base-2 logits), only raised when a
+  // chunk's probabilities relative to it grow too large, so most chunks skip the rescale
+  // of O and l.
   float m[2] = {kNegBig, kNegBig}, lsum[2] = {0.f, 0.f};
   const float sl2 = a.scale_log2;
   const int tloc[2] = {(row0 + qrow[0]) & 63, (row0 + qrow[1]) & 63};
@@ -275,12 +289,13 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
       }
     }
 
-    // online softmax per query column; build P^T operands
+    // online softmax per query column; build P^T operands.  Probabilities are taken
+    // relative to the column's reference max m; the max of the chunk is only computed when
+    // a lane's partial sum exceeds kSumCap (or is not a number), which also catches
+    // the first visited chunk, where m is still the initial large negative value.
     bf16x8 pop[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      // raw scores (keys past the row masked on the diagonal); the logit max follows from
-      // the raw max because the scale is positive and the bias is constant per column
       float x[16];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -289,25 +304,33 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
           const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
           x[4 * kt + j] = (DIAG && key > tloc[qt]) ? -INFINITY : sc[qt][kt][j];
         }
-      float mr = fmaxf(fmaxf(x[0], x[1]), x[2]);
+      float pr[16];
+      float off = bias[qt] - m[qt];
+      float ps = 0.f;
 #pragma unroll
-      for (int i = 3; i < 15; i += 2) mr = fmaxf(fmaxf(mr, x[i]), x[i + 1]);
-      mr = rowgroup_max(fmaxf(mr, x[15]));
-      const float cand = fmaf(mr, sl2, bias[qt]);
-      if (__builtin_amdgcn_ballot_w64(cand > m[qt] + kSlack) != 0ull) {
-        const float mn = fmaxf(m[qt], cand);
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = fast_exp2(fmaf(x[i], sl2, off));
+        ps += pr[i];
+      }
+      if (__builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0ull) {
+        // raise the reference max to this chunk's max logit, rescale O and l, redo p
+        float mr = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mr = fmaxf(fmaxf(mr, x[i]), x[i + 1]);
+        mr = rowgroup_max(fmaxf(mr, x[15]));
+        const float mn = fmaxf(m[qt], fmaf(mr, sl2, bias[qt]));
         const float corr = fast_exp2(m[qt] - mn);
         m[qt] = mn;
         lsum[qt] *= corr;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
-      }
-      const float off = bias[qt] - m[qt];
-      float ps = 0.f;
+        off = bias[qt] - mn;
+        ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = fast_exp2(fmaf(x[i], sl2, off));
-        ps += x[i];
+        for (int i = 0; i < 16; ++i) {
+          pr[i] = fast_exp2(fmaf(x[i], sl2, off));
+          ps += pr[i];
+        }
       }
       lsum[qt] += ps;
 #pragma unroll
@@ -315,8 +338,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
         bf16x8 v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[j] = (bf16)x[8 * p + j];          // half 0: keys 32p + 8 lg + j
-          v[4 + j] = (bf16)x[8 * p + 4 + j];  // half 1: keys 32p + 8 lg + 4 + j
+          v[j] = (bf16)pr[8 * p + j];          // half 0: keys 32p + 8 lg + j
+          v[4 + j] = (bf16)pr[8 * p + 4 + j];  // half 1: keys 32p + 8 lg + 4 + j
         }
         pop[qt][p] = v;
       }
