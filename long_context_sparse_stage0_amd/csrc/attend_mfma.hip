@@ -36,6 +36,7 @@
 
 #include "dash_internal.h"
 
+
 namespace dash {
 
 namespace {
@@ -80,8 +81,8 @@ __device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 3); }
 
 }  // namespace
 
-template <int D, int NW, int RMAX, bool DENSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW, int QT, int RMAX, bool DENSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 4 : 2)))
 void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   constexpr int NT = NW * 64;
   constexpr int KS = D / 32;          // k-steps of the QK^T contraction
@@ -90,8 +91,13 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   constexpr int VP = 64 * 2;          // V^T row pitch in LDS (bytes), chunks swizzled
   constexpr int KBYTES = 64 * KP, VBYTES = D * VP;
   constexpr int KSEG = 64 * D / 8, VSEG = D * 8;       // 16-byte segments per tile
-  constexpr int KPT = KSEG / NT, VPT = VSEG / NT;
-  static_assert(KSEG % NT == 0 && VSEG % NT == 0, "tile loads must cover every thread evenly");
+  // each thread moves KPT K segments and VPT V^T segments per chunk; with fewer K segments
+  // than threads, the first KSEG threads move K and the others V^T (one segment each)
+  constexpr bool SPLIT = KSEG < NT;
+  static_assert(SPLIT ? (KSEG + VSEG == NT) : (KSEG % NT == 0 && VSEG % NT == 0),
+                "tile loads must cover every thread evenly");
+  constexpr int KPT = SPLIT ? 1 : KSEG / NT, VPT = SPLIT ? 0 : VSEG / NT;
+  constexpr int VPTA = VPT > 0 ? VPT : 1;
   constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
@@ -101,7 +107,7 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   __shared__ int woff[MAXW + 1];
 
   const int G = a.Hq / a.Hkv;
-  const int R = NW * 32 / G;                 // rows per workgroup (<= 64, divides 64)
+  const int R = NW * 16 * QT / G;            // rows per workgroup (<= 64, divides 64)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   // heavy tiles (late rows) first: the hardware dispatches workgroups roughly in order
@@ -159,14 +165,14 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   __syncthreads();
   const int nvis = woff[nw_route] + 1;
 
-  // ---- this lane's two query columns
+  // ---- this lane's query columns (one per 16-column query tile of the wave)
   const int l16 = lane & 15, lg = lane >> 4;
-  int qrow[2], qh[2];
-  bool qok[2];
-  bf16x8 qop[2][KS];
+  int qrow[QT], qh[QT];
+  bool qok[QT];
+  bf16x8 qop[QT][KS];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int n = 32 * wv + 16 * qt + l16;
+  for (int qt = 0; qt < QT; ++qt) {
+    const int n = 16 * QT * wv + 16 * qt + l16;
     const int r = n / G, g = n % G;
     qrow[qt] = r;
     qh[qt] = kvh * G + g;
@@ -187,15 +193,18 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   // sequence read as zeros; they only occur in the diagonal chunk, where they are masked.
   const bf16* kbase = (const bf16*)a.k + (size_t)bk * a.Tk * D;
   const bf16* vtbase = (const bf16*)a.vt + (size_t)bk * a.nc * D * 64;
-  int koff[KPT], voff[VPT];
+  // this thread's K half (wave-uniform) in the split layout
+  const bool kpart = !SPLIT || __builtin_amdgcn_readfirstlane(tid) < KSEG;
+  const int vseg0 = SPLIT ? tid - KSEG : tid;
+  int koff[KPT], voff[VPTA];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int seg = tid + i * NT;
     koff[i] = (seg / (D / 8) * D + (seg % (D / 8)) * 8) * 2;
   }
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) voff[i] = (tid + i * NT) * 16;
-  uint4 kreg[KPT], vreg[VPT];
+  for (int i = 0; i < VPTA; ++i) voff[i] = (vseg0 + i * NT) * 16;
+  uint4 kreg[KPT], vreg[VPTA];
   auto prefetch = [&](int c_any) {
     const int c = __builtin_amdgcn_readfirstlane(c_any);
     const int keys_left = a.Tk - c * kChunk;            // > 0 for every visited chunk
@@ -204,6 +213,11 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
         kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtbase + (size_t)c * D * 64), (short)0, D * 64 * 2, kBufferRsrcWord3);
+    if (SPLIT) {
+      kreg[0] = __builtin_bit_cast(uint4, kpart ? __builtin_amdgcn_raw_buffer_load_b128(kr, koff[0], 0, 0)
+                                                : __builtin_amdgcn_raw_buffer_load_b128(vr, voff[0], 0, 0));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
@@ -211,7 +225,15 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     for (int i = 0; i < VPT; ++i)
       vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
   };
+  auto stash_v = [&](int buf, int seg, const uint4& val) {
+    const int row = seg / 8, ch = seg % 8;
+    *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + (ch ^ vswz(row)) * 16]) = val;
+  };
   auto stash = [&](int buf) {
+    if (SPLIT && !kpart) {
+      stash_v(buf, vseg0, kreg[0]);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int seg = tid + i * NT;
@@ -219,21 +241,22 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
       *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + (ch ^ kswz<D>(row)) * 16]) = kreg[i];
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int seg = tid + i * NT;
-      const int row = seg / 8, ch = seg % 8;
-      *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + (ch ^ vswz(row)) * 16]) = vreg[i];
-    }
+    for (int i = 0; i < VPT; ++i) stash_v(buf, vseg0 + i * NT, vreg[i]);
   };
-  // routing weight and mask bit of this lane's two rows for routed chunk c; the weight is
+  // routing weight and mask bit of this lane's rows for routed chunk c; the weight is
   // loaded one visit ahead and only turned into a bias (log2 w, or -inf where the row's bit
   // is clear) when the visit starts, so no wait on it stalls the tile prefetch
-  float wnext[2] = {1.f, 1.f};
-  bool onnext[2] = {true, true};
+  float wnext[QT];
+  bool onnext[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    wnext[qt] = 1.f;
+    onnext[qt] = true;
+  }
   auto fetch_weight = [&](int c) {
     if (DENSE) return;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const int r = qrow[qt];
       onnext[qt] = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
       const int t = min(row0 + r, a.rows - 1);
@@ -241,26 +264,32 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     }
   };
 
-  floatx4 o[2][NDT];
+  floatx4 o[QT][NDT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   // m: the reference maximum of each query column (base-2 logits), only raised when a
   // chunk's probabilities relative to it grow too large, so most chunks skip the rescale
   // of O and l.
-  float m[2] = {kNegBig, kNegBig}, lsum[2] = {0.f, 0.f};
+  float m[QT], lsum[QT];
+  int tloc[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = kNegBig;
+    lsum[qt] = 0.f;
+    tloc[qt] = (row0 + qrow[qt]) & 63;
+  }
   const float sl2 = a.scale_log2;
-  const int tloc[2] = {(row0 + qrow[0]) & 63, (row0 + qrow[1]) & 63};
 
   // one visit of chunk visit[vi]; DIAG: the query block's own chunk (always the last visit)
   auto visit_chunk = [&](int vi, auto diag_tag) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     const int buf = vi & 1;
     stash(buf);
-    float bias[2];
+    float bias[QT];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
       bias[qt] = (DIAG || DENSE) ? 0.f : (onnext[qt] ? fast_log2(wnext[qt]) : -INFINITY);
     __syncthreads();
     if (!DIAG) {
@@ -272,20 +301,20 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     const uint8_t* vl = lds_v[buf];
 
     // S^T for 64 keys: tile kt = 2 p + half
-    floatx4 sc[2][4];
+    floatx4 sc[QT][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int p = kt >> 1, half = kt & 1;
       const int key = 32 * p + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
       const int ksw = kswz<D>(key);        // p and half do not change the swizzle
-      sc[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      sc[1][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sc[qt][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(kl + key * KP + ((4 * ks + lg) ^ ksw) * 16);
-        sc[0][kt] = mfma16(ka, qop[0][ks], sc[0][kt]);
-        sc[1][kt] = mfma16(ka, qop[1][ks], sc[1][kt]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sc[qt][kt] = mfma16(ka, qop[qt][ks], sc[qt][kt]);
       }
     }
 
@@ -293,9 +322,9 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     // relative to the column's reference max m; the max of the chunk is only computed when
     // a lane's partial sum exceeds kSumCap (or is not a number), which also catches
     // the first visited chunk, where m is still the initial large negative value.
-    bf16x8 pop[2][2];
+    bf16x8 pop[QT][2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       float x[16];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -352,8 +381,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
       for (int p = 0; p < 2; ++p) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(
             vl + (16 * dt + l16) * VP + ((4 * p + lg) ^ vswz(l16)) * 16);
-        o[0][dt] = mfma16(va, pop[0][p], o[0][dt]);
-        o[1][dt] = mfma16(va, pop[1][p], o[1][dt]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mfma16(va, pop[qt][p], o[qt][dt]);
       }
     }
   };
@@ -365,7 +394,7 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
 
   // ---- normalise and write
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const float l = xor16_sum(lsum[qt]);
     const float rl = 1.0f / l;
     if (!qok[qt]) continue;
@@ -381,10 +410,11 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   }
 }
 
-// Shape: 32 query vectors per wave and up to eight waves (two per SIMD, one workgroup per
-// CU), keeping a workgroup inside one 64-row block.  (Four-wave workgroups, two per CU, were
-// measured slower on the 128K workload: the halved K/V tile reuse outweighs the
-// desynchronised barriers.)
+// Shape: two 16-column query tiles per wave and up to eight waves (two per SIMD, one
+// workgroup per CU), keeping a workgroup inside one 64-row block.  The two tiles share
+// every K and V^T operand read from LDS.  (One tile per wave at four waves per SIMD, the
+// same 256 query vectors per workgroup, was measured slower on the 128K workload: twice
+// the LDS operand traffic per MFMA outweighs the higher occupancy.)
 template <int D, bool DENSE>
 static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
@@ -393,9 +423,9 @@ static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
   const int tiles = (a.Tq + R - 1) / R;
   dim3 grid(tiles * a.B * a.Hkv);
   switch (NW) {
-    case 8: k_attend_mfma<D, 8, 64, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
-    case 4: k_attend_mfma<D, 4, 64, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
-    default: k_attend_mfma<D, 2, 64, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
+    case 8: k_attend_mfma<D, 8, 2, 64, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
+    case 4: k_attend_mfma<D, 4, 2, 64, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
+    default: k_attend_mfma<D, 2, 2, 64, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
   }
   return hipGetLastError();
 }
