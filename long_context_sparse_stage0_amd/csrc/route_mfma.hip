@@ -25,11 +25,16 @@
 // same totals for all 32 queries and takes the same decision.
 // GQA average: the G heads of a row are G adjacent columns of a 16-lane row, summed with
 // DPP (quad permutes, half-row and row mirrors) in a fixed order.
+#include <algorithm>
+
 #include "route_common.h"
 
 namespace dash {
 
 namespace {
+
+// 64-bit mask words per row that can hold routed chunks (plus one spare)
+constexpr int kRouteMaskWords = (kMaxRouted + 63) / 64 + 1;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -64,27 +69,19 @@ __device__ __forceinline__ float xg_max(float v) {
 
 }  // namespace
 
+// One workgroup's routing with MT chunk tiles per wave (MT = ceil(ntile / NW), chosen per
+// workgroup so short rows do not pay for the longest row's tile count).
 template <int D, int NW, int MT, int MODE>
-__global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit) {
-  constexpr int NT = NW * 64, KS = D / 32, NQ = 4;  // NQ reduced quantities per pass
-  constexpr int MAXW = (kMaxRouted + 63) / 64 + 1;
-  __shared__ float part[2][2][NQ][16][NW];
-  __shared__ unsigned long long mbits[32][MAXW];
-
+__device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __restrict__ ssplit,
+                                           float (&part)[2][2][4][16][NW],
+                                           uint16_t (&mbits16)[32][4 * kRouteMaskWords],
+                                           int bk, int row0, int it, int ntile) {
+  constexpr int KS = D / 32;
   const int G = a.Hq / a.Hkv;
-  const int R = 32 / G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int tile = gridDim.x - 1 - blockIdx.x;      // late (heavy) rows first
-  const int BH = a.B * a.Hkv;
-  const int rt = tile / BH, bk = tile % BH;
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
-  const int row0 = rt * R;
-  const int it = row0 / kChunk;                     // routed chunks c < it for every row
   const int T = a.Tq;
-  const int W = a.W;
-
-  for (int i = tid; i < 32 * MAXW; i += NT) (&mbits[0][0])[i] = 0ull;
 
   // queries of this lane: column l16 of query tiles 0 and 1
   bf16x8 qop[2][KS];
@@ -101,7 +98,6 @@ __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16*
   }
 
   // scores
-  const int ntile = (it + 15) / 16;
   const bf16* sp = ssplit + (size_t)bk * a.nc_alloc * 2 * D;
   float y[MT][2][4];
 #pragma unroll
@@ -132,8 +128,7 @@ __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16*
     }
   }
 
-  // tiles owned by this wave: wv, wv + 8, ... below ntile (wave-uniform, so the per-tile
-  // blocks below are skipped by scalar branches)
+  // tiles owned by this wave: wv, wv + NW, ... below ntile (wave-uniform)
   const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
 
   // ---- threshold solver for the 32 queries
@@ -274,65 +269,143 @@ __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16*
     }
   }
 
-  // ---- weights, GQA average, mask bits, w_bar at set bits
+  // ---- weights, GQA average, w_bar at active chunks, mask bits.  After the head sum all
+  // G lanes of a row hold the same averaged weights; lane g of the row stores chunk slots
+  // jj = g, g + G, ... (coalesced 16-chunk runs), and each row's 16 mask bits of a tile are
+  // gathered from the four 16-lane groups and stored as one 16-bit word.
   if (it > 0) {
     const float rG = 1.0f / (float)G;
-    const size_t rbase = (size_t)bk * a.rows + row0;
+    const int g = l16 % G;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const float rz = 1.0f / zs[qt];
-      const bool writer = (l16 % G) == 0 && (row0 + qrow[qt]) < T;
+      const int r = qrow[qt];
+      const bool row_ok = (row0 + r) < T;
+      float* wrow = a.wbar + ((size_t)bk * a.rows + row0 + r) * a.wbar_ld;
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
-        const int ct = wv + NW * j;
         if (j >= nj) continue;
+        const int ct = wv + NW * j;
+        const int c0 = 16 * ct + 4 * lg;
+        float wb[4];
+        unsigned nib = 0;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float p = entmax_weight<MODE>(y[j][qt][jj], tau[qt], inv, rz);
-          const float wb = head_sum(p, G) * rG;
-          const int c = 16 * ct + 4 * lg + jj;
-          if (writer && wb > 0.f && c < it) {
-            a.wbar[(rbase + qrow[qt]) * a.wbar_ld + c] = wb;
-            atomicOr(&mbits[qrow[qt]][c >> 6], 1ull << (c & 63));
-          }
+          const float pw = entmax_weight<MODE>(y[j][qt][jj], tau[qt], inv, rz);
+          wb[jj] = head_sum(pw, G) * rG;
+          nib |= (wb[jj] > 0.f && c0 + jj < it) ? (1u << jj) : 0u;
         }
+        // w_bar stores: this lane's slots jj = g + G s
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int jj = g + G * s;
+          if (jj >= 4) break;
+          const float v = jj == 0 ? wb[0] : jj == 1 ? wb[1] : jj == 2 ? wb[2] : wb[3];
+          if (row_ok && ((nib >> jj) & 1u)) wrow[c0 + jj] = v;
+        }
+        // mask bits of the row for chunks 16 ct + [0, 16)
+        unsigned f = nib << (4 * lg);
+        {
+          const auto x = __builtin_amdgcn_permlane16_swap(f, f, false, false);
+          f = x[0] | x[1];
+          const auto y2 = __builtin_amdgcn_permlane32_swap(f, f, false, false);
+          f = y2[0] | y2[1];
+        }
+        if (lg == 0 && g == 0) mbits16[r][ct] = (uint16_t)f;
       }
     }
   }
+}
+
+template <int D, int NW, int MT, int MODE>
+__global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit,
+                                                        int rt_lo, int rt_n) {
+  constexpr int NT = NW * 64;
+  __shared__ float part[2][2][4][16][NW];
+  __shared__ uint16_t mbits16[32][4 * kRouteMaskWords];
+
+  const int G = a.Hq / a.Hkv;
+  const int R = 32 / G;
+  const int tid = threadIdx.x;
+  const int tile = gridDim.x - 1 - blockIdx.x;      // late (heavy) rows first
+  const int BH = a.B * a.Hkv;
+  const int rt = rt_lo + tile / BH, bk = tile % BH;
+  const int row0 = rt * R;
+  const int it = row0 / kChunk;                     // routed chunks c < it for every row
+  const int T = a.Tq;
+  const int W = a.W;
+  const int ntile = (it + 15) / 16;
+  (void)rt_n;
+
+  uint32_t* m32 = reinterpret_cast<uint32_t*>(&mbits16[0][0]);
+  for (int i = tid; i < 32 * 2 * kRouteMaskWords; i += NT) m32[i] = 0u;
   __syncthreads();
+  route_rows<D, NW, MT, MODE>(a, ssplit, part, mbits16, bk, row0, it, ntile);
+  __syncthreads();
+  const uint64_t* mrow = reinterpret_cast<const uint64_t*>(&mbits16[0][0]);
   for (int idx = tid; idx < R * W; idx += NT) {
     const int r = idx / W, w = idx % W;
-    if (row0 + r < T) a.mask[((size_t)bk * a.rows + row0 + r) * W + w] = (w < MAXW) ? mbits[r][w] : 0ull;
+    if (row0 + r < T)
+      a.mask[((size_t)bk * a.rows + row0 + r) * W + w] =
+          (w < kRouteMaskWords) ? mrow[r * kRouteMaskWords + w] : 0ull;
   }
 }
 
 template <int D, int NW, int MT>
-static void launch_mt(const RouteArgs& a, const bf16* ss, dim3 grid, hipStream_t s) {
+static void launch_mt(const RouteArgs& a, const bf16* ss, int rt_lo, int rt_n, hipStream_t s) {
+  dim3 grid(rt_n * a.B * a.Hkv);
   if (a.alpha == 1.5f)
-    k_route_mfma<D, NW, MT, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
   else if (a.alpha == 2.0f)
-    k_route_mfma<D, NW, MT, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
   else
-    k_route_mfma<D, NW, MT, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss);
+    k_route_mfma<D, NW, MT, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+}
+
+// Eight waves while every row has at most 8 chunk tiles (128 chunks), sixteen beyond.  The
+// row tiles are split into contiguous ranges by the number of chunk tiles each wave holds
+// (MT = ceil(ntile / NW)), one launch per range, heaviest first, so short rows do not pay
+// for the longest row's registers and loop trip counts.
+template <int D, int NW>
+static void launch_nw(const RouteArgs& a, const bf16* ss, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int R = 32 / G;
+  const int nrt = (a.Tq + R - 1) / R;
+  int hi[9];
+  hi[0] = 0;
+  for (int mt = 1; mt <= 8; ++mt) {
+    // rows with it <= 16 * NW * mt, i.e. row0 < 64 * (16 * NW * mt + 1)
+    const long long lim = (64LL * (16LL * NW * mt + 1) + R - 1) / R;
+    hi[mt] = (int)std::min<long long>(nrt, lim);
+  }
+  hi[8] = nrt;
+  for (int mt = 8; mt >= 1; --mt) {
+    const int lo = hi[mt - 1], n = hi[mt] - lo;
+    if (n <= 0) continue;
+    switch (mt) {
+      case 1: launch_mt<D, NW, 1>(a, ss, lo, n, s); break;
+      case 2: launch_mt<D, NW, 2>(a, ss, lo, n, s); break;
+      case 3: launch_mt<D, NW, 3>(a, ss, lo, n, s); break;
+      case 4: launch_mt<D, NW, 4>(a, ss, lo, n, s); break;
+      case 5: launch_mt<D, NW, 5>(a, ss, lo, n, s); break;
+      case 6: launch_mt<D, NW, 6>(a, ss, lo, n, s); break;
+      case 7: launch_mt<D, NW, 7>(a, ss, lo, n, s); break;
+      default: launch_mt<D, NW, 8>(a, ss, lo, n, s); break;
+    }
+  }
 }
 
 template <int D>
-static void launch_d(const RouteArgs& a, const bf16* ss, dim3 grid, hipStream_t s) {
+static void launch_d(const RouteArgs& a, const bf16* ss, hipStream_t s) {
   const int max_it = (a.Tq - 1) / kChunk;
   const int tiles = (max_it + 15) / 16;
-  if (tiles <= 8) launch_mt<D, 8, 1>(a, ss, grid, s);
-  else if (tiles <= 16) launch_mt<D, 8, 2>(a, ss, grid, s);
-  else if (tiles <= 32) launch_mt<D, 8, 4>(a, ss, grid, s);
-  else if (tiles <= 64) launch_mt<D, 8, 8>(a, ss, grid, s);
-  else launch_mt<D, 16, 8>(a, ss, grid, s);
+  if (tiles <= 8) launch_nw<D, 8>(a, ss, s);
+  else launch_nw<D, 16>(a, ss, s);
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int R = 32 / G;
-  dim3 grid(((a.Tq + R - 1) / R) * a.B * a.Hkv);
-  if (a.D == 128) launch_d<128>(a, (const bf16*)summ_split, grid, s);
-  else launch_d<64>(a, (const bf16*)summ_split, grid, s);
+  if (a.D == 128) launch_d<128>(a, (const bf16*)summ_split, s);
+  else launch_d<64>(a, (const bf16*)summ_split, s);
   return hipGetLastError();
 }
 
