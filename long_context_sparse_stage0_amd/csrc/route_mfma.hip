@@ -54,17 +54,24 @@ __device__ __forceinline__ float head_sum(float v, int G) {
   return v;
 }
 
+// reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap moves: permlane16_swap(v, v) gives each lane the values of rows {2i, 2i+1} of
+// its row pair, permlane32_swap(v, v) those of the lower and the upper half-wave
+template <typename Op>
+__device__ __forceinline__ float xg_reduce(float v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float xg_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  return xg_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ float xg_min(float v) {
-  v = fminf(v, __shfl_xor(v, 16, 64));
-  return fminf(v, __shfl_xor(v, 32, 64));
+  return xg_reduce(v, [](float x, float y) { return fminf(x, y); });
 }
 __device__ __forceinline__ float xg_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  return xg_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 }  // namespace
@@ -362,45 +369,51 @@ static void launch_mt(const RouteArgs& a, const bf16* ss, int rt_lo, int rt_n, h
     k_route_mfma<D, NW, MT, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
 }
 
-// Eight waves while every row has at most 8 chunk tiles (128 chunks), sixteen beyond.  The
-// row tiles are split into contiguous ranges by the number of chunk tiles each wave holds
-// (MT = ceil(ntile / NW)), one launch per range, heaviest first, so short rows do not pay
-// for the longest row's registers and loop trip counts.
-template <int D, int NW>
-static void launch_nw(const RouteArgs& a, const bf16* ss, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int R = 32 / G;
-  const int nrt = (a.Tq + R - 1) / R;
-  int hi[9];
-  hi[0] = 0;
-  for (int mt = 1; mt <= 8; ++mt) {
-    // rows with it <= 16 * NW * mt, i.e. row0 < 64 * (16 * NW * mt + 1)
-    const long long lim = (64LL * (16LL * NW * mt + 1) + R - 1) / R;
-    hi[mt] = (int)std::min<long long>(nrt, lim);
-  }
-  hi[8] = nrt;
-  for (int mt = 8; mt >= 1; --mt) {
-    const int lo = hi[mt - 1], n = hi[mt] - lo;
-    if (n <= 0) continue;
-    switch (mt) {
-      case 1: launch_mt<D, NW, 1>(a, ss, lo, n, s); break;
-      case 2: launch_mt<D, NW, 2>(a, ss, lo, n, s); break;
-      case 3: launch_mt<D, NW, 3>(a, ss, lo, n, s); break;
-      case 4: launch_mt<D, NW, 4>(a, ss, lo, n, s); break;
-      case 5: launch_mt<D, NW, 5>(a, ss, lo, n, s); break;
-      case 6: launch_mt<D, NW, 6>(a, ss, lo, n, s); break;
-      case 7: launch_mt<D, NW, 7>(a, ss, lo, n, s); break;
-      default: launch_mt<D, NW, 8>(a, ss, lo, n, s); break;
-    }
-  }
+// Workgroup shapes by the number of 16-chunk tiles a row tile routes over: the fewest
+// waves (NW) that hold every tile with at most 8 tiles per wave, and MT = ceil(ntile/NW).
+// Light rows then run in small workgroups, several per CU, which hide each other's
+// barrier and memory latency; only rows with more than 1024 routed chunks need sixteen.
+// Row tiles are contiguous per shape (i_t grows with the row), one launch each, heaviest
+// first.
+struct RouteShape { int nw, mt; };
+constexpr RouteShape kRouteShapes[] = {
+    {1, 1}, {1, 2}, {1, 3}, {1, 4}, {1, 5}, {1, 6}, {1, 7}, {1, 8},
+    {2, 5}, {2, 6}, {2, 7}, {2, 8}, {4, 5}, {4, 6}, {4, 7}, {4, 8},
+    {8, 5}, {8, 6}, {8, 7}, {8, 8}, {16, 5}, {16, 6}, {16, 7}, {16, 8}};
+
+template <int D, int I>
+static void launch_shape(const RouteArgs& a, const bf16* ss, int lo, int n, hipStream_t s) {
+  launch_mt<D, kRouteShapes[I].nw, kRouteShapes[I].mt>(a, ss, lo, n, s);
 }
 
 template <int D>
 static void launch_d(const RouteArgs& a, const bf16* ss, hipStream_t s) {
-  const int max_it = (a.Tq - 1) / kChunk;
-  const int tiles = (max_it + 15) / 16;
-  if (tiles <= 8) launch_nw<D, 8>(a, ss, s);
-  else launch_nw<D, 16>(a, ss, s);
+  const int G = a.Hq / a.Hkv;
+  const int R = 32 / G;
+  const int nrt = (a.Tq + R - 1) / R;
+  constexpr int NS = sizeof(kRouteShapes) / sizeof(kRouteShapes[0]);
+  int hi[NS + 1];
+  hi[0] = 0;
+  for (int i = 0; i < NS; ++i) {
+    // row tiles whose ntile fits the shape's capacity: i_t <= 16 cap, i.e. row0 < 64 (16 cap + 1)
+    const long long cap = (long long)kRouteShapes[i].nw * kRouteShapes[i].mt;
+    const long long lim = (64LL * (16LL * cap + 1) + R - 1) / R;
+    hi[i + 1] = (int)std::min<long long>(nrt, lim);
+  }
+  hi[NS] = nrt;
+  using Fn = void (*)(const RouteArgs&, const bf16*, int, int, hipStream_t);
+  static const Fn fns[NS] = {
+      launch_shape<D, 0>, launch_shape<D, 1>, launch_shape<D, 2>, launch_shape<D, 3>,
+      launch_shape<D, 4>, launch_shape<D, 5>, launch_shape<D, 6>, launch_shape<D, 7>,
+      launch_shape<D, 8>, launch_shape<D, 9>, launch_shape<D, 10>, launch_shape<D, 11>,
+      launch_shape<D, 12>, launch_shape<D, 13>, launch_shape<D, 14>, launch_shape<D, 15>,
+      launch_shape<D, 16>, launch_shape<D, 17>, launch_shape<D, 18>, launch_shape<D, 19>,
+      launch_shape<D, 20>, launch_shape<D, 21>, launch_shape<D, 22>, launch_shape<D, 23>};
+  for (int i = NS - 1; i >= 0; --i) {
+    const int lo = std::max(hi[i], i > 0 ? hi[i - 1] : 0);
+    const int n = hi[i + 1] - lo;
+    if (n > 0) fns[i](a, ss, lo, n, s);
+  }
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s) {
