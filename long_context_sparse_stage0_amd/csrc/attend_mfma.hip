@@ -42,6 +42,7 @@ namespace dash {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
+constexpr int kXcds = 8;            // accelerator complex dies; workgroups are dealt round-robin
 // A lane's 16 unnormalised probabilities of a chunk may sum to at most 2^8 before the
 // column's reference max is raised; a larger sum, an overflow or a NaN triggers the rescale.
 constexpr float kSumCap = 256.0f;
@@ -110,10 +111,20 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   const int R = NW * 16 * QT / G;            // rows per workgroup (<= 64, divides 64)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // heavy tiles (late rows) first: the hardware dispatches workgroups roughly in order
-  const int tile = gridDim.x - 1 - blockIdx.x;
+  // Workgroup -> (64-row query block, b, kv head, row tile).  Consecutive workgroups are
+  // dealt round-robin to the 8 XCDs; a group of 8 * RPB consecutive workgroups gives each
+  // XCD the RPB row tiles of one query block, which share nearly the same mask and so read
+  // the same K/V tiles through that XCD's L2.  Blocks go heavy (late rows) first.
   const int BH = a.B * a.Hkv;
-  const int rt = tile / BH, bk = tile % BH;
+  const int RPB = kChunk / R;                // row tiles per 64-row block
+  const int nunits = ((a.Tq + kChunk - 1) / kChunk) * BH;
+  const int grp = kXcds * RPB;
+  const int xcd = (blockIdx.x % grp) % kXcds, sub = (blockIdx.x % grp) / kXcds;
+  const int unit = (blockIdx.x / grp) * kXcds + xcd;
+  if (unit >= nunits) return;                // padding of the last group (whole workgroup)
+  const int uu = nunits - 1 - unit;
+  const int bk = uu % BH;
+  const int rt = (uu / BH) * RPB + sub;
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int row0 = rt * R;
   const int it = row0 / kChunk;              // diagonal chunk, shared by all R rows
@@ -421,7 +432,8 @@ static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
   const int NW = G >= 4 ? 8 : 2 * G;
   const int R = NW * 32 / G;
   const int tiles = (a.Tq + R - 1) / R;
-  dim3 grid(tiles * a.B * a.Hkv);
+  const int nunits = ((a.Tq + kChunk - 1) / kChunk) * a.B * a.Hkv;
+  dim3 grid(((nunits + kXcds - 1) / kXcds) * kXcds * (kChunk / R));
   switch (NW) {
     case 8: k_attend_mfma<D, 8, 2, 64, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
     case 4: k_attend_mfma<D, 4, 2, 64, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;

@@ -10,8 +10,9 @@ Two steps, the first run twice under rocprofv3 (one counter per pass):
     python3 -m long_context_sparse_stage0_amd.traffic summarize gpurun_out/traffic
 
 `run` launches, on the 128K prefill workload, the full prefill once (to build the mask and
-the weights), then Stage 2 alone three times, then a plain device-to-device copy of
-1 GiB (the calibration kernel: 1 GiB read, 1 GiB written).  `summarize` reads the
+the weights), then Stage 2 alone three times, then, as the last dispatch, a plain
+elementwise copy (dst = src + 1) of 1 GiB of fp32: one dispatch that reads 1 GiB and
+writes 1 GiB, the calibration kernel.  `summarize` reads the
 per-dispatch FETCH_SIZE / WRITE_SIZE (KiB), scales each counter by (known copy bytes /
 the copy's counter reading), and writes profiles/stage2_traffic.json (read by bench.py,
 tagged with the hash of the Stage 2 source so a changed kernel invalidates it) and a short
@@ -59,7 +60,7 @@ def run():
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    dst.copy_(src)
+    torch.add(src, 1.0, out=dst)        # calibration: one dispatch, 1 GiB read + 1 GiB written
     torch.cuda.synchronize()
     print(f"traffic run done ({w.name})", flush=True)
 
@@ -87,10 +88,12 @@ def summarize(base):
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         ds = _dispatches(os.path.join(base, sub), counter)
         st2 = [v for _, n, v in ds if "k_attend_mfma" in n and "true" not in n]
-        other = [(v, n) for _, n, v in ds if "dash::" not in n]
+        other = [(d, v, n) for d, n, v in ds if "dash::" not in n]
         if not st2 or not other:
             raise SystemExit(f"{counter}: no Stage 2 or copy dispatch found in {base}/{sub}")
-        copy_kib, copy_name = max(other)
+        _, copy_kib, copy_name = max(other)      # the last dispatch of the run
+        if "elementwise" not in copy_name:
+            raise SystemExit(f"{counter}: last dispatch is not the calibration copy: {copy_name}")
         factor = (COPY_BYTES / 1024.0) / copy_kib
         # the first Stage 2 dispatch belongs to the full prefill; all are the same work
         kib = sum(st2) / len(st2)
