@@ -187,3 +187,23 @@ def test_decode_steps_with_append(dash):
     ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], rows=rows)
     g = np.stack(outs, axis=2)                       # [B, Hq, steps, D]
     compare_out(g, ref["out"], "bf16", what="decode steps")
+
+
+@pytest.mark.parametrize("T,dtype,G", [(1, "bf16", 4), (63, "bf16", 16), (64, "bf16", 2),
+                                       (65, "bf16", 8), (1, "fp32", 1), (64, "fp32", 2),
+                                       (129, "fp32", 4)])
+def test_prefill_tiny_sequences(dash, T, dtype, G):
+    """Degenerate lengths: a single token, rows that have no routed chunk at all, and the
+    first row that routes over exactly one chunk."""
+    w = Workload(name=f"tiny_{T}", kind="prefill", B=2, Hq=2 * G, Hkv=2, T=T, D=64,
+                 dtype=dtype, seed=700 + T, needle_amp=1.0)
+    check_prefill(run_prefill(dash, w), w)
+
+
+def test_decode_short_sequences(dash):
+    """Decode rows with one token in the cache, a full first chunk (no routed chunk yet) and
+    the first row that routes over one chunk."""
+    w = Workload(name="dec_short", kind="prefill", B=3, Hq=8, Hkv=2, T=200, D=128,
+                 dtype="bf16", seed=34, needle_amp=1.0)
+    say("[parity] decode short sequences")
+    _decode_case(dash, w, [1, 64, 65])
