@@ -121,7 +121,7 @@ PrefillLayout prefill_layout(const Dims& d) {
 }
 
 struct DecodeLayout {
-  size_t mask, wbar, pml, po, total;
+  size_t mask, wbar, list, pml, po, total;
 };
 
 DecodeLayout decode_layout(const Dims& d) {
@@ -131,6 +131,8 @@ DecodeLayout decode_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.W * 8);
   L.wbar = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * 4);
+  L.list = off;
+  off += align256((size_t)d.B * d.Hkv * (d.nc + 2) * 4);
   const size_t nseg = (size_t)dash::decode_nseg_max(d.nc);
   L.pml = off;
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 32 * 4) : 0;
@@ -348,6 +350,8 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   ra.alpha = d.alpha;
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
   ra.dtype = d.dtype;
+  ra.list = reinterpret_cast<int32_t*>(ws + L.list);
+  ra.list_ld = d.nc + 2;
   e = d.dtype == DASH_BF16 ? dash::launch_decode_route(ra, s) : dash::launch_route_valu(ra, s);
   if (e != hipSuccess) return hip_fail(e, "decode route launch");
 
@@ -372,6 +376,8 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   aa.scale_log2 = d.scale * 1.4426950408889634f;
   aa.dtype = d.dtype;
   aa.dense = 0;
+  aa.list = reinterpret_cast<const int32_t*>(ws + L.list);
+  aa.list_ld = d.nc + 2;
   if (d.dtype == DASH_BF16)
     e = dash::launch_decode_attend(aa, reinterpret_cast<float*>(ws + L.pml),
                                    reinterpret_cast<float*>(ws + L.po), s);

@@ -10,6 +10,7 @@ namespace dash {
 constexpr int kChunk = 64;          // tokens per chunk (the pages' only chunk size)
 constexpr int kMaxRouted = 2048;    // routed chunks per row held in registers (32 per lane)
 constexpr int kMaxRoutedRegs = kMaxRouted / 64;
+constexpr int kMaxRoutedWords = kMaxRouted / 64;   // mask words that can hold routed chunks
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +56,8 @@ struct RouteArgs {
   int tcap;               // prefill: T; decode: cache capacity (a query row must be < tcap)
   float alpha, zscale;    // zscale = (alpha - 1) * gamma * sm_scale
   int dtype;
+  int32_t* list;          // decode: [B * Hkv][list_ld]: count, then the active chunks in
+  int list_ld;            // increasing order followed by the diagonal chunk (or nullptr)
 };
 
 struct AttendArgs {
@@ -70,6 +73,8 @@ struct AttendArgs {
   float scale_log2;       // sm_scale * log2(e)
   int dtype;
   int dense;              // 1: every chunk c < i_t active with prior 1 (comparator)
+  const int32_t* list;    // decode: the route kernel's item lists (see RouteArgs)
+  int list_ld;
 };
 
 // summ_split (nullable, bf16 inputs only): [B, Hkv, nc_alloc, 2, D] bf16 hi and lo planes of

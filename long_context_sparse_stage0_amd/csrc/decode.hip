@@ -36,6 +36,9 @@ __device__ __forceinline__ float xg_sum(float v) {
 }
 
 constexpr int kSeg = 16;        // list items per attend workgroup
+// dword 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, offsets in
+// bytes, bounds checked against the record count)
+constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kAttWaves = 4;
 constexpr float kNegBig = -1.0e30f;
 
@@ -113,6 +116,8 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   __syncthreads();
 
   // GQA average in head order, mask words by ballot, w_bar at set bits
+  __shared__ uint64_t wbits[kMaxRoutedWords];
+  __shared__ int wpre[kMaxRoutedWords + 1];
   const float rG = 1.0f / (float)G;
   for (int w = wv; w < a.W; w += NW) {
     const int c = 64 * w + lane;
@@ -123,7 +128,37 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
     const bool on = c < it && wb > 0.f;
     const uint64_t bits = __ballot(on);
     if (on) a.wbar[(size_t)bk * a.wbar_ld + c] = wb;
-    if (lane == 0) a.mask[(size_t)bk * a.W + w] = bits;
+    if (lane == 0) {
+      a.mask[(size_t)bk * a.W + w] = bits;
+      if (w < kMaxRoutedWords) wbits[w] = bits;
+    }
+  }
+  // the attend kernels' work list: count, the set chunks in increasing order, then the
+  // diagonal chunk
+  const int nwr = (it + 63) / 64;                 // words that can hold routed chunks
+  __syncthreads();
+  if (wv == 0) {
+    int v = lane < nwr ? __popcll(wbits[lane]) : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o, 64);
+      if (lane >= o) v += u;
+    }
+    if (lane < nwr) wpre[lane + 1] = v;
+    if (lane == 0) wpre[0] = 0;
+  }
+  __syncthreads();
+  int32_t* lst = a.list + (size_t)bk * a.list_ld;
+  for (int w = wv; w < nwr; w += NW) {
+    const uint64_t bits = wbits[w];
+    if ((bits >> lane) & 1ull) {
+      const uint64_t below = lane ? (bits & ((1ull << lane) - 1ull)) : 0ull;
+      lst[1 + wpre[w] + __popcll(below)] = 64 * w + lane;
+    }
+  }
+  if (tid == 0) {
+    lst[0] = wpre[nwr] + 1;
+    lst[1 + wpre[nwr]] = it;
   }
 }
 
@@ -149,17 +184,14 @@ __device__ __forceinline__ bf16x8 vt_operand(const bf16* tile, int pitch, int k0
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, float* __restrict__ pml,
+__global__ __launch_bounds__(kAttWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void k_decode_attend(AttendArgs a, float* __restrict__ pml,
                                                                   float* __restrict__ po, int nseg_max) {
   constexpr int KS = D / 32, NDT = D / 16;
   constexpr int VP = D + 16;                      // V row pitch in LDS (bf16 elements)
   constexpr int SEGR = D / 8;                     // 16-byte segments per V row
   constexpr int VL = 64 * SEGR / 64;              // segments per lane per tile
-  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
   __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][64 * VP];
-  __shared__ uint64_t wl[MAXW];
-  __shared__ int wpre[MAXW + 1];
-  __shared__ int items[kSeg];
   __shared__ float mrg_ml[kAttWaves][2][16];
 
   const int G = a.Hq / a.Hkv;
@@ -170,37 +202,21 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
   const int t = a.seq_lens[b] - 1;
   if (t < 0 || t >= a.Tk) return;                 // the combine kernel writes NaN
   const int it = t / kChunk;
-  const int W = a.W;
 
-  // ---- the list: set mask bits in chunk order, then the diagonal chunk
-  if (tid < W) wl[tid] = a.mask[(size_t)bk * W + tid];
-  __syncthreads();
-  if (wv == 0) {  // inclusive scan of the words' popcounts
-    int v = lane < W ? __popcll(wl[lane]) : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(v, o, 64);
-      if (lane >= o) v += u;
-    }
-    if (lane < W) wpre[lane + 1] = v;
-    if (lane == 0) wpre[0] = 0;
-  }
-  __syncthreads();
-  const int nact = wpre[W];
-  const int lo = seg * kSeg, hi = min(lo + kSeg, nact + 1);
-  const int nitems = hi - lo;
+  // ---- this workgroup's items from the route kernel's list, with their routing bias
+  // (log2 w_bar; 0 for the diagonal chunk), staged in LDS once so that the loop below never
+  // waits on a global load other than its own tiles
+  __shared__ int citem[kSeg];
+  __shared__ float cbias[kSeg];
+  const int32_t* lst = a.list + (size_t)bk * a.list_ld;
+  const int ntot = lst[0];                        // active chunks + the diagonal chunk
+  const int lo = seg * kSeg;
+  const int nitems = min(kSeg, ntot - lo);
   if (nitems <= 0) return;
   if (tid < nitems) {
-    const int r = lo + tid;
-    int c = it;
-    if (r < nact) {
-      int w = 0;
-      while (wpre[w + 1] <= r) ++w;
-      uint64_t bits = wl[w];
-      for (int k = r - wpre[w]; k > 0; --k) bits &= bits - 1;
-      c = 64 * w + __builtin_ctzll(bits);
-    }
-    items[tid] = c;
+    const int c = lst[1 + lo + tid];
+    citem[tid] = c;
+    cbias[tid] = c == it ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]);
   }
   __syncthreads();
 
@@ -224,37 +240,39 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // registers for one item: K operands (A of S^T) and this lane's V segments
+  // registers for one item: K operands (A of S^T) and this lane's V segments, fetched
+  // through buffer descriptors whose range ends at the item's last valid key (t on the
+  // diagonal), so keys past it read as zeros without branches
   bf16x8 kop[4][KS];
   uint4 vseg[VL];
-  auto load_item = [&](int c) {
-    const int kmax = (c == it) ? t : c * kChunk + 63;
+  int koff[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
-      const int kabs = c * kChunk + key;
-      const bool kok = kabs <= kmax;
-      const bf16* kr = kb + (size_t)(kok ? kabs : 0) * D;
+  for (int kt = 0; kt < 4; ++kt) {
+    const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
+    koff[kt] = (key * D + 8 * lg) * 2;
+  }
+  auto load_item = [&](int c_any) {
+    const int c = __builtin_amdgcn_readfirstlane(c_any);
+    const int nkeys = min(kChunk, t - c * kChunk + 1);          // 64 except on the diagonal
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kb + (size_t)c * kChunk * D), (short)0, nkeys * D * 2, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vb + (size_t)c * kChunk * D), (short)0, nkeys * D * 2, kBufferRsrcWord3);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(kr + 32 * ks + 8 * lg);
-        kop[kt][ks] = kok ? v : bf16x8{};
-      }
-    }
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int sg = i * 64 + lane;
-      const int key = sg / SEGR, db = (sg % SEGR) * 8;
-      const int kabs = c * kChunk + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kabs <= kmax) v = *reinterpret_cast<const uint4*>(vb + (size_t)kabs * D + db);
-      vseg[i] = v;
-    }
+      for (int ks = 0; ks < KS; ++ks)
+        kop[kt][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[kt] + 64 * ks, 0, 0));
+#pragma unroll
+    for (int i = 0; i < VL; ++i)
+      vseg[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (i * 64 + lane) * 16, 0, 0));
   };
 
-  if (wv < nitems) load_item(items[wv]);
+  if (wv < nitems) load_item(citem[wv]);
   for (int ii = wv; ii < nitems; ii += kAttWaves) {
-    const int c = items[ii];
+    const int c = citem[ii];
     const bool diag = c == it;
     const int kmax = diag ? t : c * kChunk + 63;
     // V rows -> LDS (row-major, padded)
@@ -275,9 +293,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s[kt] = mfma16(kop[kt][ks], qop[ks], s[kt]);
     }
-    const float bias = diag ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]);
+    const float bias = cbias[ii];
     // next item's loads overlap the softmax and the PV product
-    if (ii + kAttWaves < nitems) load_item(items[ii + kAttWaves]);
+    if (ii + kAttWaves < nitems) load_item(citem[ii + kAttWaves]);
     float x[16];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -362,10 +380,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_decode_attend(AttendArgs a, 
 template <typename TOut, int D>
 __global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
                                                       const float* __restrict__ po, int nseg_max) {
-  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
   __shared__ float fs[256];
   __shared__ float red[D / 64 > 0 ? D / 64 : 1];
-  __shared__ int cnt[MAXW];
   const int bh = blockIdx.x, b = bh / a.Hq, h = bh % a.Hq;
   const int G = a.Hq / a.Hkv, kvh = h / G, q = h % G;
   const int bk = b * a.Hkv + kvh;
@@ -376,11 +392,7 @@ __global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float*
     op[d] = from_f32<TOut>(__builtin_nanf(""));
     return;
   }
-  for (int w = d; w < a.W; w += D) cnt[w] = __popcll(a.mask[(size_t)bk * a.W + w]);
-  __syncthreads();
-  int nact = 0;
-  for (int w = 0; w < a.W; ++w) nact += cnt[w];
-  const int nseg = (nact + 1 + kSeg - 1) / kSeg;   // <= 256 for 2048 routed chunks
+  const int nseg = (a.list[(size_t)bk * a.list_ld] + kSeg - 1) / kSeg;   // <= 129
   // max over segments
   float mloc = kNegBig;
   for (int s = d; s < nseg; s += D) mloc = fmaxf(mloc, pml[((size_t)bk * nseg_max + s) * 32 + q]);
