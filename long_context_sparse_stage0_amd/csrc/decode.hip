@@ -17,6 +17,8 @@
 //                    partials are merged in LDS and written once per workgroup.
 //   k_decode_combine log-sum-exp merge of the segment partials, one workgroup per (b, head).
 // Decoding is HBM-bound: the active K/V chunks (32 KiB each at D = 128) dominate the bytes.
+#include <type_traits>
+
 #include "route_common.h"
 
 namespace dash {
@@ -71,15 +73,14 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   }
   const float* sb = a.summ + (size_t)bk * a.nc_alloc * D;
   const int ntile = (it + 15) / 16;
-  for (int ct = wv; ct < ntile; ct += NW) {
-    const int crow = 16 * ct + l16;
-    const bool cok = crow < it;
-    const float* srow = sb + (size_t)(cok ? crow : 0) * D;
+  // two tiles per wave at a time: both tiles' summary rows are requested before either
+  // tile's products, halving the exposed load latency
+  auto tile_scores = [&](int ct, const float4 (&xr)[2 * KS]) {
+    const bool cok = 16 * ct + l16 < it;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float4 x0 = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
-      const float4 x1 = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
+      const float4 x0 = xr[2 * ks], x1 = xr[2 * ks + 1];
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       bf16x8 hi, lo;
 #pragma unroll
@@ -93,25 +94,50 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
       acc = mfma16(lo, qop[ks], acc);
     }
     *reinterpret_cast<float4*>(&sc[l16 * ld + 16 * ct + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  auto load_rows = [&](int ct, float4 (&xr)[2 * KS]) {
+    const int crow = 16 * ct + l16;
+    const float* srow = sb + (size_t)(crow < it ? crow : 0) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      xr[2 * ks] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
+      xr[2 * ks + 1] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
+    }
+  };
+  for (int ct = wv; ct < ntile; ct += 2 * NW) {
+    float4 xa[2 * KS], xb[2 * KS];
+    const bool two = ct + NW < ntile;                 // wave-uniform
+    load_rows(ct, xa);
+    if (two) load_rows(ct + NW, xb);
+    tile_scores(ct, xa);
+    if (two) tile_scores(ct + NW, xb);
   }
   __syncthreads();
 
-  // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...
-  if (wv < G && it > 0) {
-    float y[NR];
+  // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...; the
+  // register count follows the routed length
+  auto solve = [&](auto nr_tag) {
+    constexpr int NRU = decltype(nr_tag)::value;
+    float y[NRU];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
+    for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
       y[r] = c < it ? a.zscale * sc[wv * ld + c] : -INFINITY;
     }
     float z;
-    const float tau = entmax_threshold<MODE, NR>(y, it, a.alpha, WaveReduce(), &z);
+    const float tau = entmax_threshold<MODE, NRU>(y, it, a.alpha, WaveReduce(), &z);
     const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
+    for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
       if (c < it) sc[wv * ld + c] = entmax_weight<MODE>(y[r], tau, inv, rz);
     }
+  };
+  if (wv < G && it > 0) {
+    if (it <= 256) solve(std::integral_constant<int, 4>{});
+    else if (it <= 512) solve(std::integral_constant<int, 8>{});
+    else if (it <= 1024) solve(std::integral_constant<int, 16>{});
+    else solve(std::integral_constant<int, NR>{});
   }
   __syncthreads();
 
