@@ -121,7 +121,7 @@ PrefillLayout prefill_layout(const Dims& d) {
 }
 
 struct DecodeLayout {
-  size_t mask, wbar, list, pml, po, total;
+  size_t mask, wbar, list, sco, pml, po, total;
 };
 
 DecodeLayout decode_layout(const Dims& d) {
@@ -133,6 +133,8 @@ DecodeLayout decode_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.nc * 4);
   L.list = off;
   off += align256((size_t)d.B * d.Hkv * (d.nc + 2) * 4);
+  L.sco = off;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hq * (16 * ((d.nc + 15) / 16)) * 4) : 0;
   const size_t nseg = (size_t)dash::decode_nseg_max(d.nc);
   L.pml = off;
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 32 * 4) : 0;
@@ -352,6 +354,8 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   ra.dtype = d.dtype;
   ra.list = reinterpret_cast<int32_t*>(ws + L.list);
   ra.list_ld = d.nc + 2;
+  ra.sco = reinterpret_cast<float*>(ws + L.sco);
+  ra.sco_ld = 16 * ((d.nc + 15) / 16);
   e = d.dtype == DASH_BF16 ? dash::launch_decode_route(ra, s) : dash::launch_route_valu(ra, s);
   if (e != hipSuccess) return hip_fail(e, "decode route launch");
 

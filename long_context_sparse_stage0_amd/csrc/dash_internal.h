@@ -71,6 +71,8 @@ struct RouteArgs {
   int dtype;
   int32_t* list;          // decode: [B * Hkv][list_ld]: count, then the active chunks in
   int list_ld;            // increasing order followed by the diagonal chunk (or nullptr)
+  float* sco;             // decode: [B * Hkv][G][sco_ld] scaled scores (or nullptr)
+  int sco_ld;
 };
 
 struct AttendArgs {

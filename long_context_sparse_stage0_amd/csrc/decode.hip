@@ -3,12 +3,15 @@
 // complete chunk's summary is frozen and cached; the kernels support incremental decoding
 // with a chunk-representation cache, "Hauptbeiträge").  Decode row t equals prefill row t.
 //
-// Three kernels per step, all on the caller's stream:
-//   k_decode_route   one 16-wave workgroup per (b, kv head): the G heads' scores against
-//                    every routed summary on MFMA (fp32 summaries split into bf16 hi + lo
-//                    in registers), staged in LDS so that wave g solves head g's entmax
+// Four kernels per step, all on the caller's stream:
+//   k_decode_scores  the G heads' scores against every routed summary on MFMA (fp32
+//                    summaries split into bf16 hi + lo in registers), one 16-chunk tile per
+//                    wave over many workgroups, so the summary reads are spread over the
+//                    whole GPU rather than one CU per (b, kv head).
+//   k_decode_route   one 16-wave workgroup per (b, kv head): wave g solves head g's entmax
 //                    threshold with wave-only reductions; then a fixed-order sum over the
-//                    heads, a ballot per 64 chunks for the mask word and w_bar at set bits.
+//                    heads, a ballot per 64 chunks for the mask word, w_bar at set bits and
+//                    the attend kernels' work list.
 //   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
 //                    chunk form a list; each workgroup takes 16 consecutive items, each of
 //                    its 4 waves a quarter of them.  S^T = K Q^T with K rows loaded straight
@@ -47,20 +50,22 @@ constexpr float kNegBig = -1.0e30f;
 }  // namespace
 
 // ------------------------------------------------------------------------------ route
-template <int D, int MODE>
-__global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
-  constexpr int NW = 16, KS = D / 32, NR = kMaxRoutedRegs;
-  constexpr int ld = kMaxRouted + 16;            // covers 16 * ceil(routed / 16) columns
-  __shared__ __attribute__((aligned(16))) float sc[16 * ld];  // [head][chunk] scores, then weights
+// Scores of one row per (b, kv head) against every routed summary, spread over many
+// workgroups (one 16-chunk tile per wave): S^T tile = 16 chunks x 16 head columns on MFMA,
+// the fp32 summaries split into bf16 hi + lo in registers.  Written scaled, as
+// sco[b, kv head][g][c], for the solver kernel.
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_scores(RouteArgs a) {
+  constexpr int KS = D / 32;
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int bk = blockIdx.x, b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int t = a.seq_lens[b] - 1;
   const bool valid = t >= 0 && t < a.tcap;
   const int it = valid ? t / kChunk : 0;
-
-  // scores: S^T tile = 16 chunks x 16 head columns (columns >= G are zero queries)
+  const int ct = blockIdx.x * 4 + wv;              // this wave's tile of 16 chunks
+  if (16 * ct >= it) return;                       // (whole wave)
   bf16x8 qop[KS];
   {
     const bool qok = l16 < G;
@@ -71,48 +76,52 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
       qop[ks] = qok ? v : bf16x8{};
     }
   }
-  const float* sb = a.summ + (size_t)bk * a.nc_alloc * D;
-  const int ntile = (it + 15) / 16;
-  // two tiles per wave at a time: both tiles' summary rows are requested before either
-  // tile's products, halving the exposed load latency
-  auto tile_scores = [&](int ct, const float4 (&xr)[2 * KS]) {
-    const bool cok = 16 * ct + l16 < it;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int crow = 16 * ct + l16;
+  const bool cok = crow < it;
+  const float* srow = a.summ + ((size_t)bk * a.nc_alloc + (cok ? crow : 0)) * D;
+  float4 xr[2 * KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float4 x0 = xr[2 * ks], x1 = xr[2 * ks + 1];
-      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16 h = (bf16)xs[i];
-        hi[i] = h;
-        lo[i] = (bf16)(xs[i] - (float)h);
-      }
-      if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
-      acc = mfma16(hi, qop[ks], acc);
-      acc = mfma16(lo, qop[ks], acc);
-    }
-    *reinterpret_cast<float4*>(&sc[l16 * ld + 16 * ct + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  };
-  auto load_rows = [&](int ct, float4 (&xr)[2 * KS]) {
-    const int crow = 16 * ct + l16;
-    const float* srow = sb + (size_t)(crow < it ? crow : 0) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      xr[2 * ks] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
-      xr[2 * ks + 1] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
-    }
-  };
-  for (int ct = wv; ct < ntile; ct += 2 * NW) {
-    float4 xa[2 * KS], xb[2 * KS];
-    const bool two = ct + NW < ntile;                 // wave-uniform
-    load_rows(ct, xa);
-    if (two) load_rows(ct + NW, xb);
-    tile_scores(ct, xa);
-    if (two) tile_scores(ct + NW, xb);
+  for (int ks = 0; ks < KS; ++ks) {
+    xr[2 * ks] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
+    xr[2 * ks + 1] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
   }
-  __syncthreads();
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float4 x0 = xr[2 * ks], x1 = xr[2 * ks + 1];
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16 h = (bf16)xs[i];
+      hi[i] = h;
+      lo[i] = (bf16)(xs[i] - (float)h);
+    }
+    if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
+    acc = mfma16(hi, qop[ks], acc);
+    acc = mfma16(lo, qop[ks], acc);
+  }
+  // C[4 lg + j][l16]: chunk 16 ct + 4 lg + j, head column l16
+  if (l16 < G) {
+    float* dst = a.sco + ((size_t)bk * G + l16) * a.sco_ld + 16 * ct + 4 * lg;
+    *reinterpret_cast<float4*>(dst) =
+        make_float4(a.zscale * acc[0], a.zscale * acc[1], a.zscale * acc[2], a.zscale * acc[3]);
+  }
+}
+
+// Threshold, weights, GQA average, mask, work list: one 16-wave workgroup per (b, kv head).
+template <int D, int MODE>
+__global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
+  constexpr int NW = 16, NR = kMaxRoutedRegs;
+  constexpr int ld = kMaxRouted + 16;
+  __shared__ __attribute__((aligned(16))) float sc[16 * ld];  // [head][chunk] weights
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bk = blockIdx.x;
+  const int t = a.seq_lens[bk / a.Hkv] - 1;
+  const bool valid = t >= 0 && t < a.tcap;
+  const int it = valid ? t / kChunk : 0;
+  const float* srow = a.sco + ((size_t)bk * G + (wv < G ? wv : 0)) * a.sco_ld;
 
   // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...; the
   // register count follows the routed length
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
-      y[r] = c < it ? a.zscale * sc[wv * ld + c] : -INFINITY;
+      y[r] = c < it ? srow[c] : -INFINITY;
     }
     float z;
     const float tau = entmax_threshold<MODE, NRU>(y, it, a.alpha, WaveReduce(), &z);
@@ -450,16 +459,20 @@ __global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float*
 int decode_nseg_max(int nc) { return (nc + 1 + kSeg - 1) / kSeg; }
 
 hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
-  const size_t lds = 0;
+  dim3 gs((a.nc_alloc + 63) / 64, a.B * a.Hkv);
+  if (a.D == 128) k_decode_scores<128><<<gs, 256, 0, s>>>(a);
+  else k_decode_scores<64><<<gs, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(a.B * a.Hkv);
   if (a.D == 128) {
-    if (a.alpha == 1.5f) k_decode_route<128, kAlpha15><<<grid, 1024, lds, s>>>(a);
-    else if (a.alpha == 2.0f) k_decode_route<128, kAlpha2><<<grid, 1024, lds, s>>>(a);
-    else k_decode_route<128, kAlphaGeneral><<<grid, 1024, lds, s>>>(a);
+    if (a.alpha == 1.5f) k_decode_route<128, kAlpha15><<<grid, 1024, 0, s>>>(a);
+    else if (a.alpha == 2.0f) k_decode_route<128, kAlpha2><<<grid, 1024, 0, s>>>(a);
+    else k_decode_route<128, kAlphaGeneral><<<grid, 1024, 0, s>>>(a);
   } else {
-    if (a.alpha == 1.5f) k_decode_route<64, kAlpha15><<<grid, 1024, lds, s>>>(a);
-    else if (a.alpha == 2.0f) k_decode_route<64, kAlpha2><<<grid, 1024, lds, s>>>(a);
-    else k_decode_route<64, kAlphaGeneral><<<grid, 1024, lds, s>>>(a);
+    if (a.alpha == 1.5f) k_decode_route<64, kAlpha15><<<grid, 1024, 0, s>>>(a);
+    else if (a.alpha == 2.0f) k_decode_route<64, kAlpha2><<<grid, 1024, 0, s>>>(a);
+    else k_decode_route<64, kAlphaGeneral><<<grid, 1024, 0, s>>>(a);
   }
   return hipGetLastError();
 }
