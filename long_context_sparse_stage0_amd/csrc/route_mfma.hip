@@ -7,7 +7,7 @@
 // blog, "Трёхстадийная архитектура" (active chunks packed in 64-bit words).  The entmax
 // definition is that of Peters, Niculae and Martins (2019).
 //
-// Work unit: one workgroup (8 or 16 waves) per (b, kv head, R = 32/G rows of one 64-row
+// Work unit: one workgroup (1 to 8 waves) per (b, kv head, R = 32/G or 16/G rows of one 64-row
 // block): 32 query vectors that all route over the same chunks c < i_t.  Chunk tiles of 16
 // are dealt to the waves round-robin (tile w, w + NW, ...), and every score stays in
 // registers (at most 8 tiles x 2 query tiles x 4 = 64 values per lane; 16 waves cover
@@ -26,6 +26,7 @@
 // GQA average: the G heads of a row are G adjacent columns of a 16-lane row, summed with
 // DPP (quad permutes, half-row and row mirrors) in a fixed order.
 #include <algorithm>
+#include <utility>
 
 #include "route_common.h"
 
@@ -78,10 +79,10 @@ __device__ __forceinline__ float xg_max(float v) {
 
 // One workgroup's routing with MT chunk tiles per wave (MT = ceil(ntile / NW), chosen per
 // workgroup so short rows do not pay for the longest row's tile count).
-template <int D, int NW, int MT, int MODE>
+template <int D, int NW, int MT, int QTR, int MODE>
 __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __restrict__ ssplit,
-                                           float (&part)[2][2][4][16][NW],
-                                           uint16_t (&mbits16)[32][4 * kRouteMaskWords],
+                                           float (&part)[2][QTR][4][16][NW],
+                                           uint16_t (&mbits16)[16 * QTR][4 * kRouteMaskWords],
                                            int bk, int row0, int it, int ntile) {
   constexpr int KS = D / 32;
   const int G = a.Hq / a.Hkv;
@@ -91,10 +92,10 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   const int T = a.Tq;
 
   // queries of this lane: column l16 of query tiles 0 and 1
-  bf16x8 qop[2][KS];
-  int qrow[2];
+  bf16x8 qop[QTR][KS];
+  int qrow[QTR];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QTR; ++qt) {
     const int n = 16 * qt + l16;
     const int r = n / G, g = n % G;
     qrow[qt] = r;
@@ -106,11 +107,13 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
 
   // scores
   const bf16* sp = ssplit + (size_t)bk * a.nc_alloc * 2 * D;
-  float y[MT][2][4];
+  float y[MT][QTR][4];
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
     const int ct = wv + NW * j;
-    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[QTR];
+#pragma unroll
+    for (int qt = 0; qt < QTR; ++qt) acc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (ct < ntile) {  // wave-uniform
       const int crow = 16 * ct + l16;
       const bool cok = crow < it;
@@ -120,18 +123,18 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
         bf16x8 hi = *reinterpret_cast<const bf16x8*>(srow + 32 * ks + 8 * lg);
         bf16x8 lo = *reinterpret_cast<const bf16x8*>(srow + D + 32 * ks + 8 * lg);
         if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
-        acc0 = mfma16(hi, qop[0][ks], acc0);
-        acc1 = mfma16(hi, qop[1][ks], acc1);
-        acc0 = mfma16(lo, qop[0][ks], acc0);
-        acc1 = mfma16(lo, qop[1][ks], acc1);
+#pragma unroll
+        for (int qt = 0; qt < QTR; ++qt) acc[qt] = mfma16(hi, qop[qt][ks], acc[qt]);
+#pragma unroll
+        for (int qt = 0; qt < QTR; ++qt) acc[qt] = mfma16(lo, qop[qt][ks], acc[qt]);
       }
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int c = 16 * ct + 4 * lg + jj;
       const bool ok = (ct < ntile) && (c < it);
-      y[j][0][jj] = ok ? a.zscale * acc0[jj] : -INFINITY;
-      y[j][1][jj] = ok ? a.zscale * acc1[jj] : -INFINITY;
+#pragma unroll
+      for (int qt = 0; qt < QTR; ++qt) y[j][qt][jj] = ok ? a.zscale * acc[qt][jj] : -INFINITY;
     }
   }
 
@@ -139,14 +142,21 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
 
   // ---- threshold solver for the 32 queries
-  float tau[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f}, zs[2] = {1.f, 1.f};
-  bool done[2] = {true, true};
+  float tau[QTR], hi[QTR], zs[QTR];
+  bool done[QTR];
+#pragma unroll
+  for (int qt = 0; qt < QTR; ++qt) {
+    tau[qt] = 0.f;
+    hi[qt] = 0.f;
+    zs[qt] = 1.f;
+    done[qt] = true;
+  }
   const float inv = 1.0f / (a.alpha - 1.0f);
   int buf = 0;
   if (it > 0) {
     // pass 0: max
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QTR; ++qt) {
       float m = -INFINITY;
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
@@ -162,7 +172,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     const float n = (float)it;
     const float hoff = (MODE == kAlpha15) ? rsqrtf(n) : (MODE == kAlpha2 ? 1.0f / n : pow_pos(n, 1.0f - a.alpha));
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QTR; ++qt) {
       float m = part[buf][qt][0][l16][0];
 #pragma unroll
       for (int w = 1; w < NW; ++w) m = fmaxf(m, part[buf][qt][0][l16][w]);
@@ -173,7 +183,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     buf ^= 1;
     for (int pass = 0; pass < 96; ++pass) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QTR; ++qt) {
         float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
@@ -210,7 +220,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
       }
       __syncthreads();
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QTR; ++qt) {
         float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -248,11 +258,14 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
         }
       }
       buf ^= 1;
-      if (__ballot(!(done[0] && done[1])) == 0ull) break;
+      bool all_done = true;
+#pragma unroll
+      for (int qt = 0; qt < QTR; ++qt) all_done = all_done && done[qt];
+      if (__ballot(!all_done) == 0ull) break;
     }
     // normaliser
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QTR; ++qt) {
       float z = 0.f;
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
@@ -268,7 +281,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     }
     __syncthreads();
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QTR; ++qt) {
       float z = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) z += part[buf][qt][0][l16][w];
@@ -284,7 +297,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     const float rG = 1.0f / (float)G;
     const int g = l16 % G;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QTR; ++qt) {
       const float rz = 1.0f / zs[qt];
       const int r = qrow[qt];
       const bool row_ok = (row0 + r) < T;
@@ -324,15 +337,15 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   }
 }
 
-template <int D, int NW, int MT, int MODE>
+template <int D, int NW, int MT, int QTR, int MODE>
 __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit,
                                                         int rt_lo, int rt_n) {
   constexpr int NT = NW * 64;
-  __shared__ float part[2][2][4][16][NW];
-  __shared__ uint16_t mbits16[32][4 * kRouteMaskWords];
+  __shared__ float part[2][QTR][4][16][NW];
+  __shared__ uint16_t mbits16[16 * QTR][4 * kRouteMaskWords];
 
   const int G = a.Hq / a.Hkv;
-  const int R = 32 / G;
+  const int R = 16 * QTR / G;                       // rows per workgroup
   const int tid = threadIdx.x;
   const int tile = gridDim.x - 1 - blockIdx.x;      // late (heavy) rows first
   const int BH = a.B * a.Hkv;
@@ -345,9 +358,9 @@ __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16*
   (void)rt_n;
 
   uint32_t* m32 = reinterpret_cast<uint32_t*>(&mbits16[0][0]);
-  for (int i = tid; i < 32 * 2 * kRouteMaskWords; i += NT) m32[i] = 0u;
+  for (int i = tid; i < 16 * QTR * 2 * kRouteMaskWords; i += NT) m32[i] = 0u;
   __syncthreads();
-  route_rows<D, NW, MT, MODE>(a, ssplit, part, mbits16, bk, row0, it, ntile);
+  route_rows<D, NW, MT, QTR, MODE>(a, ssplit, part, mbits16, bk, row0, it, ntile);
   __syncthreads();
   const uint64_t* mrow = reinterpret_cast<const uint64_t*>(&mbits16[0][0]);
   for (int idx = tid; idx < R * W; idx += NT) {
@@ -358,62 +371,64 @@ __global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16*
   }
 }
 
-template <int D, int NW, int MT>
+template <int D, int NW, int MT, int QTR>
 static void launch_mt(const RouteArgs& a, const bf16* ss, int rt_lo, int rt_n, hipStream_t s) {
   dim3 grid(rt_n * a.B * a.Hkv);
   if (a.alpha == 1.5f)
-    k_route_mfma<D, NW, MT, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
   else if (a.alpha == 2.0f)
-    k_route_mfma<D, NW, MT, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
   else
-    k_route_mfma<D, NW, MT, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
 }
 
-// Workgroup shapes by the number of 16-chunk tiles a row tile routes over: the fewest
-// waves (NW) that hold every tile with at most 8 tiles per wave, and MT = ceil(ntile/NW).
-// Light rows then run in small workgroups, several per CU, which hide each other's
-// barrier and memory latency; only rows with more than 1024 routed chunks need sixteen.
-// Row tiles are contiguous per shape (i_t grows with the row), one launch each, heaviest
-// first.
-struct RouteShape { int nw, mt; };
+// Workgroup shapes by the number of 16-chunk tiles a row tile routes over.  Up to 64 tiles
+// (1024 routed chunks): 32 query vectors per workgroup (two query tiles) on the fewest
+// waves (NW) that hold every tile at no more than 8 tiles per wave, MT = ceil(ntile / NW).
+// Beyond: one query tile (16 query vectors) on 8 waves of up to 16 tiles each, which fits
+// the same registers, so every shape runs at least two workgroups per CU; they hide each
+// other's barrier and memory latency (one 16-wave workgroup per CU cannot).  Rows are
+// contiguous per shape (i_t grows with the row), one launch each, heaviest first.
+struct RouteShape { int nw, mt, qtr; };
 constexpr RouteShape kRouteShapes[] = {
-    {1, 1}, {1, 2}, {1, 3}, {1, 4}, {1, 5}, {1, 6}, {1, 7}, {1, 8},
-    {2, 5}, {2, 6}, {2, 7}, {2, 8}, {4, 5}, {4, 6}, {4, 7}, {4, 8},
-    {8, 5}, {8, 6}, {8, 7}, {8, 8}, {16, 5}, {16, 6}, {16, 7}, {16, 8}};
+    {1, 1, 2}, {1, 2, 2}, {1, 3, 2}, {1, 4, 2}, {1, 5, 2}, {1, 6, 2}, {1, 7, 2}, {1, 8, 2},
+    {2, 5, 2}, {2, 6, 2}, {2, 7, 2}, {2, 8, 2}, {4, 5, 2}, {4, 6, 2}, {4, 7, 2}, {4, 8, 2},
+    {8, 5, 2}, {8, 6, 2}, {8, 7, 2}, {8, 8, 2},
+    {8, 9, 1}, {8, 10, 1}, {8, 11, 1}, {8, 12, 1}, {8, 13, 1}, {8, 14, 1}, {8, 15, 1},
+    {8, 16, 1}};
 
 template <int D, int I>
 static void launch_shape(const RouteArgs& a, const bf16* ss, int lo, int n, hipStream_t s) {
-  launch_mt<D, kRouteShapes[I].nw, kRouteShapes[I].mt>(a, ss, lo, n, s);
+  launch_mt<D, kRouteShapes[I].nw, kRouteShapes[I].mt, kRouteShapes[I].qtr>(a, ss, lo, n, s);
+}
+
+template <int D, int... I>
+static void launch_all(const RouteArgs& a, const bf16* ss, hipStream_t s,
+                       std::integer_sequence<int, I...>) {
+  constexpr int NS = sizeof...(I);
+  using Fn = void (*)(const RouteArgs&, const bf16*, int, int, hipStream_t);
+  static const Fn fns[NS] = {launch_shape<D, I>...};
+  const int G = a.Hq / a.Hkv;
+  // rows [row_hi(i-1), row_hi(i)) go to shape i: i_t <= 16 cap, i.e. row < 64 (16 cap + 1)
+  long long row_hi[NS];
+  for (int i = 0; i < NS; ++i) {
+    const long long cap = (long long)kRouteShapes[i].nw * kRouteShapes[i].mt;
+    row_hi[i] = std::min<long long>(a.Tq, 64LL * (16LL * cap + 1));
+  }
+  row_hi[NS - 1] = a.Tq;
+  for (int i = NS - 1; i >= 0; --i) {
+    const long long r0 = i > 0 ? row_hi[i - 1] : 0, r1 = row_hi[i];
+    if (r1 <= r0) continue;
+    const int R = 16 * kRouteShapes[i].qtr / G;     // rows per workgroup (divides 64)
+    const int lo = (int)(r0 / R), hi = (int)((r1 + R - 1) / R);
+    fns[i](a, ss, lo, hi - lo, s);
+  }
 }
 
 template <int D>
 static void launch_d(const RouteArgs& a, const bf16* ss, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int R = 32 / G;
-  const int nrt = (a.Tq + R - 1) / R;
   constexpr int NS = sizeof(kRouteShapes) / sizeof(kRouteShapes[0]);
-  int hi[NS + 1];
-  hi[0] = 0;
-  for (int i = 0; i < NS; ++i) {
-    // row tiles whose ntile fits the shape's capacity: i_t <= 16 cap, i.e. row0 < 64 (16 cap + 1)
-    const long long cap = (long long)kRouteShapes[i].nw * kRouteShapes[i].mt;
-    const long long lim = (64LL * (16LL * cap + 1) + R - 1) / R;
-    hi[i + 1] = (int)std::min<long long>(nrt, lim);
-  }
-  hi[NS] = nrt;
-  using Fn = void (*)(const RouteArgs&, const bf16*, int, int, hipStream_t);
-  static const Fn fns[NS] = {
-      launch_shape<D, 0>, launch_shape<D, 1>, launch_shape<D, 2>, launch_shape<D, 3>,
-      launch_shape<D, 4>, launch_shape<D, 5>, launch_shape<D, 6>, launch_shape<D, 7>,
-      launch_shape<D, 8>, launch_shape<D, 9>, launch_shape<D, 10>, launch_shape<D, 11>,
-      launch_shape<D, 12>, launch_shape<D, 13>, launch_shape<D, 14>, launch_shape<D, 15>,
-      launch_shape<D, 16>, launch_shape<D, 17>, launch_shape<D, 18>, launch_shape<D, 19>,
-      launch_shape<D, 20>, launch_shape<D, 21>, launch_shape<D, 22>, launch_shape<D, 23>};
-  for (int i = NS - 1; i >= 0; --i) {
-    const int lo = std::max(hi[i], i > 0 ? hi[i - 1] : 0);
-    const int n = hi[i + 1] - lo;
-    if (n > 0) fns[i](a, ss, lo, n, s);
-  }
+  launch_all<D>(a, ss, s, std::make_integer_sequence<int, NS>{});
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s) {
