@@ -337,9 +337,11 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   }
 }
 
+// one-tile shapes are held to 4 waves per SIMD (128 registers) so that two 8-wave
+// workgroups share a CU
 template <int D, int NW, int MT, int QTR, int MODE>
-__global__ __launch_bounds__(NW * 64) void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit,
-                                                        int rt_lo, int rt_n) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QTR == 1 ? 4 : 1)))
+void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit, int rt_lo, int rt_n) {
   constexpr int NT = NW * 64;
   __shared__ float part[2][QTR][4][16][NW];
   __shared__ uint16_t mbits16[16 * QTR][4 * kRouteMaskWords];
