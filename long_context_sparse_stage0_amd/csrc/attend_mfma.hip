@@ -308,6 +308,14 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
       prefetch(cn);
       if (cn != it) fetch_weight(cn);
     }
+    // a wave none of whose rows has this routed chunk adds exactly nothing (p = 0, no
+    // rescale): it only takes part in the tile loads and leaves its SIMD to the other wave
+    if (!DIAG && !DENSE) {
+      bool any = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) any = any || bias[qt] != -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(any) == 0ull) return;
+    }
     const uint8_t* kl = lds_k[buf];
     const uint8_t* vl = lds_v[buf];
 
