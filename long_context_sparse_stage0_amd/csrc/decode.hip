@@ -31,13 +31,19 @@ namespace {
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// reductions over lanes l, l^16, l^32, l^48 (the four 16-lane rows) with the row-swap moves
+template <typename Op>
+__device__ __forceinline__ float xg_reduce(float v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float xg_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  return xg_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float xg_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  return xg_reduce(v, [](float x, float y) { return x + y; });
 }
 
 constexpr int kSeg = 16;        // list items per attend workgroup
@@ -46,6 +52,9 @@ constexpr int kSeg = 16;        // list items per attend workgroup
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kAttWaves = 4;
 constexpr float kNegBig = -1.0e30f;
+// A lane's 16 unnormalised probabilities of an item may sum to at most 2^8 before the
+// reference max is raised; a larger sum, an overflow or a NaN triggers the rescale.
+constexpr float kSumCap = 256.0f;
 
 }  // namespace
 
@@ -331,39 +340,61 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
     const float bias = cbias[ii];
     // next item's loads overlap the softmax and the PV product
     if (ii + kAttWaves < nitems) load_item(citem[ii + kAttWaves]);
+    // online softmax against the reference max m, which is only raised (with the rescale
+    // of O and l) when a lane's partial probability sum exceeds kSumCap; keys past the
+    // query are masked on the diagonal item only
     float x[16];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
-        x[4 * kt + j] = (c * kChunk + key <= kmax) ? fmaf(s[kt][j], sl2, bias) : -INFINITY;
-      }
-    float mx = x[0];
+      for (int j = 0; j < 4; ++j) x[4 * kt + j] = s[kt][j];
+    if (diag) {
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = xg_max(mx);
-    const float mn = fmaxf(m, mx);
-    const float corr = fast_exp2(m - mn);
-    m = mn;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
+          if (c * kChunk + key > kmax) x[4 * kt + j] = -INFINITY;
+        }
+    }
+    float off = bias - m;
     float ps = 0.f;
+    float pr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      x[i] = fast_exp2(x[i] - mn);
-      ps += x[i];
+      pr[i] = fast_exp2(fmaf(x[i], sl2, off));
+      ps += pr[i];
     }
-    lsum = fmaf(lsum, corr, ps);
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0ull) {
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = xg_max(mx);
+      const float mn = fmaxf(m, fmaf(mx, sl2, bias));
+      const float corr = fast_exp2(m - mn);
+      m = mn;
+      lsum *= corr;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= corr;
+      off = bias - mn;
+      ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = fast_exp2(fmaf(x[i], sl2, off));
+        ps += pr[i];
+      }
+    }
+    lsum += ps;
     bf16x8 pop[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pop[p][j] = (bf16)x[8 * p + j];
-        pop[p][4 + j] = (bf16)x[8 * p + 4 + j];
+        pop[p][j] = (bf16)pr[8 * p + j];
+        pop[p][4 + j] = (bf16)pr[8 * p + 4 + j];
       }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] *= corr;
 #pragma unroll
       for (int p = 0; p < 2; ++p)
         o[dt] = mfma16(vt_operand(vl, VP, 32 * p + 8 * lg, 16 * dt, l16), pop[p], o[dt]);
