@@ -141,3 +141,13 @@ def test_decode_64k_all_steps_sampled(dash):
         act = float(bits.sum()) / (B * Hkv * ((L - 1) // 64))
         say(f"[fullsize]   step {s}: out err {e:.2e}, near-threshold flips {amb}, "
             f"active fraction {act:.3f}")
+
+
+@pytest.mark.parametrize("alpha,lam", [(1.25, 32.0), (2.0, 2.0)])
+def test_sweep_64k_sampled_rows(dash, alpha, lam):
+    """Two corners of the 64K sparsity sweep (32/8 heads, Poisson needle counts): the
+    densest (alpha = 1.25, 32 needles per block) and the sparsest (alpha = 2, 2 needles)."""
+    from long_context_sparse_stage0_amd.workloads import sweep_cell
+    w = sweep_cell(alpha, lam)
+    rows = _sample_rows(w.T, 10, 3, [64, 32768, w.T - 1])
+    _prefill_bench_config(dash, w, rows)
