@@ -265,6 +265,59 @@ def cpu_baseline(args, w, x):
                       f"{t_s0 + t_rows:.1f}s of CPU time, 1 BLAS thread"}
 
 
+def bench_sweep(args, dash, torch):
+    """Sparsity sweep: the 64K, 32/8-head prefill at alpha in {1.25, 1.5, 2} x planted-needle
+    count per query block ~ Poisson(2, 8, 32).  One JSON line per cell on stdout (this mode
+    is a report, not the benchmark line)."""
+    from long_context_sparse_stage0_amd import synth
+    from long_context_sparse_stage0_amd.workloads import SWEEP
+    dev = torch.device("cuda:0")
+    for w in SWEEP:
+        x = synth.prefill_inputs(w)
+        q, k, v, hc = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "head_cls"))
+        del x
+        B, Hq, T, D = q.shape
+        nc = -(-T // 64)
+        W = -(-nc // 64)
+        out = torch.empty_like(q)
+        ab = torch.empty((B, w.Hkv, T, W), dtype=torch.int64, device=dev)
+        p = dash.make_params(B, Hq, w.Hkv, T, D, alpha=w.alpha, gamma=w.gamma, enable_gqa=True,
+                             dtype=torch.bfloat16)
+        ws = dash.alloc_workspace(dash.workspace_size("prefill", p), dev)
+        kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=True)
+        dash.prefill_stage(0, q, k, v, hc, out, ws, **kw)
+        dash.prefill_stage(1, q, k, v, hc, out, ws, active_blocks=ab, **kw)
+        torch.cuda.synchronize()
+        pc = popcount64(ab).sum(dim=-1).to(torch.float64)
+        routed = (torch.arange(T, device=dev) // 64).to(torch.float64).sum() * B * w.Hkv
+        active = float(pc.sum() / routed)
+        flops2 = float(w.G * 4 * D * (64.0 * pc.sum()
+                                      + B * w.Hkv * (torch.arange(T, device=dev) % 64 + 1).sum()))
+        del ab, pc
+
+        def step():
+            for s in range(3):
+                dash.prefill_stage(s, q, k, v, hc, out, ws, **kw)
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        line = {"workload": w.name, "alpha": w.alpha, "needle_lambda": w.needle_lambda,
+                "active_fraction": active, "ms_per_prefill": ms, "tokens_per_s": B * T / (ms / 1e3),
+                "stage2_algorithmic_flops": flops2}
+        print(json.dumps(line), flush=True)
+        log(f"{w.name}: active {active:.3f}, {ms:.2f} ms, {B * T / (ms / 1e3):.3e} tokens/s")
+        del q, k, v, hc, out, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +329,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="report the 64K sparsity sweep (one JSON line per cell) instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -288,6 +343,9 @@ def main():
     from long_context_sparse_stage0_amd.workloads import ALL, DECODE_64K_B16
     dash.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        bench_sweep(args, dash, torch)
+        return
     w = ALL[args.workload]
     pre = bench_prefill(args, w, dash, torch)
     dec = None if args.no_decode else bench_decode(args, DECODE_64K_B16, dash, torch)
