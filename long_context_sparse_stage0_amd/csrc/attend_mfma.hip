@@ -9,10 +9,10 @@
 // materialisation).  All G query heads of a KV head share the mask and the weights.
 //
 // Work unit: one workgroup per (b, kv head, R consecutive rows inside one 64-row block),
-// i.e. R x G query vectors (256 for G >= 4), 32 per wave.  The workgroup walks the union
-// of its rows' mask words in increasing chunk order (a visit list built in LDS), then the
-// diagonal chunk; per visit, each row gets bias log2(w_bar) where its own bit is set and
-// -inf where it is not, so the union walk computes exactly the per-row result.
+// i.e. R x G query vectors (256 for G >= 4), 32 per wave.  The workgroup visits the
+// diagonal chunk, then the union of its rows' mask words in increasing chunk order (a visit
+// list built in LDS); per routed visit, each row gets bias log2(w_bar) where its own bit is
+// set and -inf where it is not, so the union walk computes exactly the per-row result.
 //
 // MFMA mapping (16x16x32, wave64; lane l, k-slot (l/16, i)):
 //   S^T = K Q^T  : A = K rows, B = Q^T.  The 16 rows of a key tile are permuted so that
@@ -21,10 +21,12 @@
 //   O^T += V^T P^T: B = P^T straight from those registers (k-slot i <-> key 8(l/16)+i),
 //                  A = V^T rows read as one 16-byte LDS load from a chunk-transposed copy
 //                  of V ([chunk][d][64 keys]) that Stage 0's companion kernel writes.
-// Softmax runs in base 2 (the logit scale carries log2 e); the running max starts at a
-// large finite negative value so a query whose row is masked for a whole chunk stays NaN-
-// free.  K/V tiles are register-prefetched one visit ahead into the other of two LDS
-// buffers.
+// Softmax runs in base 2: Q is multiplied once by the logit scale times log2 e (rounded to
+// bf16, a relative change of at most 2^-9 per element).  The diagonal chunk, visited first,
+// sets each query column's reference max m from its own keys; on every routed visit the QK
+// accumulator starts at bias - m, so the MFMA returns the base-2 exponent itself, and the
+// column sums of the bf16 probabilities come from one more MFMA with an all-ones operand.
+// K/V tiles are register-prefetched one visit ahead into the other of two LDS buffers.
 //
 // LDS layout: a 16-byte LDS access by a full wave is served in two half-wave passes, and a
 // pass is conflict free when its 32 lanes hit 32 distinct 16-byte slots modulo 512 bytes
@@ -43,9 +45,12 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;
 constexpr int kXcds = 8;            // accelerator complex dies; workgroups are dealt round-robin
-// A lane's 16 unnormalised probabilities of a chunk may sum to at most 2^8 before the
-// column's reference max is raised; a larger sum, an overflow or a NaN triggers the rescale.
-constexpr float kSumCap = 256.0f;
+// A column's 64 unnormalised probabilities of a chunk may sum to at most 2^11 before its
+// reference max is raised; a larger sum, an overflow or a NaN triggers the rescale.
+constexpr float kColCap = 2048.0f;
+// A operand of all ones: the MFMA then returns each column's sum of the B operand
+__device__ const bf16x8 kOnes = {(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f,
+                                 (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
 // dword 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, offsets in
 // bytes, bounds checked against the record count)
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -62,10 +67,6 @@ __device__ __forceinline__ float rowgroup_max(float v) {
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
 }
 
 // Swizzle of the 16-byte chunk index inside a K row (D/8 chunks per row).  A half-wave's
@@ -166,13 +167,13 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     } else {
       for (int r = 0; r < R; ++r) u |= rowbits[r][tid];
     }
-    int o = woff[tid];
+    int o = woff[tid] + 1;
     while (u) {
       visit[o++] = (uint16_t)(64 * tid + __builtin_ctzll(u));
       u &= u - 1;
     }
   }
-  if (tid == 0) visit[woff[nw_route]] = (uint16_t)it;
+  if (tid == 0) visit[0] = (uint16_t)it;
   __syncthreads();
   const int nvis = woff[nw_route] + 1;
 
@@ -193,6 +194,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * a.scale_log2);
       if (!qok[qt]) v = bf16x8{};
       qop[qt][ks] = v;
     }
@@ -291,9 +294,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     lsum[qt] = 0.f;
     tloc[qt] = (row0 + qrow[qt]) & 63;
   }
-  const float sl2 = a.scale_log2;
 
-  // one visit of chunk visit[vi]; DIAG: the query block's own chunk (always the last visit)
+  // one visit of chunk visit[vi]; DIAG: the query block's own chunk (always the first visit)
   auto visit_chunk = [&](int vi, auto diag_tag) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     const int buf = vi & 1;
@@ -303,10 +305,10 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     for (int qt = 0; qt < QT; ++qt)
       bias[qt] = (DIAG || DENSE) ? 0.f : (onnext[qt] ? fast_log2(wnext[qt]) : -INFINITY);
     __syncthreads();
-    if (!DIAG) {
+    if (vi + 1 < nvis) {
       const int cn = visit[vi + 1];
       prefetch(cn);
-      if (cn != it) fetch_weight(cn);
+      fetch_weight(cn);
     }
     // a wave none of whose rows has this routed chunk adds exactly nothing (p = 0, no
     // rescale): it only takes part in the tile loads and leaves its SIMD to the other wave
@@ -321,77 +323,94 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
 
     // S^T for 64 keys: tile kt = 2 p + half
     floatx4 sc[QT][4];
+    floatx4 seed[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float off = DIAG ? 0.f : bias[qt] - m[qt];
+      seed[qt] = floatx4{off, off, off, off};
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int p = kt >> 1, half = kt & 1;
       const int key = 32 * p + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
       const int ksw = kswz<D>(key);        // p and half do not change the swizzle
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sc[qt][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(kl + key * KP + ((4 * ks + lg) ^ ksw) * 16);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) sc[qt][kt] = mfma16(ka, qop[qt][ks], sc[qt][kt]);
+        for (int qt = 0; qt < QT; ++qt)
+          sc[qt][kt] = mfma16(ka, qop[qt][ks], ks == 0 ? seed[qt] : sc[qt][kt]);
       }
     }
 
-    // online softmax per query column; build P^T operands.  Probabilities are taken
-    // relative to the column's reference max m; the max of the chunk is only computed when
-    // a lane's partial sum exceeds kSumCap (or is not a number), which also catches
-    // the first visited chunk, where m is still the initial large negative value.
-    bf16x8 pop[QT][2];
+    // online softmax per query column; build P^T operands.  On routed visits x is already
+    // the exponent relative to the column's reference max m; the chunk's max is only taken
+    // when a column's probability sum exceeds kColCap (or is not a number).
+    float x[QT][16];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float x[16];
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
-          x[4 * kt + j] = (DIAG && key > tloc[qt]) ? -INFINITY : sc[qt][kt][j];
+          x[qt][4 * kt + j] = (DIAG && key > tloc[qt]) ? -INFINITY : sc[qt][kt][j];
         }
-      float pr[16];
-      float off = bias[qt] - m[qt];
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[i] = fast_exp2(fmaf(x[i], sl2, off));
-        ps += pr[i];
-      }
-      if (__builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0ull) {
-        // raise the reference max to this chunk's max logit, rescale O and l, redo p
-        float mr = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) mr = fmaxf(fmaxf(mr, x[i]), x[i + 1]);
-        mr = rowgroup_max(fmaxf(mr, x[15]));
-        const float mn = fmaxf(m[qt], fmaf(mr, sl2, bias[qt]));
-        const float corr = fast_exp2(m[qt] - mn);
-        m[qt] = mn;
-        lsum[qt] *= corr;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
-        off = bias[qt] - mn;
-        ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pr[i] = fast_exp2(fmaf(x[i], sl2, off));
-          ps += pr[i];
-        }
-      }
-      lsum[qt] += ps;
+    // bf16 probabilities 2^(x - sh) as the PV operand (half 0: keys 32p + 8 lg + j, half 1:
+    // + 4), and their column sums from the matrix cores (all-ones A operand)
+    bf16x8 pop[QT][2];
+    floatx4 csum[QT];
+    auto probs = [&](int qt, float sh) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         bf16x8 v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v[j] = (bf16)pr[8 * p + j];          // half 0: keys 32p + 8 lg + j
-          v[4 + j] = (bf16)pr[8 * p + 4 + j];  // half 1: keys 32p + 8 lg + 4 + j
+          v[j] = (bf16)fast_exp2(x[qt][8 * p + j] - sh);
+          v[4 + j] = (bf16)fast_exp2(x[qt][8 * p + 4 + j] - sh);
         }
         pop[qt][p] = v;
       }
+      csum[qt] = mfma16(kOnes, pop[qt][0], floatx4{0.f, 0.f, 0.f, 0.f});
+      csum[qt] = mfma16(kOnes, pop[qt][1], csum[qt]);
+    };
+    auto colmax = [&](int qt) {
+      float mr = fmaxf(fmaxf(x[qt][0], x[qt][1]), x[qt][2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mr = fmaxf(fmaxf(mr, x[qt][i]), x[qt][i + 1]);
+      return rowgroup_max(fmaxf(mr, x[qt][15]));
+    };
+    if (DIAG) {
+      // first visit: the reference max is this chunk's max logit (the query's own key is
+      // always present), so every later offset bias - m is of moderate size
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        m[qt] = colmax(qt);
+        probs(qt, m[qt]);
+      }
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) probs(qt, 0.f);
+      bool over = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) over = over || !(csum[qt][0] <= kColCap);
+      if (__builtin_amdgcn_ballot_w64(over) != 0ull) {
+        // raise the reference max by this chunk's largest offset logit, rescale O and l
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float mr = fmaxf(colmax(qt), 0.f);
+          const float corr = fast_exp2(-mr);
+          m[qt] += mr;
+          lsum[qt] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt] *= corr;
+          probs(qt, mr);
+        }
+      }
     }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) lsum[qt] += csum[qt][0];
 
     // O^T += V^T P^T
 #pragma unroll
@@ -407,14 +426,13 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   };
 
   prefetch(visit[0]);
-  if (visit[0] != it) fetch_weight(visit[0]);
-  for (int vi = 0; vi + 1 < nvis; ++vi) visit_chunk(vi, std::false_type{});
-  visit_chunk(nvis - 1, std::true_type{});
+  visit_chunk(0, std::true_type{});
+  for (int vi = 1; vi < nvis; ++vi) visit_chunk(vi, std::false_type{});
 
   // ---- normalise and write
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float l = xor16_sum(lsum[qt]);
+    const float l = lsum[qt];               // full column sum (every lane of the column)
     const float rl = 1.0f / l;
     if (!qok[qt]) continue;
     bf16* op = (bf16*)a.out + ((size_t)(b * a.Hq + qh[qt]) * T + row0 + qrow[qt]) * D;

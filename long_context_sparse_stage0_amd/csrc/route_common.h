@@ -112,12 +112,41 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
   return tau;
 }
 
+// Start point from the first pass's moments (own design, alpha = 1.5).  With the scores
+// modelled as Gaussian with the mean and variance v of the current support (n entries),
+// sum_c [y_c - tau]_+^2 at tau = mean + a sqrt(v) is n v g(a), g(a) = E[(Z - a)_+^2]
+// = (1 + a^2) Q(a) - a phi(a) for a standard normal Z (Q its upper tail, phi its density).
+// Returns the a solving n v g(a) = target by Newton steps from a = 0 (g is decreasing and
+// convex, g' = -2 (phi(a) - a Q(a))).  A target above 1 leans the estimate left of tau*;
+// the caller still checks that the point is a lower bound before relying on it.
+__device__ __forceinline__ float gauss_sq_tail_offset(float nv, float target) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const float Q = 0.5f * erfcf(a * 0.70710678f);
+    const float ph = 0.39894228f * expf(-0.5f * a * a);
+    const float g = fmaf(a, a, 1.f) * Q - a * ph;
+    const float h = ph - a * Q;
+    a += (nv * g - target) / (2.f * nv * h);
+  }
+  return a;
+}
+
 template <int MODE>
 __device__ __forceinline__ float entmax_weight(float y, float tau, float inv, float rz) {
   const float d = y - tau;
   if (!(d > 0.f)) return 0.f;
   const float p = (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
   return p * rz;
+}
+
+// The same weight without a branch, for bulk use: max(d, 0) gives +0 outside the support.
+template <int MODE>
+__device__ __forceinline__ float entmax_weight_nonneg(float y, float tau, float inv, float rz) {
+  const float d = fmaxf(y - tau, 0.f);
+  if (MODE == kAlpha15) return d * (d * rz);
+  if (MODE == kAlpha2) return d * rz;
+  return d > 0.f ? pow_pos(d, inv) * rz : 0.f;
 }
 
 }  // namespace dash

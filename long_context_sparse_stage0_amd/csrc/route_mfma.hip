@@ -19,7 +19,9 @@
 // of 8 -- enough for mask bits to agree with a float64 reference outside a 1e-4 margin.
 //
 // Threshold solver (own design, see route_common.h): monotone steps from max y - 1 with an
-// exact closed-form finish for alpha = 1.5 and 2.  Per pass each lane reduces its own
+// exact closed-form finish for alpha = 1.5 and 2; for alpha = 1.5 on long rows the second
+// point comes from a Gaussian model of the first pass's moments, checked to be a lower
+// bound of tau* before the iteration continues from it (about half the passes).  Per pass each lane reduces its own
 // values, the four 16-lane groups combine by lane shuffles, and the eight waves combine
 // through a double-buffered LDS table (one barrier per pass); every wave then holds the
 // same totals for all 32 queries and takes the same decision.
@@ -36,6 +38,11 @@ namespace {
 
 // 64-bit mask words per row that can hold routed chunks (plus one spare)
 constexpr int kRouteMaskWords = (kMaxRouted + 63) / 64 + 1;
+// Moment-based start of the threshold solver (alpha = 1.5): used from this many routed
+// chunks on (shorter rows need few passes, and the start costs about one pass of a short
+// row), aiming at a squared-excess sum of kModelTarget, i.e. a little left of tau*.
+constexpr int kModelStartChunks = 256;
+constexpr float kModelTarget = 1.5f;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -142,15 +149,19 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
 
   // ---- threshold solver for the 32 queries
-  float tau[QTR], hi[QTR], zs[QTR];
-  bool done[QTR];
+  float tau[QTR], hi[QTR], zs[QTR], lo[QTR];
+  bool done[QTR], probe[QTR];
 #pragma unroll
   for (int qt = 0; qt < QTR; ++qt) {
     tau[qt] = 0.f;
     hi[qt] = 0.f;
     zs[qt] = 1.f;
+    lo[qt] = 0.f;
     done[qt] = true;
+    probe[qt] = false;
   }
+  // long rows (alpha = 1.5) take a moment-based start after the first pass
+  const bool model_start = MODE == kAlpha15 && it >= kModelStartChunks;
   const float inv = 1.0f / (a.alpha - 1.0f);
   int buf = 0;
   if (it > 0) {
@@ -240,6 +251,13 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
           }
         } else if (MODE == kAlpha15) {
           const float F = s2 - 1.0f;
+          if (probe[qt] && F < 0.f) {
+            // the moment-based point lies past tau*: resume from the plain step
+            probe[qt] = false;
+            tau[qt] = lo[qt];
+            continue;
+          }
+          probe[qt] = false;
           const float disc = fmaf(s1, s1, -cnt * F);
           bool fin = false;
           if (disc >= 0.f) {
@@ -249,7 +267,20 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
               done[qt] = fin = true;
             }
           }
-          if (!fin) tau[qt] = fminf(tau[qt] + fmaxf(F / (2.0f * s1), mn), hi[qt]);
+          if (!fin) {
+            float nt = fminf(tau[qt] + fmaxf(F / (2.0f * s1), mn), hi[qt]);
+            if (model_start && pass == 0) {
+              const float mean = s1 / cnt, var = fmaxf(fmaf(-mean, mean, s2 / cnt), 0.f);
+              const float est =
+                  tau[qt] + mean + gauss_sq_tail_offset(cnt * var, kModelTarget) * sqrtf(var);
+              if (est > nt) {               // false for a NaN estimate
+                lo[qt] = nt;
+                nt = fminf(est, hi[qt]);
+                probe[qt] = true;
+              }
+            }
+            tau[qt] = nt;
+          }
         } else {
           const float F = s2 - 1.0f;
           const float step = F / (inv * s1);
@@ -294,11 +325,11 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   // jj = g, g + G, ... (coalesced 16-chunk runs), and each row's 16 mask bits of a tile are
   // gathered from the four 16-lane groups and stored as one 16-bit word.
   if (it > 0) {
-    const float rG = 1.0f / (float)G;
     const int g = l16 % G;
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) {
-      const float rz = 1.0f / zs[qt];
+      // 1/G of the GQA mean folded into each head's normaliser
+      const float rz = 1.0f / (zs[qt] * (float)G);
       const int r = qrow[qt];
       const bool row_ok = (row0 + r) < T;
       float* wrow = a.wbar + ((size_t)bk * a.rows + row0 + r) * a.wbar_ld;
@@ -311,9 +342,9 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
         unsigned nib = 0;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float pw = entmax_weight<MODE>(y[j][qt][jj], tau[qt], inv, rz);
-          wb[jj] = head_sum(pw, G) * rG;
-          nib |= (wb[jj] > 0.f && c0 + jj < it) ? (1u << jj) : 0u;
+          // chunks past it hold y = -inf, so their weight and bit are 0
+          wb[jj] = head_sum(entmax_weight_nonneg<MODE>(y[j][qt][jj], tau[qt], inv, rz), G);
+          nib |= (wb[jj] > 0.f ? 1u : 0u) << jj;
         }
         // w_bar stores: this lane's slots jj = g + G s
 #pragma unroll
