@@ -42,7 +42,7 @@ constexpr int kRouteMaskWords = (kMaxRouted + 63) / 64 + 1;
 // chunks on (shorter rows need few passes, and the start costs about one pass of a short
 // row), aiming at a squared-excess sum of kModelTarget, i.e. a little left of tau*.
 constexpr int kModelStartChunks = 256;
-constexpr float kModelTarget = 1.5f;
+constexpr float kModelTarget = 1.25f;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -252,9 +252,10 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
         } else if (MODE == kAlpha15) {
           const float F = s2 - 1.0f;
           if (probe[qt] && F < 0.f) {
-            // the moment-based point lies past tau*: resume from the plain step
+            // the moment-based point lies past tau*.  F is convex, so its tangent there
+            // meets zero at or below tau*: resume from that point or the plain step
             probe[qt] = false;
-            tau[qt] = lo[qt];
+            tau[qt] = fmaxf(lo[qt], tau[qt] + F / (2.0f * s1));
             continue;
           }
           probe[qt] = false;

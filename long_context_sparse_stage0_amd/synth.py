@@ -172,3 +172,39 @@ def decode_inputs(w: Workload, workers: int = 8) -> Dict[str, np.ndarray]:
 
     _parallel(one, [(b, h) for b in range(B) for h in range(Hkv)], workers)
     return {"q_steps": qs, "k_cache": k, "v_cache": v, "head_cls": head_cls(w)}
+
+
+def chunk_valued_prefill(T: int, D: int, G: int, dist: str, amp: float, seed: int,
+                         dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """Prefill inputs whose chunks carry prescribed values (B = 1, one kv head, G heads).
+
+    Every key of chunk c equals one vector whose first coordinate is u_c, drawn from `dist`,
+    and whose other coordinates are N(0, 1); head_cls is zero; every query of head h is
+    amp * (1 + h / 32) along the first axis.  So the chunk-level logits of a row are
+    u_c scaled by the query's length, with the shape of `dist`:
+      "uniform"        u ~ U(0, 1)
+      "left_outliers"  u ~ N(0, 0.05), with a tenth of the chunks at N(-0.8, 0.01)
+      "exp_left"       u = -E, E ~ Exp(mean 0.1)
+    V ~ N(0, 1).  Returns q [1,G,T,D], k, v [1,1,T,D], head_cls [1,D] as float32 arrays
+    holding values representable in `dtype`."""
+    nc = -(-T // CHUNK)
+    r = _rng(seed, 7001)
+    if dist == "uniform":
+        u = r.uniform(0.0, 1.0, nc)
+    elif dist == "left_outliers":
+        u = r.normal(0.0, 0.05, nc)
+        low = r.random(nc) < 0.1
+        u[low] = r.normal(-0.8, 0.01, int(low.sum()))
+    elif dist == "exp_left":
+        u = -r.exponential(0.1, nc)
+    else:
+        raise ValueError(f"unknown distribution {dist}")
+    kc = _rng(seed, 7002).standard_normal((nc, D))
+    kc[:, 0] = u
+    k = np.repeat(kc, CHUNK, axis=0)[:T][None, None]
+    v = _rng(seed, 7003).standard_normal((1, 1, T, D))
+    q = np.zeros((1, G, T, D))
+    for h in range(G):
+        q[0, h, :, 0] = amp * (1.0 + h / 32.0)
+    return {"q": _store(q, dtype), "k": _store(k, dtype), "v": _store(v, dtype),
+            "head_cls": np.zeros((1, D), np.float32)}

@@ -92,6 +92,30 @@ def test_prefill_16k_gqa_sampled_rows(dash):
     check_prefill(run_prefill(dash, w, rows=rows), w)
 
 
+@pytest.mark.parametrize("dist", ["uniform", "left_outliers", "exp_left"])
+def test_prefill_router_shaped_scores(dash, dist):
+    """Chunk logits with a uniform, a left-outlier and a left-skewed distribution over
+    300 chunks (16 heads): on rows past 256 routed chunks the router's Gaussian start point
+    lies past the threshold for these shapes, so the fallback step decides the result."""
+    T, D, G = 64 * 300, 128, 16
+    x = synth.chunk_valued_prefill(T, D, G, dist, amp=2.0 * math.sqrt(D), seed=4242)
+    say(f"[parity] prefill shaped scores {dist} T={T} G={G}")
+    q, k, v, hc = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "head_cls"))
+    out, ab, bw = dash.prefill(q, k, v, hc, alpha=1.5, enable_gqa=True,
+                               return_active_blocks=True, return_block_weights=True)
+    torch.cuda.synchronize()
+    rows = np.array([64 * 200 + 5, 64 * 256, 64 * 256 + 63, 64 * 280 + 17, T - 1])
+    ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=1.5, rows=rows)
+    nc = -(-T // 64)
+    e_out = compare_out(out.float().cpu().numpy()[:, :, rows], ref["out"], "bf16")
+    e_w = compare_weights(bw.cpu().numpy()[:, :, rows], ref["w_bar"])
+    amb = compare_mask(unpack_words(ab.cpu().numpy(), nc)[:, :, rows], ref["mask"],
+                       ref["margin"], rows)
+    frac = O.zero_fraction(ref["w_bar"], rows)
+    say(f"[parity]   out err {e_out:.2e}  w err {e_w:.2e}  near-threshold flips {amb}  "
+        f"zero-weight fraction {frac:.3f}")
+
+
 def test_dense_causal_matches_textbook(dash):
     rng = np.random.default_rng(3)
     B, Hq, Hkv, T, D = 1, 4, 2, 300, 128
