@@ -42,6 +42,10 @@ constexpr int kRouteMaskWords = (kMaxRouted + 63) / 64 + 1;
 // chunks on (shorter rows need few passes, and the start costs about one pass of a short
 // row), aiming at a squared-excess sum of kModelTarget, i.e. a little left of tau*.
 constexpr int kModelStartChunks = 256;
+// dword 3 of a raw buffer descriptor (32-bit data, byte offsets, bounds checked against the
+// record count), and a byte offset beyond any record count used here
+constexpr int kWbarRsrcWord3 = 0x00020000;
+constexpr int kDropOffset = 0x7ffffff0;
 constexpr float kModelTarget = 1.25f;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
@@ -60,6 +64,15 @@ __device__ __forceinline__ float head_sum(float v, int G) {
   if (G >= 8) v += dpp<0x141>(v);   // row_half_mirror
   if (G >= 16) v += dpp<0x140>(v);  // row_mirror
   return v;
+}
+
+// one step of head_sum applied to every value of query tile qt
+template <int CTRL, int MT, int QTR>
+__device__ __forceinline__ void head_step(float (&v)[MT][QTR][4], int qt) {
+#pragma unroll
+  for (int j = 0; j < MT; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) v[j][qt][jj] += dpp<CTRL>(v[j][qt][jj]);
 }
 
 // reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950
@@ -329,31 +342,46 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     const int g = l16 % G;
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) {
-      // 1/G of the GQA mean folded into each head's normaliser
+      // 1/G of the GQA mean folded into each head's normaliser; the weights replace the
+      // scores in place (chunks past it hold y = -inf, so their weight and bit are 0)
       const float rz = 1.0f / (zs[qt] * (float)G);
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          y[j][qt][jj] = entmax_weight_nonneg<MODE>(y[j][qt][jj], tau[qt], inv, rz);
+      // GQA sum over the G adjacent lanes of a row, one (wave-uniform) test of G per step
+      // for all of the lane's weights
+      if (G >= 2) head_step<0xB1>(y, qt);
+      if (G >= 4) head_step<0x4E>(y, qt);
+      if (G >= 8) head_step<0x141>(y, qt);
+      if (G >= 16) head_step<0x140>(y, qt);
+      // w_bar stores go through a buffer descriptor over this workgroup's rows that ends at
+      // the last row below T: a lane with nothing to store uses an offset past the end, which
+      // the hardware drops, so the stores need no branches
       const int r = qrow[qt];
-      const bool row_ok = (row0 + r) < T;
-      float* wrow = a.wbar + ((size_t)bk * a.rows + row0 + r) * a.wbar_ld;
+      const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          a.wbar + ((size_t)bk * a.rows + row0) * a.wbar_ld, (short)0,
+          min(16 * QTR / G, T - row0) * a.wbar_ld * 4, kWbarRsrcWord3);
+      const int rbase = r * a.wbar_ld;
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         if (j >= nj) continue;
         const int ct = wv + NW * j;
         const int c0 = 16 * ct + 4 * lg;
-        float wb[4];
+        const float* wb = y[j][qt];
         unsigned nib = 0;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          // chunks past it hold y = -inf, so their weight and bit are 0
-          wb[jj] = head_sum(entmax_weight_nonneg<MODE>(y[j][qt][jj], tau[qt], inv, rz), G);
-          nib |= (wb[jj] > 0.f ? 1u : 0u) << jj;
-        }
-        // w_bar stores: this lane's slots jj = g + G s
+        for (int jj = 0; jj < 4; ++jj) nib |= (wb[jj] > 0.f ? 1u : 0u) << jj;
+        // w_bar stores at set bits: this lane's slots are jj = g + G s < 4 (G a power of two)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+          if (s > 0 && G * s >= 4) break;      // wave-uniform
           const int jj = g + G * s;
-          if (jj >= 4) break;
           const float v = jj == 0 ? wb[0] : jj == 1 ? wb[1] : jj == 2 ? wb[2] : wb[3];
-          if (row_ok && ((nib >> jj) & 1u)) wrow[c0 + jj] = v;
+          const bool st = jj < 4 && ((nib >> jj) & 1u);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), wrsrc,
+                                                st ? (rbase + c0 + jj) * 4 : kDropOffset, 0, 0);
         }
         // mask bits of the row for chunks 16 ct + [0, 16)
         unsigned f = nib << (4 * lg);
@@ -363,7 +391,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
           const auto y2 = __builtin_amdgcn_permlane32_swap(f, f, false, false);
           f = y2[0] | y2[1];
         }
-        if (lg == 0 && g == 0) mbits16[r][ct] = (uint16_t)f;
+        mbits16[r][ct] = (uint16_t)f;           // the same word from every lane of row r
       }
     }
   }
