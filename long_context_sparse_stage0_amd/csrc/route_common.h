@@ -20,6 +20,9 @@
 // Every step is a valid lower bound (Newton from the left on a convex function, or a
 // point where F is still positive), so the iteration is monotone and each pass that does
 // not finish drops at least one element.
+// For alpha = 1.5 and at least kEntmaxModelMinN entries, the second point comes from a
+// Gaussian model of the first pass's moments instead (see gauss_sq_tail_offset); it is used
+// only after a pass confirms F >= 0 there, so the same invariants hold.
 #pragma once
 #include "dash_internal.h"
 
@@ -39,6 +42,31 @@ struct WaveReduce {
   __device__ __forceinline__ float max(float v) const { return wave_max(v); }
 };
 
+// Start point from the first pass's moments (own design, alpha = 1.5).  With the scores
+// modelled as Gaussian with the mean and variance v of the current support (n entries),
+// sum_c [y_c - tau]_+^2 at tau = mean + a sqrt(v) is n v g(a), g(a) = E[(Z - a)_+^2]
+// = (1 + a^2) Q(a) - a phi(a) for a standard normal Z (Q its upper tail, phi its density).
+// Returns the a solving n v g(a) = target by Newton steps from a = 0 (g is decreasing and
+// convex, g' = -2 (phi(a) - a Q(a))).  A target above 1 leans the estimate left of tau*;
+// the caller still checks that the point is a lower bound before relying on it.
+__device__ __forceinline__ float gauss_sq_tail_offset(float nv, float target) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const float Q = 0.5f * erfcf(a * 0.70710678f);
+    const float ph = 0.39894228f * expf(-0.5f * a * a);
+    const float g = fmaf(a, a, 1.f) * Q - a * ph;
+    const float h = ph - a * Q;
+    a += (nv * g - target) / (2.f * nv * h);
+  }
+  return a;
+}
+
+// Moment-based start (alpha = 1.5) from this many entries on, aiming at a squared-excess
+// sum of kEntmaxModelTarget, i.e. a little left of tau*.
+constexpr int kEntmaxModelMinN = 256;
+constexpr float kEntmaxModelTarget = 1.25f;
+
 // y[NR]: this lane's scores ((alpha-1)-scaled), -inf for absent entries.
 // Returns tau; *zsum receives sum_c [y_c - tau]_+^(1/(alpha-1)) (the normaliser).
 template <int MODE, int NR, class Red>
@@ -53,6 +81,12 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
   const float hi = m - ((MODE == kAlpha15) ? rsqrtf((float)n)
                                             : (MODE == kAlpha2 ? 1.0f / (float)n
                                                                : pow_pos((float)n, 1.0f - alpha)));
+  // alpha = 1.5 with many entries: after the first pass, a point from the support's moments
+  // (gauss_sq_tail_offset); the next pass checks it is still a lower bound of tau*, else the
+  // solver resumes at the tangent of F there, which lies at or below tau* (F is convex)
+  const bool model = MODE == kAlpha15 && n >= kEntmaxModelMinN;
+  bool probe = false;
+  float lo = tau;
   for (int it = 0; it < 96; ++it) {
     float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
 #pragma unroll
@@ -86,6 +120,12 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
       tau = fminf(tau + fmaxf(delta, mn), hi);
     } else if (MODE == kAlpha15) {
       const float F = s2 - 1.0f;
+      if (probe && F < 0.f) {
+        probe = false;
+        tau = fmaxf(lo, tau + F / (2.0f * s1));
+        continue;
+      }
+      probe = false;
       const float disc = fmaf(s1, s1, -cnt * F);
       if (disc >= 0.f) {
         const float delta = (s1 - sqrtf(disc)) / cnt;
@@ -94,7 +134,18 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
           break;
         }
       }
-      tau = fminf(tau + fmaxf(F / (2.0f * s1), mn), hi);
+      float nt = fminf(tau + fmaxf(F / (2.0f * s1), mn), hi);
+      if (model && it == 0) {
+        const float mean = s1 / cnt, var = fmaxf(fmaf(-mean, mean, s2 / cnt), 0.f);
+        const float est =
+            tau + mean + gauss_sq_tail_offset(cnt * var, kEntmaxModelTarget) * sqrtf(var);
+        if (est > nt) {                       // false for a NaN estimate
+          lo = nt;
+          nt = fminf(est, hi);
+          probe = true;
+        }
+      }
+      tau = nt;
     } else {
       const float F = s2 - 1.0f;
       const float step = F / (inv * s1);
@@ -110,26 +161,6 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
   }
   *zsum = red.sum(z);
   return tau;
-}
-
-// Start point from the first pass's moments (own design, alpha = 1.5).  With the scores
-// modelled as Gaussian with the mean and variance v of the current support (n entries),
-// sum_c [y_c - tau]_+^2 at tau = mean + a sqrt(v) is n v g(a), g(a) = E[(Z - a)_+^2]
-// = (1 + a^2) Q(a) - a phi(a) for a standard normal Z (Q its upper tail, phi its density).
-// Returns the a solving n v g(a) = target by Newton steps from a = 0 (g is decreasing and
-// convex, g' = -2 (phi(a) - a Q(a))).  A target above 1 leans the estimate left of tau*;
-// the caller still checks that the point is a lower bound before relying on it.
-__device__ __forceinline__ float gauss_sq_tail_offset(float nv, float target) {
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const float Q = 0.5f * erfcf(a * 0.70710678f);
-    const float ph = 0.39894228f * expf(-0.5f * a * a);
-    const float g = fmaf(a, a, 1.f) * Q - a * ph;
-    const float h = ph - a * Q;
-    a += (nv * g - target) / (2.f * nv * h);
-  }
-  return a;
 }
 
 template <int MODE>

@@ -38,15 +38,10 @@ namespace {
 
 // 64-bit mask words per row that can hold routed chunks (plus one spare)
 constexpr int kRouteMaskWords = (kMaxRouted + 63) / 64 + 1;
-// Moment-based start of the threshold solver (alpha = 1.5): used from this many routed
-// chunks on (shorter rows need few passes, and the start costs about one pass of a short
-// row), aiming at a squared-excess sum of kModelTarget, i.e. a little left of tau*.
-constexpr int kModelStartChunks = 256;
 // dword 3 of a raw buffer descriptor (32-bit data, byte offsets, bounds checked against the
 // record count), and a byte offset beyond any record count used here
 constexpr int kWbarRsrcWord3 = 0x00020000;
 constexpr int kDropOffset = 0x7ffffff0;
-constexpr float kModelTarget = 1.25f;
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -174,7 +169,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     probe[qt] = false;
   }
   // long rows (alpha = 1.5) take a moment-based start after the first pass
-  const bool model_start = MODE == kAlpha15 && it >= kModelStartChunks;
+  const bool model_start = MODE == kAlpha15 && it >= kEntmaxModelMinN;
   const float inv = 1.0f / (a.alpha - 1.0f);
   int buf = 0;
   if (it > 0) {
@@ -286,7 +281,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
             if (model_start && pass == 0) {
               const float mean = s1 / cnt, var = fmaxf(fmaf(-mean, mean, s2 / cnt), 0.f);
               const float est =
-                  tau[qt] + mean + gauss_sq_tail_offset(cnt * var, kModelTarget) * sqrtf(var);
+                  tau[qt] + mean + gauss_sq_tail_offset(cnt * var, kEntmaxModelTarget) * sqrtf(var);
               if (est > nt) {               // false for a NaN estimate
                 lo[qt] = nt;
                 nt = fminf(est, hi[qt]);
