@@ -107,7 +107,7 @@ PrefillLayout prefill_layout(const Dims& d) {
   L.summ = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
   L.ssplit = off;
-  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * d.nc * 2 * d.D * 2) : 0;
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * dash::split_bk_stride(d.nc, d.D) * 2) : 0;
   L.vt = off;
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * d.nc * d.D * 64 * 2) : 0;
   L.mask = off;

@@ -7,6 +7,16 @@
 
 namespace dash {
 
+// Tiled layout of the split summaries: tiles of 16 chunks per (b, kv head); in a tile, for
+// plane p (0 hi, 1 lo), 32-element slice ks and chunk r, 32 consecutive bf16.
+__host__ __device__ inline int split_tiles(int nc) { return (nc + 15) / 16; }
+__host__ __device__ inline size_t split_bk_stride(int nc, int D) {
+  return (size_t)split_tiles(nc) * 16 * 2 * D;
+}
+__host__ __device__ inline int split_offset(int c, int p, int e, int D) {
+  return (c >> 4) * 32 * D + ((p * (D / 32) + (e >> 5)) * 16 + (c & 15)) * 32 + (e & 31);
+}
+
 constexpr int kChunk = 64;          // tokens per chunk (the pages' only chunk size)
 constexpr int kMaxRouted = 2048;    // routed chunks per row held in registers (32 per lane)
 constexpr int kMaxRoutedRegs = kMaxRouted / 64;
@@ -92,8 +102,10 @@ struct AttendArgs {
   int list_ld;
 };
 
-// summ_split (nullable, bf16 inputs only): [B, Hkv, nc_alloc, 2, D] bf16 hi and lo planes of
-// the fp32 summaries (hi = bf16(x), lo = bf16(x - hi)) for the MFMA router.
+// summ_split (nullable, bf16 inputs only): bf16 hi and lo planes of the fp32 summaries
+// (hi = bf16(x), lo = bf16(x - hi)) for the MFMA router, tiled for its operand loads: per
+// (b, kv head) split_tiles(nc_alloc) tiles of 16 chunks, each [plane][D/32][16 chunks][32]
+// (see split_offset), so one wave-wide 16-byte load reads 1 KiB of contiguous memory.
 hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
                          int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,

@@ -121,7 +121,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   }
 
   // scores
-  const bf16* sp = ssplit + (size_t)bk * a.nc_alloc * 2 * D;
+  const bf16* sp = ssplit + (size_t)bk * split_bk_stride(a.nc_alloc, D);
   float y[MT][QTR][4];
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
@@ -130,13 +130,13 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) acc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (ct < ntile) {  // wave-uniform
+      // the tile's 16 chunk rows are allocated even past nc; rows past it are zeroed
       const int crow = 16 * ct + l16;
       const bool cok = crow < it;
-      const bf16* srow = sp + (size_t)(cok ? crow : 0) * 2 * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 hi = *reinterpret_cast<const bf16x8*>(srow + 32 * ks + 8 * lg);
-        bf16x8 lo = *reinterpret_cast<const bf16x8*>(srow + D + 32 * ks + 8 * lg);
+        bf16x8 hi = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 0, 32 * ks + 8 * lg, D));
+        bf16x8 lo = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 1, 32 * ks + 8 * lg, D));
         if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
 #pragma unroll
         for (int qt = 0; qt < QTR; ++qt) acc[qt] = mfma16(hi, qop[qt][ks], acc[qt]);

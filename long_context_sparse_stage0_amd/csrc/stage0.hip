@@ -76,12 +76,12 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = acc[e];
     if (ssplit != nullptr) {
-      bf16* sp = ssplit + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * 2 * D + lane * E;
+      bf16* sp = ssplit + (size_t)(b * Hkv + kvh) * split_bk_stride(nc_alloc, D);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bf16 hi = (bf16)acc[e];
-        sp[e] = hi;
-        sp[D + e] = (bf16)(acc[e] - (float)hi);
+        sp[split_offset(c, 0, lane * E + e, D)] = hi;
+        sp[split_offset(c, 1, lane * E + e, D)] = (bf16)(acc[e] - (float)hi);
       }
     }
     __syncthreads();
