@@ -52,16 +52,9 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// sum over the G adjacent lanes of a 16-lane row that hold the heads of one row
-__device__ __forceinline__ float head_sum(float v, int G) {
-  if (G >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (G >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  if (G >= 8) v += dpp<0x141>(v);   // row_half_mirror
-  if (G >= 16) v += dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
-// one step of head_sum applied to every value of query tile qt
+// one butterfly step of the sum over the G adjacent lanes of a 16-lane row that hold the
+// heads of one row, applied to every value of query tile qt; the steps for G = 2, 4, 8, 16
+// are the DPP moves quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
 template <int CTRL, int MT, int QTR>
 __device__ __forceinline__ void head_step(float (&v)[MT][QTR][4], int qt) {
 #pragma unroll
