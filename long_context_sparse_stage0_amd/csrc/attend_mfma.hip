@@ -26,7 +26,9 @@
 // sets each query column's reference max m from its own keys; on every routed visit the QK
 // accumulator starts at bias - m, so the MFMA returns the base-2 exponent itself, and the
 // column sums of the bf16 probabilities come from one more MFMA with an all-ones operand.
-// K/V tiles are register-prefetched one visit ahead into the other of two LDS buffers.
+// Visits go in rounds of two behind one workgroup barrier: the K/V tiles of a round's two
+// chunks are register-prefetched during the previous round and stored into two of four LDS
+// slots (the pair the round before last used).
 //
 // LDS layout: a 16-byte LDS access by a full wave is served in two half-wave passes, and a
 // pass is conflict free when its 32 lanes hit 32 distinct 16-byte slots modulo 512 bytes
@@ -102,8 +104,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   constexpr int VPTA = VPT > 0 ? VPT : 1;
   constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[4][KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[4][VBYTES];
   __shared__ uint64_t rowbits[RMAX][MAXW];
   __shared__ uint16_t visit[kMaxRouted + 2];
   __shared__ int woff[MAXW + 1];
@@ -218,8 +220,9 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   }
 #pragma unroll
   for (int i = 0; i < VPTA; ++i) voff[i] = (vseg0 + i * NT) * 16;
-  uint4 kreg[KPT], vreg[VPTA];
-  auto prefetch = [&](int c_any) {
+  uint4 kreg[2][KPT], vreg[2][VPTA];
+  auto prefetch = [&](int c_any, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
     const int c = __builtin_amdgcn_readfirstlane(c_any);
     const int keys_left = a.Tk - c * kChunk;            // > 0 for every visited chunk
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -228,53 +231,56 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtbase + (size_t)c * D * 64), (short)0, D * 64 * 2, kBufferRsrcWord3);
     if (SPLIT) {
-      kreg[0] = __builtin_bit_cast(uint4, kpart ? __builtin_amdgcn_raw_buffer_load_b128(kr, koff[0], 0, 0)
-                                                : __builtin_amdgcn_raw_buffer_load_b128(vr, voff[0], 0, 0));
+      kreg[S][0] = __builtin_bit_cast(uint4, kpart ? __builtin_amdgcn_raw_buffer_load_b128(kr, koff[0], 0, 0)
+                                                   : __builtin_amdgcn_raw_buffer_load_b128(vr, voff[0], 0, 0));
       return;
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
+      kreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
+      vreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
   };
   auto stash_v = [&](int buf, int seg, const uint4& val) {
     const int row = seg / 8, ch = seg % 8;
     *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + (ch ^ vswz(row)) * 16]) = val;
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
     if (SPLIT && !kpart) {
-      stash_v(buf, vseg0, kreg[0]);
+      stash_v(buf, vseg0, kreg[S][0]);
       return;
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int seg = tid + i * NT;
       const int row = seg / (D / 8), ch = seg % (D / 8);
-      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + (ch ^ kswz<D>(row)) * 16]) = kreg[i];
+      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + (ch ^ kswz<D>(row)) * 16]) = kreg[S][i];
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) stash_v(buf, vseg0 + i * NT, vreg[i]);
+    for (int i = 0; i < VPT; ++i) stash_v(buf, vseg0 + i * NT, vreg[S][i]);
   };
-  // routing weight and mask bit of this lane's rows for routed chunk c; the weight is
-  // loaded one visit ahead and only turned into a bias (log2 w, or -inf where the row's bit
-  // is clear) when the visit starts, so no wait on it stalls the tile prefetch
-  float wnext[QT];
-  bool onnext[QT];
+  // routing weight and mask bit of this lane's rows for routed chunk c, in set S (the first
+  // or second visit of a round); the weight is loaded one round ahead and only turned into a
+  // bias (log2 w, or -inf where the row's bit is clear) when the round starts, so no wait on
+  // it stalls the tile prefetch
+  float wnext[2][QT];
+  bool onnext[2][QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    wnext[qt] = 1.f;
-    onnext[qt] = true;
+    wnext[0][qt] = wnext[1][qt] = 1.f;
+    onnext[0][qt] = onnext[1][qt] = true;
   }
-  auto fetch_weight = [&](int c) {
+  auto fetch_weight = [&](int c, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
     if (DENSE) return;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int r = qrow[qt];
-      onnext[qt] = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
+      onnext[S][qt] = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
       const int t = min(row0 + r, a.rows - 1);
-      wnext[qt] = a.wbar[((size_t)bk * a.rows + t) * a.wbar_ld + c];
+      wnext[S][qt] = a.wbar[((size_t)bk * a.rows + t) * a.wbar_ld + c];
     }
   };
 
@@ -295,21 +301,11 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     tloc[qt] = (row0 + qrow[qt]) & 63;
   }
 
-  // one visit of chunk visit[vi]; DIAG: the query block's own chunk (always the first visit)
-  auto visit_chunk = [&](int vi, auto diag_tag) {
+  // the work of one visit on the tile in LDS slot buf; DIAG: the query block's own chunk
+  // (always the first visit)
+  auto visit_chunk = [&](int buf, const float (&bias)[QT], auto diag_tag) {
     constexpr bool DIAG = decltype(diag_tag)::value;
-    const int buf = vi & 1;
-    stash(buf);
-    float bias[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-      bias[qt] = (DIAG || DENSE) ? 0.f : (onnext[qt] ? fast_log2(wnext[qt]) : -INFINITY);
-    __syncthreads();
-    if (vi + 1 < nvis) {
-      const int cn = visit[vi + 1];
-      prefetch(cn);
-      fetch_weight(cn);
-    }
+    asm volatile("" ::: "memory");      // keep each visit's LDS reads inside it
     // a wave none of whose rows has this routed chunk adds exactly nothing (p = 0, no
     // rescale): it only takes part in the tile loads and leaves its SIMD to the other wave
     if (!DIAG && !DENSE) {
@@ -425,9 +421,53 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     }
   };
 
-  prefetch(visit[0]);
-  visit_chunk(0, std::true_type{});
-  for (int vi = 1; vi < nvis; ++vi) visit_chunk(vi, std::false_type{});
+  // rounds of two visits behind one barrier: visits 2r and 2r + 1 use LDS slots 2(r & 1) and
+  // 2(r & 1) + 1, which round r - 2 used; every wave finished that round before the barrier
+  // of round r - 1.  Visit 0 is the diagonal chunk.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  prefetch(visit[0], S0{});
+  if (1 < nvis) {
+    prefetch(visit[1], S1{});
+    fetch_weight(visit[1], S1{});
+  }
+  auto round = [&](int r, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;   // round 0: visit 0 is the diagonal
+    const int v0 = 2 * r, v1 = 2 * r + 1;
+    const bool has1 = v1 < nvis;
+    const int b0 = 2 * (r & 1), b1 = b0 + 1;
+    stash(b0, S0{});
+    if (has1) stash(b1, S1{});
+    float bias[2][QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      bias[0][qt] = (FIRST || DENSE) ? 0.f : (onnext[0][qt] ? fast_log2(wnext[0][qt]) : -INFINITY);
+      bias[1][qt] = DENSE ? 0.f : (onnext[1][qt] ? fast_log2(wnext[1][qt]) : -INFINITY);
+    }
+    __syncthreads();
+    if (v0 + 2 < nvis) {
+      prefetch(visit[v0 + 2], S0{});
+      fetch_weight(visit[v0 + 2], S0{});
+    }
+    if (v1 + 2 < nvis) {
+      prefetch(visit[v1 + 2], S1{});
+      fetch_weight(visit[v1 + 2], S1{});
+    }
+    if (FIRST) {
+      visit_chunk(b0, bias[0], std::true_type{});
+      if (has1) visit_chunk(b1, bias[1], std::false_type{});
+    } else {
+#pragma nounroll
+      for (int h = 0; h < (has1 ? 2 : 1); ++h) {
+        float bh[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) bh[qt] = h ? bias[1][qt] : bias[0][qt];
+        visit_chunk(b0 + h, bh, std::false_type{});
+      }
+    }
+  };
+  round(0, std::true_type{});
+  for (int r = 1; 2 * r < nvis; ++r) round(r, std::false_type{});
 
   // ---- normalise and write
 #pragma unroll
