@@ -11,14 +11,17 @@
 //   k_decode_route   one 16-wave workgroup per (b, kv head): wave g solves head g's entmax
 //                    threshold with wave-only reductions; then a fixed-order sum over the
 //                    heads, a ballot per 64 chunks for the mask word, w_bar at set bits and
-//                    the attend kernels' work list.
+//                    the attend kernel's work list.
 //   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
-//                    chunk form a list; each workgroup takes 16 consecutive items, each of
-//                    its 4 waves a quarter of them.  S^T = K Q^T with K rows loaded straight
-//                    from global as MFMA operands, V staged through wave-private LDS in
-//                    [d][key] order for the V^T P^T product; the waves' (max, sum, O)
-//                    partials are merged in LDS and written once per workgroup.
-//   k_decode_combine log-sum-exp merge of the segment partials, one workgroup per (b, head).
+//                    chunk form a list, cut into as many equal segments as keep every
+//                    workgroup slot of the GPU busy in one round; each of a workgroup's 4
+//                    waves takes every fourth item of its segment.  S^T = K Q^T with K rows
+//                    loaded straight from global as MFMA operands, V staged through
+//                    wave-private LDS in [d][key] order for the V^T P^T product; the waves'
+//                    (max, sum, O) partials are merged in LDS and written once per
+//                    workgroup.
+//   k_decode_combine log-sum-exp merge of the segment partials, one workgroup per (b, kv
+//                    head).
 // Decoding is HBM-bound: the active K/V chunks (32 KiB each at D = 128) dominate the bytes.
 #include <type_traits>
 
@@ -154,7 +157,11 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   if (wv < G && it > 0) {
     if (it <= 256) solve(std::integral_constant<int, 4>{});
     else if (it <= 512) solve(std::integral_constant<int, 8>{});
+    else if (it <= 768) solve(std::integral_constant<int, 12>{});
     else if (it <= 1024) solve(std::integral_constant<int, 16>{});
+    else if (it <= 1280) solve(std::integral_constant<int, 20>{});
+    else if (it <= 1536) solve(std::integral_constant<int, 24>{});
+    else if (it <= 1792) solve(std::integral_constant<int, 28>{});
     else solve(std::integral_constant<int, NR>{});
   }
   __syncthreads();
@@ -229,8 +236,9 @@ __device__ __forceinline__ bf16x8 vt_operand(const bf16* tile, int pitch, int k0
 
 template <int D>
 __global__ __launch_bounds__(kAttWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void k_decode_attend(AttendArgs a, float* __restrict__ pml,
-                                                                  float* __restrict__ po, int nseg_max) {
+void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ po, int nseg_max,
+                     int seg_target) {
+  constexpr int NT = kAttWaves * 64;
   constexpr int KS = D / 32, NDT = D / 16;
   constexpr int VP = D + 16;                      // V row pitch in LDS (bf16 elements)
   constexpr int SEGR = D / 8;                     // 16-byte segments per V row
@@ -244,25 +252,30 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
   const int seg = blockIdx.x, bk = blockIdx.y;
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int t = a.seq_lens[b] - 1;
-  if (t < 0 || t >= a.Tk) return;                 // the combine kernel writes NaN
+  if (t < 0 || t >= a.Tk) {                       // no valid query row: NaN outputs
+    if (seg == 0)
+      for (int i = tid; i < G * D; i += NT)
+        ((bf16*)a.out)[((size_t)b * a.Hq + kvh * G) * D + i] = (bf16)__builtin_nanf("");
+    return;
+  }
   const int it = t / kChunk;
 
-  // ---- this workgroup's items from the route kernel's list, with their routing bias
-  // (log2 w_bar; 0 for the diagonal chunk), staged in LDS once so that the loop below never
-  // waits on a global load other than its own tiles
-  __shared__ int citem[kSeg];
-  __shared__ float cbias[kSeg];
+  // ---- this workgroup's segment of the route kernel's list (active chunks + the diagonal
+  // chunk): seg_target segments of at least kSeg items each
   const int32_t* lst = a.list + (size_t)bk * a.list_ld;
-  const int ntot = lst[0];                        // active chunks + the diagonal chunk
-  const int lo = seg * kSeg;
-  const int nitems = min(kSeg, ntot - lo);
-  if (nitems <= 0) return;
-  if (tid < nitems) {
-    const int c = lst[1 + lo + tid];
-    citem[tid] = c;
-    cbias[tid] = c == it ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]);
-  }
-  __syncthreads();
+  const int ntot = lst[0];
+  const int per = max(kSeg, (ntot + seg_target - 1) / seg_target);
+  const int nsegb = (ntot + per - 1) / per;
+  if (seg >= nsegb) return;                       // (whole workgroup)
+  const int lo = seg * per;
+  const int nitems = min(per, ntot - lo);
+  // wave wv takes items lo + wv + kAttWaves j; lane j of myc holds the chunk of item j
+  const int nmy = max(0, (nitems - wv + kAttWaves - 1) / kAttWaves);
+  const int32_t* myl = lst + 1 + lo + wv;
+  const int myc = lane < nmy ? myl[kAttWaves * lane] : it;
+  auto chunk_of = [&](int j) {
+    return j < 64 ? __builtin_amdgcn_readlane(myc, j) : myl[kAttWaves * j];
+  };
 
   // ---- query columns: the G heads of this kv head (columns >= G are zero)
   bf16x8 qop[KS];
@@ -314,9 +327,12 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
           uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (i * 64 + lane) * 16, 0, 0));
   };
 
-  if (wv < nitems) load_item(citem[wv]);
-  for (int ii = wv; ii < nitems; ii += kAttWaves) {
-    const int c = citem[ii];
+  if (nmy > 0) load_item(chunk_of(0));
+  // routing bias of each item (log2 w_bar; 0 for the diagonal chunk), lane j for item j,
+  // loaded while the first tiles are in flight
+  const float mybias = (lane < nmy && myc != it) ? fast_log2(a.wbar[(size_t)bk * a.wbar_ld + myc]) : 0.f;
+  for (int j = 0; j < nmy; ++j) {
+    const int c = chunk_of(j);
     const bool diag = c == it;
     const int kmax = diag ? t : c * kChunk + 63;
     // V rows -> LDS (row-major, padded)
@@ -337,9 +353,10 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) s[kt] = mfma16(kop[kt][ks], qop[ks], s[kt]);
     }
-    const float bias = cbias[ii];
+    const float bias = j < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mybias), j))
+                              : (diag ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]));
     // next item's loads overlap the softmax and the PV product
-    if (ii + kAttWaves < nitems) load_item(citem[ii + kAttWaves]);
+    if (j + 1 < nmy) load_item(chunk_of(j + 1));
     // online softmax against the reference max m, which is only raised (with the rescale
     // of O and l) when a lane's partial probability sum exceeds kSumCap; keys past the
     // query are masked on the diagonal item only
@@ -347,14 +364,14 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[4 * kt + j] = s[kt][j];
+      for (int jj = 0; jj < 4; ++jj) x[4 * kt + jj] = s[kt][jj];
     if (diag) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
-          if (c * kChunk + key > kmax) x[4 * kt + j] = -INFINITY;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + jj;
+          if (c * kChunk + key > kmax) x[4 * kt + jj] = -INFINITY;
         }
     }
     float off = bias - m;
@@ -389,9 +406,9 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pop[p][j] = (bf16)pr[8 * p + j];
-        pop[p][4 + j] = (bf16)pr[8 * p + 4 + j];
+      for (int jj = 0; jj < 4; ++jj) {
+        pop[p][jj] = (bf16)pr[8 * p + jj];
+        pop[p][4 + jj] = (bf16)pr[8 * p + 4 + jj];
       }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -418,15 +435,16 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 16 * dt + 4 * lg + j;
-          const float v = o[dt][j] * f;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 16 * dt + 4 * lg + jj;
+          const float v = o[dt][jj] * f;
           ob[d * 16 + l16] = (w == 0) ? v : ob[d * 16 + l16] + v;
         }
     }
     __syncthreads();
   }
-  const size_t pidx = (size_t)bk * nseg_max + seg;
+  const size_t pbase = (size_t)bk * nseg_max;
+  const size_t pidx = pbase + seg;
   if (tid < 16) {
     float lt = 0.f;
 #pragma unroll
@@ -434,56 +452,86 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml,
     pml[pidx * 32 + tid] = mt;
     pml[pidx * 32 + 16 + tid] = lt;
   }
-  for (int i = tid; i < 16 * D; i += kAttWaves * 64) {
+  for (int i = tid; i < 16 * D; i += NT) {
     const int q = i / D, d = i % D;
     po[(pidx * 16 + q) * D + d] = ob[d * 16 + q];
   }
+
 }
 
 // ------------------------------------------------------------------------------ combine
-// one workgroup of D threads per (b, head); the segment maxima and sums are reduced in
-// parallel, then each thread merges its column of the partial outputs.
-template <typename TOut, int D>
-__global__ __launch_bounds__(D) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
-                                                      const float* __restrict__ po, int nseg_max) {
-  __shared__ float fs[256];
-  __shared__ float red[D / 64 > 0 ? D / 64 : 1];
-  const int bh = blockIdx.x, b = bh / a.Hq, h = bh % a.Hq;
-  const int G = a.Hq / a.Hkv, kvh = h / G, q = h % G;
-  const int bk = b * a.Hkv + kvh;
-  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
-  TOut* op = (TOut*)a.out + (size_t)bh * D;
+// Log-sum-exp merge of a (b, kv head)'s segment partials into the G heads' outputs: one
+// workgroup per (b, kv head), thread -> (query column, 8 consecutive d).
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
+                                                        const float* __restrict__ po, int nseg_max,
+                                                        int seg_target) {
+  constexpr int NT = 256, NSMAX = (kMaxRouted + 1 + kSeg) / kSeg + 1;
+  constexpr int kPre = 16;                        // segments whose partials are loaded at once
+  static_assert(2 * D <= NT, "one thread per (query column, 8 d)");
+  __shared__ float fsm[NSMAX * 16], fsl[NSMAX * 16], colm[16], coll[16];
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x;
+  const int bk = blockIdx.x, b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int t = a.seq_lens[b] - 1;
-  if (t < 0 || t >= a.Tk) {
-    op[d] = from_f32<TOut>(__builtin_nanf(""));
-    return;
+  if (t < 0 || t >= a.Tk) return;                 // the attend kernel wrote NaN
+  const size_t pbase = (size_t)bk * nseg_max;
+  // every load is issued before the segment count is known: the partials of up to kPre
+  // segments and the (max, sum) pairs of all seg_target, all inside the partial buffers;
+  // those of segments past the count are never used
+  const int q = tid / (D / 8), d0 = (tid % (D / 8)) * 8;
+  const bool act = tid < 2 * D && q < G;
+  const float* src = po + (pbase * 16 + (act ? q : 0)) * D + d0;
+  const int npre = min(seg_target, kPre);
+  float4 u[kPre][2];
+#pragma unroll
+  for (int s2 = 0; s2 < kPre; ++s2)
+    if (s2 < npre) {
+      u[s2][0] = *reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D);
+      u[s2][1] = *reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D + 4);
+    }
+  for (int i = tid; i < seg_target * 16; i += NT) {
+    const size_t pi = pbase + i / 16;
+    fsm[i] = pml[pi * 32 + (i & 15)];
+    fsl[i] = pml[pi * 32 + 16 + (i & 15)];
   }
-  const int nseg = (a.list[(size_t)bk * a.list_ld] + kSeg - 1) / kSeg;   // <= 129
-  // max over segments
-  float mloc = kNegBig;
-  for (int s = d; s < nseg; s += D) mloc = fmaxf(mloc, pml[((size_t)bk * nseg_max + s) * 32 + q]);
-  mloc = wave_max(mloc);
-  if (lane == 0) red[wv] = mloc;
+  const int ntot = a.list[(size_t)bk * a.list_ld];
+  const int per = max(kSeg, (ntot + seg_target - 1) / seg_target);
+  const int nsegb = (ntot + per - 1) / per;
   __syncthreads();
-  float mt = red[0];
-  for (int w = 1; w < D / 64; ++w) mt = fmaxf(mt, red[w]);
-  __syncthreads();
-  // per-segment factors and the total sum
-  float lloc = 0.f;
-  for (int s = d; s < nseg; s += D) {
-    const size_t pi = (size_t)bk * nseg_max + s;
-    const float f = fast_exp2(pml[pi * 32 + q] - mt);
-    fs[s] = f;
-    lloc += pml[pi * 32 + 16 + q] * f;
+  if (tid < 16) {
+    float mx = kNegBig;
+    for (int s2 = 0; s2 < nsegb; ++s2) mx = fmaxf(mx, fsm[s2 * 16 + tid]);
+    float l = 0.f;
+    for (int s2 = 0; s2 < nsegb; ++s2) l += fsl[s2 * 16 + tid] * fast_exp2(fsm[s2 * 16 + tid] - mx);
+    colm[tid] = mx;
+    coll[tid] = 1.0f / l;
   }
-  lloc = wave_sum(lloc);
-  if (lane == 0) red[wv] = lloc;
   __syncthreads();
-  float l = 0.f;
-  for (int w = 0; w < D / 64; ++w) l += red[w];
-  float acc = 0.f;
-  for (int s = 0; s < nseg; ++s) acc += po[(((size_t)bk * nseg_max + s) * 16 + q) * D + d] * fs[s];
-  op[d] = from_f32<TOut>(acc / l);
+  if (!act) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const float4& u0, const float4& u1, float fct) {
+    acc[0] = fmaf(u0.x, fct, acc[0]);
+    acc[1] = fmaf(u0.y, fct, acc[1]);
+    acc[2] = fmaf(u0.z, fct, acc[2]);
+    acc[3] = fmaf(u0.w, fct, acc[3]);
+    acc[4] = fmaf(u1.x, fct, acc[4]);
+    acc[5] = fmaf(u1.y, fct, acc[5]);
+    acc[6] = fmaf(u1.z, fct, acc[6]);
+    acc[7] = fmaf(u1.w, fct, acc[7]);
+  };
+  const float cm = colm[q], cl = coll[q];
+#pragma unroll
+  for (int s2 = 0; s2 < kPre; ++s2)
+    if (s2 < nsegb) add(u[s2][0], u[s2][1], fast_exp2(fsm[s2 * 16 + q] - cm) * cl);
+  for (int s2 = kPre; s2 < nsegb; ++s2)
+    add(*reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D),
+        *reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D + 4),
+        fast_exp2(fsm[s2 * 16 + q] - cm) * cl);
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)acc[e];
+  *reinterpret_cast<bf16x8*>((bf16*)a.out + ((size_t)b * a.Hq + kvh * G + q) * D + d0) = v;
 }
 
 // ------------------------------------------------------------------------------ launchers
@@ -508,16 +556,33 @@ hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroup slots of the device (two attend workgroups per CU), looked up once per device.
+static int attend_slots() {
+  static int slots[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (slots[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    slots[dev] = 2 * cus;
+  }
+  return slots[dev];
+}
+
 hipError_t launch_decode_attend(const AttendArgs& a, float* pml, float* po, hipStream_t s) {
   const int nseg = decode_nseg_max(a.nc);
-  dim3 grid(nseg, a.B * a.Hkv);
-  if (a.D == 128) k_decode_attend<128><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg);
-  else k_decode_attend<64><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg);
+  const int bh = a.B * a.Hkv;
+  // segments per (b, kv head): enough to occupy every slot once, never more than the
+  // partial buffers hold (each segment has at least kSeg items)
+  const int target = max(1, min(nseg, attend_slots() / bh));
+  dim3 grid(target, bh);
+  if (a.D == 128) k_decode_attend<128><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, target);
+  else k_decode_attend<64><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(a.B * a.Hq);
-  if (a.D == 128) k_decode_combine<bf16, 128><<<g2, 128, 0, s>>>(a, pml, po, nseg);
-  else k_decode_combine<bf16, 64><<<g2, 64, 0, s>>>(a, pml, po, nseg);
+  if (a.D == 128) k_decode_combine<128><<<bh, 256, 0, s>>>(a, pml, po, nseg, target);
+  else k_decode_combine<64><<<bh, 256, 0, s>>>(a, pml, po, nseg, target);
   return hipGetLastError();
 }
 

@@ -183,6 +183,47 @@ def test_decode_fp32_and_invalid_len(dash):
     assert np.isnan(o[0]).all() and np.isfinite(o[1]).all()
 
 
+def test_decode_bf16_segments_and_invalid_len(dash):
+    """bf16 decode whose work lists split into several attend segments per (b, kv head),
+    merged by log-sum-exp; two calls share one workspace that starts as garbage (nothing
+    may carry over from the previous call); an out-of-range length gives NaN for that
+    sequence only."""
+    w = Workload(name="dec_segs", kind="prefill", B=2, Hq=16, Hkv=2, T=6000, D=128,
+                 dtype="bf16", seed=35, needle_amp=0.5)
+    x = synth.prefill_inputs(w)
+    say("[parity] decode bf16 segments, shared workspace, invalid length")
+    B, Hkv, T, D = w.B, w.Hkv, w.T, w.D
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    nc = -(-T // 64)
+    summ = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(B, dtype=torch.int32, device="cuda")
+    dash.append_chunk(k, hc, torch.full((B,), T, dtype=torch.int32, device="cuda"), summ, nsum,
+                      Hq=w.Hq, enable_gqa=True)
+    p = dash.make_params(B, w.Hq, Hkv, T, D, alpha=w.alpha, enable_gqa=True,
+                         dtype=torch.bfloat16)
+    ws = dash.alloc_workspace(dash.workspace_size("decode", p), "cuda")
+    ws.fill_(0xA5)                                   # garbage before the first call
+    for lens in ([T, 4097], [5000, T + 1]):
+        rows = [min(l, T) - 1 for l in lens]
+        q = torch.stack([to_dev(x["q"][b, :, rows[b]], "bf16") for b in range(B)]).contiguous()
+        lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        out, ab = dash.decode(q, k, v, lens_t, summ, alpha=w.alpha, enable_gqa=True,
+                              workspace=ws, return_active_blocks=True)
+        torch.cuda.synchronize()
+        g = out.float().cpu().numpy()
+        bits = unpack_words(ab.cpu().numpy(), nc)
+        for b in range(B):
+            if lens[b] > T:
+                assert np.isnan(g[b]).all(), f"b={b}: out-of-range length must give NaN"
+                continue
+            ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                            alpha=w.alpha, rows=[rows[b]])
+            active = int(ref["mask"][0][:, 0].sum(axis=-1).min())   # per kv head
+            assert active + 1 > 16, f"b={b}: {active} active chunks give one segment only"
+            compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"decode segs b={b}")
+            compare_mask(bits[b][:, None], ref["mask"][0], ref["margin"][0], [rows[b]])
+
+
 def test_decode_steps_with_append(dash):
     """Decode 100 consecutive steps from a 600-token prompt (GQA 4), appending each chunk
     as it fills; every step equals the oracle's prefill row of the full sequence."""
