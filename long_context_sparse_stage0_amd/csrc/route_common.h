@@ -49,15 +49,24 @@ struct WaveReduce {
 // Returns the a solving n v g(a) = target by Newton steps from a = 0 (g is decreasing and
 // convex, g' = -2 (phi(a) - a Q(a))).  A target above 1 leans the estimate left of tau*;
 // the caller still checks that the point is a lower bound before relying on it.
+// Q comes from the rational erfc approximation 7.1.26 of Abramowitz and Stegun (absolute
+// error below 1.5e-7), which shares the factor exp(-a^2 / 2) with phi, so a step costs one
+// exp2 and two reciprocals.
 __device__ __forceinline__ float gauss_sq_tail_offset(float nv, float target) {
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    const float Q = 0.5f * erfcf(a * 0.70710678f);
-    const float ph = 0.39894228f * expf(-0.5f * a * a);
+    const float e = fast_exp2(-0.72134752f * a * a);              // exp(-a^2 / 2)
+    const float tt = __builtin_amdgcn_rcpf(fmaf(0.23164189f, fabsf(a), 1.f));  // p / sqrt 2
+    const float poly =
+        tt * fmaf(tt, fmaf(tt, fmaf(tt, fmaf(tt, 1.061405429f, -1.453152027f), 1.421413741f),
+                           -0.284496736f), 0.254829592f);
+    const float qh = 0.5f * poly * e;                             // Q(|a|)
+    const float Q = a >= 0.f ? qh : 1.f - qh;
+    const float ph = 0.39894228f * e;
     const float g = fmaf(a, a, 1.f) * Q - a * ph;
     const float h = ph - a * Q;
-    a += (nv * g - target) / (2.f * nv * h);
+    a += (nv * g - target) * __builtin_amdgcn_rcpf(2.f * nv * h);
   }
   return a;
 }
