@@ -67,6 +67,10 @@ typedef struct dash_params {
   int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
   int32_t estimate_diagonal; /* must be 0: the diagonal chunk is always kept at prior 1 */
+  float sigma;        /* prior strength, finite >= 0: keys of a routed chunk c get the logit
+                         bias sigma * log w_bar_c.  1 is the prior itself, 0 a uniform prior
+                         over the active chunks (gist.science, "Stufe 2": a hyperparameter
+                         sigma weighs the routing values against a uniform baseline) */
 } dash_params;
 
 /* Version of this ABI (major * 100 + minor). */

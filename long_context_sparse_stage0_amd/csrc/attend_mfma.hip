@@ -11,7 +11,7 @@
 // Work unit: one workgroup per (b, kv head, R consecutive rows inside one 64-row block),
 // i.e. R x G query vectors (256 for G >= 4), 32 per wave.  The workgroup visits the
 // diagonal chunk, then the union of its rows' mask words in increasing chunk order (a visit
-// list built in LDS); per routed visit, each row gets bias log2(w_bar) where its own bit is
+// list built in LDS); per routed visit, each row gets bias sigma log2(w_bar) where its own bit is
 // set and -inf where it is not, so the union walk computes exactly the per-row result.
 //
 // MFMA mapping (16x16x32, wave64; lane l, k-slot (l/16, i)):
@@ -443,8 +443,8 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
     float bias[2][QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      bias[0][qt] = (FIRST || DENSE) ? 0.f : (onnext[0][qt] ? fast_log2(wnext[0][qt]) : -INFINITY);
-      bias[1][qt] = DENSE ? 0.f : (onnext[1][qt] ? fast_log2(wnext[1][qt]) : -INFINITY);
+      bias[0][qt] = (FIRST || DENSE) ? 0.f : (onnext[0][qt] ? a.sigma * fast_log2(wnext[0][qt]) : -INFINITY);
+      bias[1][qt] = DENSE ? 0.f : (onnext[1][qt] ? a.sigma * fast_log2(wnext[1][qt]) : -INFINITY);
     }
     __syncthreads();
     if (v0 + 2 < nvis) {

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void k_attend_valu(AttendArgs a) {
     while (bits) {
       const int c = 64 * w + __builtin_ctzll(bits);
       bits &= bits - 1;
-      const float bias = a.dense ? 0.f : fast_log2(a.wbar[rowi * a.wbar_ld + c]);
+      const float bias = a.dense ? 0.f : a.sigma * fast_log2(a.wbar[rowi * a.wbar_ld + c]);
       visit(c, bias);
     }
   }

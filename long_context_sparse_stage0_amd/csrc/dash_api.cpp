@@ -35,7 +35,7 @@ constexpr int kMaxT = dash::kChunk * (dash::kMaxRouted + 1);
 
 struct Dims {
   int B, Hq, Hkv, T, D, G, nc, nfull, W;
-  float scale, alpha, gamma;
+  float scale, alpha, gamma, sigma;
   int dtype;
   size_t es;
 };
@@ -63,6 +63,8 @@ int check_params(const dash_params* p, Dims* d, bool need_bf16 = false) {
     return fail(DASH_ERR_INVALID_ARG, "alpha must be finite and > 1");
   if (!(p->gamma > 0.0f) || !std::isfinite(p->gamma))
     return fail(DASH_ERR_INVALID_ARG, "gamma must be finite and > 0");
+  if (!(p->sigma >= 0.0f) || !std::isfinite(p->sigma))
+    return fail(DASH_ERR_INVALID_ARG, "sigma (prior strength) must be finite and >= 0");
   if (!std::isfinite(p->sm_scale)) return fail(DASH_ERR_INVALID_ARG, "sm_scale is not finite");
   if (p->estimate_diagonal != 0)
     return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is not built");
@@ -82,6 +84,7 @@ int check_params(const dash_params* p, Dims* d, bool need_bf16 = false) {
   d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt((float)p->D);
   d->alpha = p->alpha;
   d->gamma = p->gamma;
+  d->sigma = p->sigma;
   d->dtype = p->dtype;
   d->es = p->dtype == DASH_BF16 ? 2 : 4;
   return DASH_OK;
@@ -176,7 +179,7 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
 
 extern "C" {
 
-int dash_abi_version(void) { return 100; }
+int dash_abi_version(void) { return 101; }
 
 const char* dash_last_error(void) { return g_err.c_str(); }
 
@@ -275,6 +278,7 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   aa.wbar_ld = d.nc;
   aa.nc = d.nc;
   aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.sigma = d.sigma;
   aa.dtype = d.dtype;
   aa.dense = 0;
   if (d.dtype == DASH_BF16) {
@@ -378,6 +382,7 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   aa.wbar_ld = d.nc;
   aa.nc = d.nc;
   aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.sigma = d.sigma;
   aa.dtype = d.dtype;
   aa.dense = 0;
   aa.list = reinterpret_cast<const int32_t*>(ws + L.list);
@@ -448,6 +453,7 @@ int dash_dense_causal(const dash_params* p, const void* q, const void* k, const 
   aa.wbar_ld = d.nc;
   aa.nc = d.nc;
   aa.scale_log2 = d.scale * 1.4426950408889634f;
+  aa.sigma = d.sigma;
   aa.dtype = d.dtype;
   aa.dense = 1;
   void* vt = workspace;

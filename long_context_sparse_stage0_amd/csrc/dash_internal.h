@@ -96,6 +96,7 @@ struct AttendArgs {
   const int32_t* seq_lens;
   int B, Hq, Hkv, D, Tq, Tk, rows, W, wbar_ld, nc;
   float scale_log2;       // sm_scale * log2(e)
+  float sigma;            // prior strength: a routed chunk's bias is sigma * log2 w_bar
   int dtype;
   int dense;              // 1: every chunk c < i_t active with prior 1 (comparator)
   const int32_t* list;    // decode: the route kernel's item lists (see RouteArgs)

@@ -328,9 +328,10 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   };
 
   if (nmy > 0) load_item(chunk_of(0));
-  // routing bias of each item (log2 w_bar; 0 for the diagonal chunk), lane j for item j,
+  // routing bias of each item (sigma log2 w_bar; 0 for the diagonal chunk), lane j for item j,
   // loaded while the first tiles are in flight
-  const float mybias = (lane < nmy && myc != it) ? fast_log2(a.wbar[(size_t)bk * a.wbar_ld + myc]) : 0.f;
+  const float mybias =
+      (lane < nmy && myc != it) ? a.sigma * fast_log2(a.wbar[(size_t)bk * a.wbar_ld + myc]) : 0.f;
   for (int j = 0; j < nmy; ++j) {
     const int c = chunk_of(j);
     const bool diag = c == it;
@@ -354,7 +355,7 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
       for (int ks = 0; ks < KS; ++ks) s[kt] = mfma16(kop[kt][ks], qop[ks], s[kt]);
     }
     const float bias = j < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mybias), j))
-                              : (diag ? 0.f : fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]));
+                              : (diag ? 0.f : a.sigma * fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]));
     // next item's loads overlap the softmax and the PV product
     if (j + 1 < nmy) load_item(chunk_of(j + 1));
     // online softmax against the reference max m, which is only raised (with the rescale

@@ -47,7 +47,7 @@ class DashParams(ctypes.Structure):
         ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("gamma", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("enable_gqa", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("estimate_diagonal", ctypes.c_int32),
+        ("estimate_diagonal", ctypes.c_int32), ("sigma", ctypes.c_float),
     ]
 
 
@@ -92,11 +92,12 @@ def _check(rc: int):
 
 
 def make_params(B, Hq, Hkv, T, D, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=None,
-                enable_gqa=False, dtype=torch.bfloat16, estimate_diagonal=False) -> DashParams:
+                enable_gqa=False, dtype=torch.bfloat16, estimate_diagonal=False,
+                sigma=1.0) -> DashParams:
     return DashParams(B=B, Hq=Hq, Hkv=Hkv, T=T, D=D, chunk_size=chunk_size, alpha=alpha,
                       gamma=gamma, sm_scale=0.0 if sm_scale is None else sm_scale,
                       enable_gqa=int(bool(enable_gqa)), dtype=DTYPES.get(dtype, 99),
-                      estimate_diagonal=int(bool(estimate_diagonal)))
+                      estimate_diagonal=int(bool(estimate_diagonal)), sigma=sigma)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -128,7 +129,7 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=None,
-            enable_gqa=False, estimate_diagonal=False, return_active_blocks=False,
+            sigma=1.0, enable_gqa=False, estimate_diagonal=False, return_active_blocks=False,
             return_block_weights=False, return_summaries=False, out=None, workspace=None,
             stream=None):
     """Causal prefill.  q [B,Hq,T,D]; k, v [B,Hkv,T,D]; head_cls [Hkv,D].
@@ -139,7 +140,7 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
     Hkv = k.shape[1]
     p = make_params(B, Hq, Hkv, T, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
                     sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype,
-                    estimate_diagonal=estimate_diagonal)
+                    estimate_diagonal=estimate_diagonal, sigma=sigma)
     nc = -(-T // 64)
     W = -(-nc // 64)
     dev = q.device
@@ -158,13 +159,14 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
 
 
 def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=1.0,
-                  sm_scale=None, enable_gqa=False, active_blocks=None, block_weights=None,
+                  sm_scale=None, sigma=1.0, enable_gqa=False, active_blocks=None,
+                  block_weights=None,
                   summaries=None, stream=None):
     """Run one prefill stage (0, 1 or 2) from the intermediates a full `prefill` call with
     the same tensors and workspace left behind (profiling aid)."""
     B, Hq, T, D = q.shape
     p = make_params(B, Hq, k.shape[1], T, D, alpha=alpha, gamma=gamma, sm_scale=sm_scale,
-                    enable_gqa=enable_gqa, dtype=q.dtype)
+                    enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
     _check(load().dash_prefill_stage(ctypes.byref(p), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(head_cls), _ptr(out), _ptr(active_blocks),
                                      _ptr(block_weights), _ptr(summaries), _ptr(workspace),
@@ -172,14 +174,14 @@ def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=
 
 
 def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha=1.5,
-           gamma=1.0, sm_scale=None, enable_gqa=False, return_active_blocks=False,
+           gamma=1.0, sm_scale=None, sigma=1.0, enable_gqa=False, return_active_blocks=False,
            out=None, workspace=None, stream=None):
     """One decode step.  q [B,Hq,D]; caches [B,Hkv,T_max,D]; seq_lens [B] int32 (device);
     summary_cache [B,Hkv,ceil(T_max/64),D] fp32."""
     B, Hq, D = q.shape
     Hkv, T_max = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
-                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype)
+                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     nc = -(-T_max // 64)

@@ -329,7 +329,8 @@ def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
 # ---------------------------------------------------------------------------------------
 
 def prefill_dense_formulation(q, k, v, head_cls, *, alpha: float, gamma: float = 1.0,
-                              scale: Optional[float] = None, chunk: int = CHUNK) -> np.ndarray:
+                              scale: Optional[float] = None, sigma: float = 1.0,
+                              chunk: int = CHUNK) -> np.ndarray:
     """Same result as `prefill(...)["out"]`, written as one masked softmax per head.
 
     Summaries by explicit loops, routing weights by the sorted-support entmax, and the
@@ -369,7 +370,7 @@ def prefill_dense_formulation(q, k, v, head_cls, *, alpha: float, gamma: float =
                     wbar = wsum / G
                     for c in range(it):
                         if wbar[c] > 0.0:
-                            bias[t, c * chunk:(c + 1) * chunk] = math.log(wbar[c])
+                            bias[t, c * chunk:(c + 1) * chunk] = sigma * math.log(wbar[c])
                 bias[t, it * chunk:t + 1] = 0.0
             for g in range(G):
                 h = kvh * G + g

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = _lib()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.dash_abi_version() == 100
+    assert lib.dash_abi_version() == 101
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
@@ -41,7 +41,7 @@ MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
 
 def _params(**kw):
     base = dict(B=1, Hq=4, Hkv=2, T=256, D=128, chunk_size=64, alpha=1.5, gamma=1.0,
-                sm_scale=0.0, enable_gqa=1, dtype=0, estimate_diagonal=0)
+                sm_scale=0.0, enable_gqa=1, dtype=0, estimate_diagonal=0, sigma=1.0)
     base.update(kw)
     return dash.DashParams(**base)
 
@@ -70,6 +70,9 @@ def _ws(p):
     (dict(B=0), -1),
     (dict(dtype=7), -3),
     (dict(estimate_diagonal=1), -4),
+    (dict(sigma=-0.5), -1),
+    (dict(sigma=float("nan")), -1),
+    (dict(sigma=float("inf")), -1),
     (dict(T=64 * 2049 + 1), -4),
 ])
 def test_param_validation(kw, code):

@@ -26,19 +26,19 @@ def dash():
     return d
 
 
-def run_prefill(dash, w: Workload, rows=None, alpha=None):
+def run_prefill(dash, w: Workload, rows=None, alpha=None, sigma=1.0):
     alpha = w.alpha if alpha is None else alpha
     x = synth.prefill_inputs(w)
     say(f"[parity] prefill {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} "
-        f"{w.dtype} alpha={alpha}")
+        f"{w.dtype} alpha={alpha} sigma={sigma}")
     q, k, v, hc = (to_dev(x[n], w.dtype) for n in ("q", "k", "v", "head_cls"))
-    out, ab, bw, sm = dash.prefill(q, k, v, hc, alpha=alpha, gamma=w.gamma,
+    out, ab, bw, sm = dash.prefill(q, k, v, hc, alpha=alpha, gamma=w.gamma, sigma=sigma,
                                    enable_gqa=w.enable_gqa, return_active_blocks=True,
                                    return_block_weights=True, return_summaries=True)
     torch.cuda.synchronize()
     rows = np.arange(w.T) if rows is None else np.asarray(rows)
     ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=alpha, gamma=w.gamma,
-                    rows=rows)
+                    sigma=sigma, rows=rows)
     nc = -(-w.T // 64)
     g_out = out.float().cpu().numpy()[:, :, rows]
     g_bits = unpack_words(ab.cpu().numpy(), nc)[:, :, rows]
@@ -75,6 +75,39 @@ def test_prefill_bf16_small(dash, G, alpha, T, D):
     w = Workload(name=f"small_g{G}", kind="prefill", B=2, Hq=2 * G, Hkv=2, T=T, D=D,
                  dtype="bf16", alpha=alpha, seed=900 + G, needle_amp=1.0)
     check_prefill(run_prefill(dash, w), w)
+
+
+@pytest.mark.parametrize("dtype,sigma", [("bf16", 0.0), ("bf16", 0.5), ("bf16", 2.0),
+                                         ("fp32", 0.0), ("fp32", 2.0)])
+def test_prefill_prior_strength(dash, dtype, sigma):
+    """Prior strength sigma != 1: routed keys get the bias sigma * log w_bar (0: a uniform
+    prior over the active chunks)."""
+    w = Workload(name=f"sigma_{dtype}", kind="prefill", B=1, Hq=8, Hkv=2, T=900, D=128,
+                 dtype=dtype, seed=950, needle_amp=1.0)
+    check_prefill(run_prefill(dash, w, sigma=sigma), w)
+
+
+def test_decode_prior_strength(dash):
+    """Decode with sigma = 2 equals the oracle's prefill row with the same sigma."""
+    w = Workload(name="dec_sigma", kind="prefill", B=2, Hq=16, Hkv=2, T=1500, D=128,
+                 dtype="bf16", seed=951, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say("[parity] decode sigma 2")
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    lens = [1500, 1000]
+    nc = -(-w.T // 64)
+    summ = torch.zeros((2, 2, nc, 128), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dash.append_chunk(k, hc, lens_t, summ, nsum, Hq=16, enable_gqa=True)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(2)]).contiguous()
+    out = dash.decode(q, k, v, lens_t, summ, sigma=2.0, enable_gqa=True)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    for b in range(2):
+        ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                        sigma=2.0, rows=[lens[b] - 1])
+        compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"decode sigma b={b}")
 
 
 def test_prefill_fp32_gqa_and_scale(dash):

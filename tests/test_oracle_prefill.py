@@ -42,6 +42,18 @@ def test_block_walk_equals_dense_formulation(alpha, G):
     assert 0.0 <= frac < 1.0
 
 
+@pytest.mark.parametrize("sigma", [0.0, 2.0])
+def test_block_walk_equals_dense_formulation_prior_strength(sigma):
+    T, D = 300, 8
+    q, k, v, hc = _rand(1, 8, 2, T, D, seed=77, needle=2.0)
+    walk = O.prefill(q, k, v, hc, alpha=1.5, sigma=sigma)
+    dense = O.prefill_dense_formulation(q, k, v, hc, alpha=1.5, sigma=sigma)
+    np.testing.assert_allclose(walk["out"], dense, rtol=0, atol=1e-12)
+    # and sigma matters whenever a routed weight lies strictly between 0 and 1
+    ref = O.prefill(q, k, v, hc, alpha=1.5)
+    assert np.abs(walk["out"] - ref["out"]).max() > 1e-6
+
+
 def test_row_subset_equals_full():
     q, k, v, hc = _rand(2, 4, 2, 200, 8, seed=3, needle=1.0)
     full = O.prefill(q, k, v, hc)

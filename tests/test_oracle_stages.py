@@ -157,3 +157,41 @@ def test_prior_bias_equals_weighted_key_multiplicity():
     wt = wt * e[: t + 1]
     ref = (wt[:, None] * v[: t + 1]).sum(0) / wt.sum()
     np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_prior_strength_zero_uses_the_support_only():
+    """sigma = 0: the prior is uniform over the active chunks, so the row is plain softmax
+    attention over the keys of the chunks with w_bar > 0 plus the causal diagonal keys, and
+    rescaling the positive weights changes nothing."""
+    rng = np.random.default_rng(21)
+    T, D = 300, 8
+    q, k, v = (rng.normal(size=(T, D)) for _ in range(3))
+    t = 290
+    w = np.array([0.6, 0.0, 0.1, 0.3])
+    o = O.attend_row(q[t], k, v, t, w, scale=0.4, sigma=0.0)
+    keys = [j for j in range(t + 1) if j >= 256 or w[j // 64] > 0]
+    s = 0.4 * k[keys] @ q[t]
+    p = np.exp(s - s.max())
+    np.testing.assert_allclose(o, (p / p.sum()) @ v[keys], atol=1e-13)
+    w2 = np.where(w > 0, rng.uniform(0.01, 5.0, size=w.shape), 0.0)
+    np.testing.assert_allclose(O.attend_row(q[t], k, v, t, w2, scale=0.4, sigma=0.0), o,
+                               atol=1e-13)
+
+
+@pytest.mark.parametrize("sigma", [0.5, 2.0])
+def test_prior_strength_is_a_power_of_the_multiplicity(sigma):
+    """A block of weight w with prior strength sigma behaves like its keys replicated with
+    multiplicity w ** sigma."""
+    rng = np.random.default_rng(13)
+    D = 4
+    k = rng.normal(size=(130, D))
+    v = rng.normal(size=(130, D))
+    q = rng.normal(size=D)
+    t = 129
+    w = np.array([0.2, 0.8])
+    o = O.attend_row(q, k, v, t, w, scale=1.0, sigma=sigma)
+    e = np.exp(k @ q)
+    wt = np.concatenate([np.full(64, 0.2 ** sigma), np.full(64, 0.8 ** sigma), np.ones(t + 1 - 128)])
+    wt = wt * e[: t + 1]
+    ref = (wt[:, None] * v[: t + 1]).sum(0) / wt.sum()
+    np.testing.assert_allclose(o, ref, atol=1e-13)
