@@ -229,13 +229,53 @@ def bench_decode(args, w, dash, torch):
     frac_active = act / (B * Hkv * sum((w.T + s) // 64 for s in range(S)))
     log(f"decode {us:.1f} us/step ({(t1 - t0) * 1e6 / S:.1f} wall), {gbs:.0f} GB/s, "
         f"active fraction {frac_active:.3f}")
-    del kc, vc, qs, summ, ws
+    o_last = out.clone()
+
+    # the same steps over paged caches: every chunk of every sequence in a shuffled page of
+    # one pool [pages, Hkv, 64, D], appends through the block table
+    nc_ = -(-TT // 64)
+    perm = torch.randperm(B * nc_, generator=torch.Generator().manual_seed(20267000)).to(dev)
+
+    def to_pages(cache):
+        pad = torch.zeros((B, Hkv, nc_ * 64, D), dtype=cache.dtype, device=dev)
+        pad[:, :, :TT] = cache
+        pool = torch.empty((B * nc_, Hkv, 64, D), dtype=cache.dtype, device=dev)
+        pool[perm] = pad.view(B, Hkv, nc_, 64, D).permute(0, 2, 1, 3, 4).reshape(B * nc_, Hkv, 64, D)
+        return pool
+    kp, vp = to_pages(kc), to_pages(vc)
+    del kc, vc
     torch.cuda.empty_cache()
+    table = perm.view(B, nc_).to(torch.int32).contiguous()
+    summ.zero_()
+    nsum.zero_()
+    dash.append_chunk_paged(kp, table, hc, init_len, summ, nsum, Hq=Hq, enable_gqa=True)
+
+    def run_paged(n):
+        for s in range(n):
+            L = w.T + 1 + s
+            dash.decode_paged(qs[s], kp, vp, table, lens_all[s], summ, alpha=w.alpha,
+                              enable_gqa=True, out=out, workspace=ws)
+            if L % 64 == 0:
+                dash.append_chunk_paged(kp, table, hc, lens_all[s], summ, nsum, Hq=Hq,
+                                        enable_gqa=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_paged(S)
+    e1.record()
+    torch.cuda.synchronize()
+    us_p = e0.elapsed_time(e1) * 1e3 / S
+    same = bool(torch.equal(out, o_last))
+    log(f"decode (paged caches) {us_p:.1f} us/step; last step identical to contiguous: {same}")
+    del kp, vp, qs, summ, ws
+    torch.cuda.empty_cache()
+    gbs_p = bytes_total / S / (us_p * 1e-6) / 1e9
     return {"workload": w.name, "us_per_step": us, "tokens_per_s": B / (us * 1e-6),
             "steps": S, "algorithmic_bytes_per_step": bytes_total / S,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS},
-            "active_fraction": frac_active}
+            "active_fraction": frac_active,
+            "paged": {"us_per_step": us_p, "achieved_gbs": gbs_p, "frac": gbs_p / PEAK_HBM_GBS,
+                      "pages": B * nc_, "identical_to_contiguous": same}}
 
 
 def cpu_baseline(args, w, x):

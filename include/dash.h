@@ -147,6 +147,31 @@ int dash_append_chunk(const dash_params* p, const void* k_cache, const void* hea
                       int32_t* n_summarized, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Paged caches: dash_decode and dash_append_chunk over a shared pool of pages, for
+ * continuous batching (the pages' incremental decoding with a chunk-representation cache,
+ * gist.science "Hauptbeiträge" and "Stufe 0"; the paging is this library's layout).  A
+ * page holds one chunk of every KV head; p->T is the logical capacity T_max per sequence.
+ *   k_pages, v_pages [num_pages, Hkv, C, D] bf16 (caller-owned; dtype must be DASH_BF16)
+ *   block_table      [B, ceil(T_max/C)] int32 (device): page of chunk c of sequence b;
+ *                    entries for chunks past a sequence's length are never read
+ * Everything else, the workspace and the results are as for dash_decode /
+ * dash_append_chunk; the summary cache stays per sequence.  A page id outside
+ * [0, num_pages) is never dereferenced: decode reads its keys and values as zeros and
+ * append leaves that chunk's summary untouched (the output is then meaningless).
+ * Errors: DASH_ERR_INVALID_ARG for a NULL block_table or num_pages <= 0,
+ * DASH_ERR_UNSUPPORTED for fp32.
+ * ------------------------------------------------------------------------------- */
+int dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
+                      const void* v_pages, int32_t num_pages, const int32_t* block_table,
+                      const int32_t* seq_lens, const float* summary_cache, void* out,
+                      uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int dash_append_chunk_paged(const dash_params* p, const void* k_pages, int32_t num_pages,
+                            const int32_t* block_table, const void* head_cls,
+                            const int32_t* seq_lens, float* summary_cache,
+                            int32_t* n_summarized, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Dense causal softmax attention with the same layout (the comparator the pages time
  * against: FlashAttention-3 in their Table 5).  Uses p->B, Hq, Hkv, T, D, sm_scale,
  * enable_gqa, dtype (bf16 only).

@@ -316,12 +316,20 @@ int dash_decode_workspace_size(const dash_params* p, size_t* bytes) {
   return ok();
 }
 
-int dash_decode(const dash_params* p, const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* seq_lens, const float* summary_cache, void* out,
-                uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
-                void* stream) {
+namespace {
+
+// block_table == nullptr: contiguous [B, Hkv, T_max, D] caches; otherwise page pools
+// [num_pages, Hkv, C, D] (bf16 only) with chunk c of sequence b in page block_table[b][c].
+int decode_impl(const dash_params* p, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, int32_t num_pages, const int32_t* seq_lens,
+                const float* summary_cache, void* out, uint64_t* active_blocks, void* workspace,
+                size_t workspace_bytes, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
+  if (block_table) {
+    if (d.dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "paged caches are bf16 only");
+    if (num_pages <= 0) return fail(DASH_ERR_INVALID_ARG, "num_pages must be positive");
+  }
   if (int rc = check_ptr(q, "q")) return rc;
   if (int rc = check_ptr(k_cache, "k_cache")) return rc;
   if (int rc = check_ptr(v_cache, "v_cache")) return rc;
@@ -387,6 +395,9 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   aa.dense = 0;
   aa.list = reinterpret_cast<const int32_t*>(ws + L.list);
   aa.list_ld = d.nc + 2;
+  aa.block_table = block_table;
+  aa.bt_ld = d.nc;
+  aa.num_pages = num_pages;
   if (d.dtype == DASH_BF16)
     e = dash::launch_decode_attend(aa, reinterpret_cast<float*>(ws + L.pml),
                                    reinterpret_cast<float*>(ws + L.po), s);
@@ -396,9 +407,9 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache, const 
   return ok();
 }
 
-int dash_append_chunk(const dash_params* p, const void* k_cache, const void* head_cls,
-                      const int32_t* seq_lens, float* summary_cache, int32_t* n_summarized,
-                      void* stream) {
+int append_impl(const dash_params* p, const void* k_cache, const int32_t* block_table,
+                int32_t num_pages, const void* head_cls, const int32_t* seq_lens,
+                float* summary_cache, int32_t* n_summarized, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
   if (int rc = check_ptr(k_cache, "k_cache")) return rc;
@@ -406,14 +417,55 @@ int dash_append_chunk(const dash_params* p, const void* k_cache, const void* hea
   if (!seq_lens) return fail(DASH_ERR_INVALID_ARG, "seq_lens is NULL");
   if (int rc = check_ptr(summary_cache, "summary_cache")) return rc;
   if (!n_summarized) return fail(DASH_ERR_INVALID_ARG, "n_summarized is NULL");
+  if (block_table) {
+    if (d.dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "paged caches are bf16 only");
+    if (num_pages <= 0) return fail(DASH_ERR_INVALID_ARG, "num_pages must be positive");
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if ((e = dash::launch_stage0(k_cache, head_cls, summary_cache, nullptr, d.B, d.Hkv, d.T, d.D, d.nc,
-                               d.nfull, n_summarized, seq_lens, d.scale, d.dtype, s)) != hipSuccess)
+                               d.nfull, n_summarized, seq_lens, d.scale, d.dtype, s, block_table,
+                               d.nc, num_pages)) != hipSuccess)
     return hip_fail(e, "append launch");
   if ((e = dash::launch_update_nsum(n_summarized, seq_lens, d.B, s)) != hipSuccess)
     return hip_fail(e, "append bookkeeping launch");
   return ok();
+}
+
+}  // namespace
+
+int dash_decode(const dash_params* p, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seq_lens, const float* summary_cache, void* out,
+                uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, nullptr, 0, seq_lens, summary_cache, out,
+                     active_blocks, workspace, workspace_bytes, stream);
+}
+
+int dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
+                      const void* v_pages, int32_t num_pages, const int32_t* block_table,
+                      const int32_t* seq_lens, const float* summary_cache, void* out,
+                      uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!block_table) return fail(DASH_ERR_INVALID_ARG, "block_table is NULL");
+  return decode_impl(p, q, k_pages, v_pages, block_table, num_pages, seq_lens, summary_cache,
+                     out, active_blocks, workspace, workspace_bytes, stream);
+}
+
+int dash_append_chunk(const dash_params* p, const void* k_cache, const void* head_cls,
+                      const int32_t* seq_lens, float* summary_cache, int32_t* n_summarized,
+                      void* stream) {
+  return append_impl(p, k_cache, nullptr, 0, head_cls, seq_lens, summary_cache, n_summarized,
+                     stream);
+}
+
+int dash_append_chunk_paged(const dash_params* p, const void* k_pages, int32_t num_pages,
+                            const int32_t* block_table, const void* head_cls,
+                            const int32_t* seq_lens, float* summary_cache,
+                            int32_t* n_summarized, void* stream) {
+  if (!block_table) return fail(DASH_ERR_INVALID_ARG, "block_table is NULL");
+  return append_impl(p, k_pages, block_table, num_pages, head_cls, seq_lens, summary_cache,
+                     n_summarized, stream);
 }
 
 int dash_dense_causal_workspace_size(const dash_params* p, size_t* bytes) {

@@ -99,6 +99,9 @@ struct AttendArgs {
   float sigma;            // prior strength: a routed chunk's bias is sigma * log2 w_bar
   int dtype;
   int dense;              // 1: every chunk c < i_t active with prior 1 (comparator)
+  const int32_t* block_table;  // decode, paged caches: [B][bt_ld] page of each chunk, or
+  int bt_ld;                   // nullptr for contiguous [B, Hkv, Tk, D] caches; pages are
+  int num_pages;               // [num_pages][Hkv][64][D] (ids outside [0, num_pages) read as 0)
   const int32_t* list;    // decode: the route kernel's item lists (see RouteArgs)
   int list_ld;
 };
@@ -107,10 +110,13 @@ struct AttendArgs {
 // (hi = bf16(x), lo = bf16(x - hi)) for the MFMA router, tiled for its operand loads: per
 // (b, kv head) split_tiles(nc_alloc) tiles of 16 chunks, each [plane][D/32][16 chunks][32]
 // (see split_offset), so one wave-wide 16-byte load reads 1 KiB of contiguous memory.
+// block_table (nullable): paged K, [num_pages][Hkv][64][D], chunk c of sequence b in page
+// block_table[b * bt_ld + c] (chunks whose page id is out of range are skipped).
 hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
                          int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,
-                         int dtype, hipStream_t s);
+                         int dtype, hipStream_t s, const int32_t* block_table = nullptr,
+                         int bt_ld = 0, int num_pages = 0);
 hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
                               hipStream_t s);
 hipError_t launch_vtranspose(const void* v, void* vt, int B, int Hkv, int T, int D, int nc,

@@ -276,6 +276,12 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   auto chunk_of = [&](int j) {
     return j < 64 ? __builtin_amdgcn_readlane(myc, j) : myl[kAttWaves * j];
   };
+  // paged caches: the page of each of those chunks (-1 past the list)
+  const int32_t* btab = a.block_table ? a.block_table + (size_t)b * a.bt_ld : nullptr;
+  const int mypg = btab ? (lane < nmy ? btab[myc] : -1) : 0;
+  auto page_of = [&](int j, int c) {
+    return j < 64 ? __builtin_amdgcn_readlane(mypg, j) : btab[c];
+  };
 
   // ---- query columns: the G heads of this kv head (columns >= G are zero)
   bf16x8 qop[KS];
@@ -308,13 +314,25 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
     koff[kt] = (key * D + 8 * lg) * 2;
   }
-  auto load_item = [&](int c_any) {
-    const int c = __builtin_amdgcn_readfirstlane(c_any);
-    const int nkeys = min(kChunk, t - c * kChunk + 1);          // 64 except on the diagonal
+  // a chunk's K and V rows: contiguous caches index by chunk, paged ones by page; a page id
+  // outside the pool gives an empty range, so its keys and values read as zeros
+  auto load_item = [&](int j) {
+    const int c = __builtin_amdgcn_readfirstlane(chunk_of(j));
+    int nkeys = min(kChunk, t - c * kChunk + 1);                // 64 except on the diagonal
+    const bf16* kp = kb + (size_t)c * kChunk * D;
+    const bf16* vp = vb + (size_t)c * kChunk * D;
+    if (btab) {
+      const int pg = __builtin_amdgcn_readfirstlane(page_of(j, c));
+      const bool okp = pg >= 0 && pg < a.num_pages;
+      const size_t off = ((size_t)(okp ? pg : 0) * a.Hkv + kvh) * kChunk * D;
+      kp = (const bf16*)a.k + off;
+      vp = (const bf16*)a.v + off;
+      if (!okp) nkeys = 0;
+    }
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kb + (size_t)c * kChunk * D), (short)0, nkeys * D * 2, kBufferRsrcWord3);
+        (void*)kp, (short)0, nkeys * D * 2, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vb + (size_t)c * kChunk * D), (short)0, nkeys * D * 2, kBufferRsrcWord3);
+        (void*)vp, (short)0, nkeys * D * 2, kBufferRsrcWord3);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -327,7 +345,7 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
           uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (i * 64 + lane) * 16, 0, 0));
   };
 
-  if (nmy > 0) load_item(chunk_of(0));
+  if (nmy > 0) load_item(0);
   // routing bias of each item (sigma log2 w_bar; 0 for the diagonal chunk), lane j for item j,
   // loaded while the first tiles are in flight
   const float mybias =
@@ -357,7 +375,7 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     const float bias = j < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mybias), j))
                               : (diag ? 0.f : a.sigma * fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]));
     // next item's loads overlap the softmax and the PV product
-    if (j + 1 < nmy) load_item(chunk_of(j + 1));
+    if (j + 1 < nmy) load_item(j + 1);
     // online softmax against the reference max m, which is only raised (with the rescale
     // of O and l) when a lane's partial probability sum exceeds kSumCap; keys past the
     // query are masked on the diagonal item only

@@ -24,7 +24,9 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
                                                int T_stride, int nc_alloc, int n_full,
                                                const int32_t* __restrict__ lo_b,
                                                const int32_t* __restrict__ seq_lens,
-                                               float scale_log2) {
+                                               float scale_log2,
+                                               const int32_t* __restrict__ block_table,
+                                               int bt_ld, int num_pages) {
   constexpr int E = D / 64;
   __shared__ float red[64][65];
   __shared__ float pis[64];
@@ -43,7 +45,14 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
   for (int e = 0; e < E; ++e) h[e] = to_f32(head_cls[kvh * D + lane * E + e]) * scale_log2;
 
   for (int c = lo + blockIdx.x; c < hi; c += gridDim.x) {
-    const TIn* kc = k + ((size_t)(b * Hkv + kvh) * T_stride + (size_t)c * kChunk) * D;
+    const TIn* kc;
+    if (block_table) {                       // paged: chunk c of sequence b lives in a page
+      const int pg = block_table[(size_t)b * bt_ld + c];
+      if (pg < 0 || pg >= num_pages) continue;   // (uniform over the wave)
+      kc = k + ((size_t)pg * Hkv + kvh) * kChunk * D;
+    } else {
+      kc = k + ((size_t)(b * Hkv + kvh) * T_stride + (size_t)c * kChunk) * D;
+    }
     float kr[64][E];
 #pragma unroll
     for (int j = 0; j < 64; ++j) {
@@ -130,7 +139,8 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t* __restrict__
 hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
                          int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,
-                         int dtype, hipStream_t s) {
+                         int dtype, hipStream_t s, const int32_t* block_table, int bt_ld,
+                         int num_pages) {
   bf16* ss = (bf16*)summ_split;
   const float sl2 = scale * 1.4426950408889634f;
   int gx = seq_lens ? 64 : n_full;
@@ -139,19 +149,21 @@ hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void*
   if (dtype == 0) {
     if (D == 128)
       k_stage0<bf16, 128><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, ss, Hkv,
-                                              T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
+                                              T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2,
+                                              block_table, bt_ld, num_pages);
     else
       k_stage0<bf16, 64><<<grid, 64, 0, s>>>((const bf16*)k, (const bf16*)head_cls, summ, ss, Hkv,
-                                             T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2);
+                                             T_stride, nc_alloc, n_full, lo_b, seq_lens, sl2,
+                                             block_table, bt_ld, num_pages);
   } else {
     if (D == 128)
       k_stage0<float, 128><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
                                                nullptr, Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
-                                               sl2);
+                                               sl2, nullptr, 0, 0);
     else
       k_stage0<float, 64><<<grid, 64, 0, s>>>((const float*)k, (const float*)head_cls, summ,
                                               nullptr, Hkv, T_stride, nc_alloc, n_full, lo_b, seq_lens,
-                                              sl2);
+                                              sl2, nullptr, 0, 0);
   }
   return hipGetLastError();
 }

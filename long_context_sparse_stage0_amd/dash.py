@@ -30,7 +30,7 @@ EXPORTS = [
     "dash_abi_version", "dash_last_error",
     "dash_prefill_workspace_size", "dash_prefill", "dash_prefill_stage",
     "dash_decode_workspace_size", "dash_decode",
-    "dash_append_chunk",
+    "dash_append_chunk", "dash_decode_paged", "dash_append_chunk_paged",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
 ]
 
@@ -80,6 +80,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_decode.restype = ctypes.c_int
     lib.dash_append_chunk.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.dash_append_chunk.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.dash_decode_paged.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_decode_paged.restype = ctypes.c_int
+    lib.dash_append_chunk_paged.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.dash_append_chunk_paged.restype = ctypes.c_int
     lib.dash_dense_causal.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_dense_causal.restype = ctypes.c_int
     _lib = lib
@@ -206,6 +211,56 @@ def append_chunk(k_cache, head_cls, seq_lens, summary_cache, n_summarized, *, ch
     _check(load().dash_append_chunk(ctypes.byref(p), _ptr(k_cache), _ptr(head_cls),
                                     _ptr(seq_lens), _ptr(summary_cache), _ptr(n_summarized),
                                     _stream(stream)))
+
+
+def _paged_params(q_or_none, k_pages, block_table, Hq, chunk_size, alpha, gamma, sm_scale,
+                  sigma, enable_gqa):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be an int32 [B, ceil(T_max/64)] tensor")
+    num_pages, Hkv, C, D = k_pages.shape
+    if C != chunk_size:
+        raise ValueError(f"pages must hold {chunk_size} tokens (got {C})")
+    B = block_table.shape[0]
+    T_max = block_table.shape[1] * chunk_size
+    p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
+                    sm_scale=sm_scale, sigma=sigma, enable_gqa=enable_gqa, dtype=k_pages.dtype)
+    return p, num_pages
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, summary_cache, *, chunk_size=64,
+                 alpha=1.5, gamma=1.0, sm_scale=None, sigma=1.0, enable_gqa=False,
+                 return_active_blocks=False, out=None, workspace=None, stream=None):
+    """One decode step over paged caches.  q [B,Hq,D]; k_pages, v_pages [num_pages,Hkv,64,D];
+    block_table [B, ceil(T_max/64)] int32 (device); the rest as for `decode`."""
+    B, Hq, D = q.shape
+    p, num_pages = _paged_params(q, k_pages, block_table, Hq, chunk_size, alpha, gamma, sm_scale,
+                                 sigma, enable_gqa)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    W = -(-block_table.shape[1] // 64)
+    if out is None:
+        out = torch.empty_like(q)
+    ab = torch.empty((B, k_pages.shape[1], W), dtype=torch.int64, device=q.device) \
+        if return_active_blocks else None
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size("decode", p), q.device)
+    _check(load().dash_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                    num_pages, _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(summary_cache), _ptr(out), _ptr(ab), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+    return (out, ab) if return_active_blocks else out
+
+
+def append_chunk_paged(k_pages, block_table, head_cls, seq_lens, summary_cache, n_summarized, *,
+                       chunk_size=64, sm_scale=None, enable_gqa=True, Hq=None, stream=None):
+    """`append_chunk` over a paged K pool [num_pages, Hkv, 64, D] and its block table."""
+    p, num_pages = _paged_params(None, k_pages, block_table,
+                                 Hq if Hq is not None else k_pages.shape[1], chunk_size, 1.5,
+                                 1.0, sm_scale, 1.0, enable_gqa)
+    _check(load().dash_append_chunk_paged(ctypes.byref(p), _ptr(k_pages), num_pages,
+                                          _ptr(block_table), _ptr(head_cls), _ptr(seq_lens),
+                                          _ptr(summary_cache), _ptr(n_summarized),
+                                          _stream(stream)))
 
 
 def dense_causal(q, k, v, *, sm_scale=None, enable_gqa=False, out=None, workspace=None,

@@ -133,6 +133,17 @@ def test_decode_append_dense_validation():
     assert lib.dash_append_chunk(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None) == -1
     assert lib.dash_append_chunk(ctypes.byref(_params(alpha=1.0)), FAKE, FAKE, FAKE, FAKE,
                                  FAKE, None) == -1
+    # paged caches: a block table is required, the pool must be non-empty, bf16 only
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, FAKE,
+                                 None, FAKE, n.value, None) == -1
+    assert lib.dash_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, n.value, None) == -1
+    assert lib.dash_decode_paged(ctypes.byref(_params(dtype=1)), FAKE, FAKE, FAKE, 4, FAKE,
+                                 FAKE, FAKE, FAKE, None, FAKE, n.value, None) == -4
+    assert lib.dash_append_chunk_paged(ctypes.byref(p), FAKE, 4, None, FAKE, FAKE, FAKE, FAKE,
+                                       None) == -1
+    assert lib.dash_append_chunk_paged(ctypes.byref(p), FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == -1
     # the dense comparator is bf16 only
     pf = _params(dtype=1)
     assert lib.dash_dense_causal_workspace_size(ctypes.byref(pf), ctypes.byref(n)) == -3

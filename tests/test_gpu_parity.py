@@ -257,6 +257,65 @@ def test_decode_bf16_segments_and_invalid_len(dash):
             compare_mask(bits[b][:, None], ref["mask"][0], ref["margin"][0], [rows[b]])
 
 
+def _page_pool(cache, perm, num_pages, lens, gen):
+    """Scatter a contiguous cache [B, Hkv, T, D] into a page pool [num_pages, Hkv, 64, D]:
+    chunk c of sequence b goes to page perm[b * nc + c]; spare pages hold noise."""
+    B, Hkv, T, D = cache.shape
+    nc = -(-T // 64)
+    padded = torch.zeros((B, Hkv, nc * 64, D), dtype=cache.dtype, device=cache.device)
+    padded[:, :, :T] = cache
+    chunks = padded.view(B, Hkv, nc, 64, D).permute(0, 2, 1, 3, 4).reshape(B * nc, Hkv, 64, D)
+    pool = torch.randn((num_pages, Hkv, 64, D), generator=gen, device="cpu").to(cache.dtype)
+    pool = pool.to(cache.device)
+    pool[torch.as_tensor(perm, device=cache.device)] = chunks
+    table = torch.as_tensor(np.asarray(perm, np.int32).reshape(B, nc)).clone()
+    for b, L in enumerate(lens):                       # entries past a length are never read
+        table[b, -(-L // 64):] = -1
+    return pool, table.to(cache.device)
+
+
+def test_decode_paged_matches_contiguous(dash):
+    """Paged caches (shuffled pages, noise in the spare ones): the summary append and the
+    decode step give bit-identical results to the contiguous caches, and equal the
+    oracle's prefill rows."""
+    w = Workload(name="dec_paged", kind="prefill", B=3, Hq=16, Hkv=2, T=1500, D=128,
+                 dtype="bf16", seed=960, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say("[parity] paged decode vs contiguous")
+    B, Hkv, T, D = w.B, w.Hkv, w.T, w.D
+    lens = [1500, 900, 130]
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    nc = -(-T // 64)
+    rng = np.random.default_rng(961)
+    num_pages = B * nc + 7
+    perm = rng.permutation(num_pages)[:B * nc]
+    gen = torch.Generator().manual_seed(962)
+    kp, table = _page_pool(k, perm, num_pages, lens, gen)
+    vp, _ = _page_pool(v, perm, num_pages, lens, gen)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    s_c = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device="cuda")
+    s_p = torch.zeros_like(s_c)
+    n_c = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n_p = torch.zeros_like(n_c)
+    dash.append_chunk(k, hc, lens_t, s_c, n_c, Hq=w.Hq, enable_gqa=True)
+    dash.append_chunk_paged(kp, table, hc, lens_t, s_p, n_p, Hq=w.Hq, enable_gqa=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s_c, s_p) and torch.equal(n_c, n_p)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(B)]).contiguous()
+    o_c, ab_c = dash.decode(q, k, v, lens_t, s_c, enable_gqa=True, return_active_blocks=True)
+    o_p, ab_p = dash.decode_paged(q, kp, vp, table, lens_t, s_p, enable_gqa=True,
+                                  return_active_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_p)
+    W = ab_c.shape[-1]
+    assert torch.equal(ab_c, ab_p[..., :W])
+    g = o_p.float().cpu().numpy()
+    for b in range(B):
+        ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                        rows=[lens[b] - 1])
+        compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"paged decode b={b}")
+
+
 def test_decode_steps_with_append(dash):
     """Decode 100 consecutive steps from a 600-token prompt (GQA 4), appending each chunk
     as it fills; every step equals the oracle's prefill row of the full sequence."""
