@@ -34,6 +34,8 @@ Readings taken where the pages are silent (each is one named argument or branch 
     sigma multiplies log g (sigma = 1 makes the bias exactly log w_bar);
   * a score exactly at the threshold gets weight 0 and mask bit 0.
 
+A top-k router (route_row_topk) is here for comparison only: it is not the method.
+
 Parity pins for this file live in tests/test_oracle_*.py.  The scale choices
 (1/sqrt(D) in Stages 0 and 2, gamma/sqrt(D) in Stage 1), the head_cls shape [Hkv, D],
 the diagonal branch and sigma are readings with no printed example: "parity unpinned".
@@ -254,6 +256,25 @@ def route_row(q_group: np.ndarray, summ: np.ndarray, t: int, *, alpha: float,
     return w_bar, margin, p
 
 
+def route_row_topk(q_group: np.ndarray, summ: np.ndarray, t: int, *, k: int, gamma: float,
+                   scale: float, chunk: int = CHUNK):
+    """Top-k routing, the comparison router (not the method's entmax): the group score of
+    chunk c is the mean over the G heads of gamma * scale * <q_h, summ_c>; the chunks whose
+    group score is at least the k-th largest are selected (every routed chunk when
+    i_t <= k), each with weight 1, i.e. no prior.
+
+    Returns (w_bar [i_t] in {0, 1}, margin [i_t] = group score - k-th largest)."""
+    it = t // chunk
+    if it == 0:
+        return np.zeros(0), np.zeros(0)
+    x = gamma * scale * (np.asarray(q_group, np.float64) @ np.asarray(summ[:it], np.float64).T)
+    z = x.mean(axis=0)
+    if it <= k:
+        return np.ones(it), np.full(it, np.inf)
+    kth = np.sort(z)[it - k]
+    return (z >= kth).astype(np.float64), z - kth
+
+
 # ---------------------------------------------------------------------------------------
 # Stage 2: attention of one query row over the diagonal chunk and the routed chunks
 # ---------------------------------------------------------------------------------------
@@ -285,11 +306,12 @@ def attend_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, w_bar: np.nd
 
 def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
             scale: Optional[float] = None, sigma: float = 1.0, chunk: int = CHUNK,
-            rows: Optional[Sequence[int]] = None, summaries: Optional[np.ndarray] = None
-            ) -> Dict[str, np.ndarray]:
+            rows: Optional[Sequence[int]] = None, summaries: Optional[np.ndarray] = None,
+            topk: int = 0) -> Dict[str, np.ndarray]:
     """Causal prefill.  q [B, Hq, T, D]; k, v [B, Hkv, T, D]; head_cls [Hkv, D].
 
     kv(h) = h // (Hq / Hkv).  `rows` restricts the rows computed (all by default).
+    topk > 0 routes with `route_row_topk` instead of entmax (margin: score - k-th score).
     Returns out [B, Hq, R, D], w_bar [B, Hkv, R, n_c], margin [B, Hkv, R, n_c]
     (nan where c >= t // C), mask [B, Hkv, R, n_c] (w_bar > 0), rows [R], summaries."""
     B, Hq, T, D = q.shape
@@ -312,8 +334,12 @@ def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
             for r, t in enumerate(rows):
                 t = int(t)
                 qg = np.asarray(q[b, kvh * G:(kvh + 1) * G, t], np.float64)
-                wb, mg, _ = route_row(qg, summaries[b, kvh], t, alpha=alpha, gamma=gamma,
-                                      scale=scale, chunk=chunk)
+                if topk > 0:
+                    wb, mg = route_row_topk(qg, summaries[b, kvh], t, k=topk, gamma=gamma,
+                                            scale=scale, chunk=chunk)
+                else:
+                    wb, mg, _ = route_row(qg, summaries[b, kvh], t, alpha=alpha, gamma=gamma,
+                                          scale=scale, chunk=chunk)
                 it = t // chunk
                 w_bar[b, kvh, r, :it] = wb
                 margin[b, kvh, r, :it] = mg

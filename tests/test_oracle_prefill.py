@@ -165,3 +165,49 @@ def test_needles_create_sparsity_in_routing():
     r = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], rows=rows)
     frac = O.zero_fraction(r["w_bar"], rows)
     assert frac > 0.3, frac
+
+
+# ---------------------------------------------------------------------------------------
+# Top-k comparison router
+# ---------------------------------------------------------------------------------------
+
+def test_topk_router_brute_force():
+    """On tiny rows the selected chunks are the k-subset with the largest total group score,
+    and k = 1 is the argmax."""
+    import itertools
+    rng = np.random.default_rng(41)
+    G, D = 4, 8
+    for trial in range(30):
+        it = int(rng.integers(2, 9))
+        t = 64 * it + int(rng.integers(0, 64))
+        qg = rng.normal(size=(G, D))
+        summ = rng.normal(size=(it, D))
+        z = (qg @ summ.T).mean(axis=0) * 0.3
+        for k in range(1, it + 1):
+            w, m = O.route_row_topk(qg, summ, t, k=k, gamma=1.0, scale=0.3)
+            sel = set(np.flatnonzero(w > 0))
+            best = max(itertools.combinations(range(it), k), key=lambda c: z[list(c)].sum())
+            assert sel == set(best) and len(sel) == k
+            assert np.all((m >= 0) == (w > 0))
+        w, _ = O.route_row_topk(qg, summ, t, k=1, gamma=1.0, scale=0.3)
+        assert np.flatnonzero(w) == [np.argmax(z)]
+
+
+def test_topk_router_keeps_ties_and_short_rows():
+    qg = np.ones((2, 4))
+    summ = np.array([[1.0, 0, 0, 0], [2.0, 0, 0, 0], [2.0, 0, 0, 0], [0.5, 0, 0, 0]])
+    w, _ = O.route_row_topk(qg, summ, 4 * 64, k=1, gamma=1.0, scale=1.0)
+    np.testing.assert_array_equal(w, [0, 1, 1, 0])            # both tied maxima
+    w, m = O.route_row_topk(qg, summ, 4 * 64 + 5, k=7, gamma=1.0, scale=1.0)
+    np.testing.assert_array_equal(w, [1, 1, 1, 1])            # i_t <= k: every chunk
+
+
+def test_topk_with_every_chunk_is_dense_causal():
+    """k at least the number of routed chunks selects everything with no prior: the whole
+    prefill equals textbook causal attention."""
+    T, D = 300, 8
+    q, k, v, hc = _rand(1, 4, 2, T, D, seed=43)
+    out = O.prefill(q, k, v, hc, topk=8)["out"]
+    for h in range(4):
+        ref = O.causal_attention(q[0, h], k[0, h // 2], v[0, h // 2])
+        np.testing.assert_allclose(out[0, h], ref, atol=1e-12)
