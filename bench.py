@@ -11,6 +11,8 @@ Prints ONE JSON line on stdout:
   decode     the 64K decode workload (B=16, 256 steps, summary appended when a chunk fills):
              us/step against the HBM roofline of its algorithmic bytes;
   dense      a dense causal flash-style kernel on the same inputs (the pages' comparator);
+  topk_router  the same prefill with a top-k comparison router (k = entmax's mean active
+             chunks per row) in place of entmax: Stage 1 and Stage 2 times;
   cpu_baseline  the float64 oracle timed on host cores over a bounded sample of rows.
 Progress lines go to stderr.
 """
@@ -97,6 +99,7 @@ def bench_prefill(args, w, dash, torch):
         union_flops = float(R * G * 4 * D * 64.0 * upc.sum() + G * 4 * D * B * Hkv * 64.0 * T)
     flops_dense = float(B * Hq * 4 * D * T * (T + 1) / 2)
     log(f"zero-weight fraction {zero_frac:.4f}; stage-2 algorithmic flops {flops2:.3e}")
+    k_match = max(1, int(round(float(active.sum()) / (B * Hkv * T))))   # mean active per row
     del pc, active
 
     def step(evs=None):
@@ -138,6 +141,32 @@ def bench_prefill(args, w, dash, torch):
             "kernel_ms": st[2]}
     res = dict(ms=ms, tokens_s=tokens_s, stages_ms=st, roofline=roof, zero_frac=zero_frac,
                flops2=flops2, flops_dense=flops_dense, x=x)
+
+    if not args.no_topk:
+        # the top-k comparison router on the same inputs, k = entmax's mean active chunks per
+        # row, so that Stage 2 gets about the same work and Stage 1 compares the routers
+        dash.prefill_stage(1, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                           enable_gqa=True, topk=k_match, active_blocks=ab)
+        torch.cuda.synchronize()
+        act_k = float(popcount64(ab).sum())
+        evk = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(-1, args.steps):
+            if i >= 0:
+                evk[i][0].record()
+            for s in range(3):
+                dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                                   enable_gqa=True, topk=k_match)
+                if i >= 0:
+                    evk[i][s + 1].record()
+        torch.cuda.synchronize()
+        stk = [float(np.mean([evk[i][s].elapsed_time(evk[i][s + 1]) for i in range(args.steps)]))
+               for s in range(3)]
+        res["topk"] = {"k": k_match, "stage1_ms": stk[1], "stage2_ms": stk[2],
+                       "prefill_ms": sum(stk),
+                       "active_fraction": act_k / float(routed.sum() * B * Hkv),
+                       "entmax_stage1_ms": st[1], "entmax_active_fraction": 1.0 - zero_frac}
+        log(f"top-k router (k={k_match}): stage 1 {stk[1]:.2f} ms (entmax {st[1]:.2f}), "
+            f"stage 2 {stk[2]:.2f} ms, active {res['topk']['active_fraction']:.3f}")
 
     if not args.no_dense:
         pd = dash.make_params(B, Hq, Hkv, T, D, enable_gqa=True, dtype=torch.bfloat16)
@@ -368,6 +397,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip timing the top-k comparison router")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
                     help="report the 64K sparsity sweep (one JSON line per cell) instead")
@@ -404,6 +435,7 @@ def main():
         "stages_ms": {"stage0_summaries_and_vT": pre["stages_ms"][0],
                       "stage1_route": pre["stages_ms"][1], "stage2_attend": pre["stages_ms"][2]},
         "dense": pre.get("dense"),
+        "topk_router": pre.get("topk"),
         "decode": dec,
     }
     print(json.dumps(line), flush=True)

@@ -71,6 +71,12 @@ typedef struct dash_params {
                          bias sigma * log w_bar_c.  1 is the prior itself, 0 a uniform prior
                          over the active chunks (gist.science, "Stufe 2": a hyperparameter
                          sigma weighs the routing values against a uniform baseline) */
+  int32_t topk;       /* 0: alpha-entmax routing (the method).  k > 0: a top-k comparison
+                         router instead -- per row and KV head, the chunks whose score summed
+                         over the G heads is at least the k-th largest (every routed chunk
+                         when there are at most k), each with weight 1 (no prior).  Not on the
+                         pages as part of the method: they compare against top-k routers
+                         (NSA, InfLLMv2; aixai.ru, experiments).  bf16 prefill only */
 } dash_params;
 
 /* Version of this ABI (major * 100 + minor). */

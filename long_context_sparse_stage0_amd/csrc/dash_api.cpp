@@ -63,6 +63,7 @@ int check_params(const dash_params* p, Dims* d, bool need_bf16 = false) {
     return fail(DASH_ERR_INVALID_ARG, "alpha must be finite and > 1");
   if (!(p->gamma > 0.0f) || !std::isfinite(p->gamma))
     return fail(DASH_ERR_INVALID_ARG, "gamma must be finite and > 0");
+  if (p->topk < 0) return fail(DASH_ERR_INVALID_ARG, "topk must be >= 0 (got %d)", p->topk);
   if (!(p->sigma >= 0.0f) || !std::isfinite(p->sigma))
     return fail(DASH_ERR_INVALID_ARG, "sigma (prior strength) must be finite and >= 0");
   if (!std::isfinite(p->sm_scale)) return fail(DASH_ERR_INVALID_ARG, "sm_scale is not finite");
@@ -179,7 +180,7 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
 
 extern "C" {
 
-int dash_abi_version(void) { return 101; }
+int dash_abi_version(void) { return 102; }
 
 const char* dash_last_error(void) { return g_err.c_str(); }
 
@@ -197,6 +198,8 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
                         void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
+  if (p->topk > 0 && d.dtype != DASH_BF16)
+    return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
   if (int rc = check_ptr(q, "q")) return rc;
   if (int rc = check_ptr(k, "k")) return rc;
   if (int rc = check_ptr(v, "v")) return rc;
@@ -248,6 +251,7 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   ra.tcap = d.T;
   ra.alpha = d.alpha;
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
+  ra.topk = p->topk;
   ra.dtype = d.dtype;
   if (stages & 2) {
     if (d.dtype == DASH_BF16)
@@ -326,6 +330,8 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
                 size_t workspace_bytes, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
+  if (p->topk > 0)
+    return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for prefill only");
   if (block_table) {
     if (d.dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "paged caches are bf16 only");
     if (num_pages <= 0) return fail(DASH_ERR_INVALID_ARG, "num_pages must be positive");

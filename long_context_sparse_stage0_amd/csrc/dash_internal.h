@@ -78,6 +78,7 @@ struct RouteArgs {
   int B, Hq, Hkv, D, Tq, rows, nc_alloc, W, wbar_ld;
   int tcap;               // prefill: T; decode: cache capacity (a query row must be < tcap)
   float alpha, zscale;    // zscale = (alpha - 1) * gamma * sm_scale
+  int topk;               // > 0: top-k comparison router instead of entmax (MFMA prefill)
   int dtype;
   int32_t* list;          // decode: [B * Hkv][list_ld]: count, then the active chunks in
   int list_ld;            // increasing order followed by the diagonal chunk (or nullptr)

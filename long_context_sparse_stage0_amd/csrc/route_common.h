@@ -28,7 +28,7 @@
 
 namespace dash {
 
-enum { kAlphaGeneral = 0, kAlpha15 = 1, kAlpha2 = 2 };
+enum { kAlphaGeneral = 0, kAlpha15 = 1, kAlpha2 = 2, kTopK = 3 };  // kTopK: comparison router
 
 __device__ __forceinline__ float pow_pos(float d, float e) {  // d > 0
   return fast_exp2(e * fast_log2(d));

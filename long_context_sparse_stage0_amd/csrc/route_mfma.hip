@@ -27,6 +27,9 @@
 // same totals for all 32 queries and takes the same decision.
 // GQA average: the G heads of a row are G adjacent columns of a 16-lane row, summed with
 // DPP (quad permutes, half-row and row mirrors) in a fixed order.
+// Top-k comparison router (topk > 0, not the method): the same scores summed over the
+// heads first, then a k-th-largest search by bits of an order-preserving key; the
+// selected chunks get weight 1 (no prior).
 #include <algorithm>
 #include <utility>
 
@@ -165,7 +168,83 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   const bool model_start = MODE == kAlpha15 && it >= kEntmaxModelMinN;
   const float inv = 1.0f / (a.alpha - 1.0f);
   int buf = 0;
-  if (it > 0) {
+  if (MODE == kTopK && it > 0) {
+    // ---- top-k comparison router: group score = sum of the G heads' scores of a row (the
+    // same order as their mean, G being a power of two); every chunk whose group score is
+    // at least the k-th largest is selected with weight 1.  The k-th largest is the largest
+    // order-preserving 32-bit key u with count(key >= u) >= k, built from the top bit down
+    // with one count per bit over the workgroup; it stops as soon as that count is exactly
+    // k, which already fixes the selected set.
+#pragma unroll
+    for (int qt = 0; qt < QTR; ++qt) {
+      if (G >= 2) head_step<0xB1>(y, qt);
+      if (G >= 4) head_step<0x4E>(y, qt);
+      if (G >= 8) head_step<0x141>(y, qt);
+      if (G >= 16) head_step<0x140>(y, qt);
+    }
+    // the scores become their keys in place (bit patterns only, never used as floats); an
+    // absent chunk (-inf) gets a key below that of every finite score, kKeyFinite
+    constexpr uint32_t kKeyFinite = 0x00800000u;
+#pragma unroll
+    for (int qt = 0; qt < QTR; ++qt)
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t u = __float_as_uint(y[j][qt][jj]);
+          y[j][qt][jj] = __uint_as_float((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+        }
+    const int kk = a.topk;
+    uint32_t thr[QTR];
+    float have[QTR];                                // count(key >= thr)
+#pragma unroll
+    for (int qt = 0; qt < QTR; ++qt) {
+      thr[qt] = 0u;
+      have[qt] = (float)it;
+    }
+    if (it > kk) {
+      for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+        for (int qt = 0; qt < QTR; ++qt) {
+          const uint32_t cand = max(thr[qt] | (1u << bit), kKeyFinite);
+          float cnt = 0.f;
+#pragma unroll
+          for (int j = 0; j < MT; ++j) {
+            if (j >= nj) continue;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) cnt += __float_as_uint(y[j][qt][jj]) >= cand ? 1.f : 0.f;
+          }
+          cnt = xg_sum(cnt);
+          if (lg == 0) part[buf][qt][0][l16][wv] = cnt;
+        }
+        __syncthreads();
+        bool settled = true;
+#pragma unroll
+        for (int qt = 0; qt < QTR; ++qt) {
+          float tot = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) tot += part[buf][qt][0][l16][w];
+          if (have[qt] != (float)kk && tot >= (float)kk) {
+            thr[qt] |= 1u << bit;
+            have[qt] = tot;
+          }
+          settled = settled && have[qt] == (float)kk;
+        }
+        buf ^= 1;
+        // every wave read the same totals, so the exit is uniform over the workgroup
+        if (__ballot(!settled) == 0ull) break;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QTR; ++qt) {
+      const uint32_t lim = max(thr[qt], kKeyFinite);
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) y[j][qt][jj] = __float_as_uint(y[j][qt][jj]) >= lim ? 1.f : 0.f;
+    }
+  }
+  if (MODE != kTopK && it > 0) {
     // pass 0: max
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) {
@@ -332,18 +411,20 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     for (int qt = 0; qt < QTR; ++qt) {
       // 1/G of the GQA mean folded into each head's normaliser; the weights replace the
       // scores in place (chunks past it hold y = -inf, so their weight and bit are 0)
-      const float rz = 1.0f / (zs[qt] * (float)G);
+      if (MODE != kTopK) {
+        const float rz = 1.0f / (zs[qt] * (float)G);
 #pragma unroll
-      for (int j = 0; j < MT; ++j)
+        for (int j = 0; j < MT; ++j)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          y[j][qt][jj] = entmax_weight_nonneg<MODE>(y[j][qt][jj], tau[qt], inv, rz);
-      // GQA sum over the G adjacent lanes of a row, one (wave-uniform) test of G per step
-      // for all of the lane's weights
-      if (G >= 2) head_step<0xB1>(y, qt);
-      if (G >= 4) head_step<0x4E>(y, qt);
-      if (G >= 8) head_step<0x141>(y, qt);
-      if (G >= 16) head_step<0x140>(y, qt);
+          for (int jj = 0; jj < 4; ++jj)
+            y[j][qt][jj] = entmax_weight_nonneg<MODE>(y[j][qt][jj], tau[qt], inv, rz);
+        // GQA sum over the G adjacent lanes of a row, one (wave-uniform) test of G per step
+        // for all of the lane's weights
+        if (G >= 2) head_step<0xB1>(y, qt);
+        if (G >= 4) head_step<0x4E>(y, qt);
+        if (G >= 8) head_step<0x141>(y, qt);
+        if (G >= 16) head_step<0x140>(y, qt);
+      }
       // w_bar stores go through a buffer descriptor over this workgroup's rows that ends at
       // the last row below T: a lane with nothing to store uses an offset past the end, which
       // the hardware drops, so the stores need no branches
@@ -424,7 +505,9 @@ void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit, int rt_lo, int r
 template <int D, int NW, int MT, int QTR>
 static void launch_mt(const RouteArgs& a, const bf16* ss, int rt_lo, int rt_n, hipStream_t s) {
   dim3 grid(rt_n * a.B * a.Hkv);
-  if (a.alpha == 1.5f)
+  if (a.topk > 0)
+    k_route_mfma<D, NW, MT, QTR, kTopK><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+  else if (a.alpha == 1.5f)
     k_route_mfma<D, NW, MT, QTR, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
   else if (a.alpha == 2.0f)
     k_route_mfma<D, NW, MT, QTR, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);

@@ -48,6 +48,7 @@ class DashParams(ctypes.Structure):
         ("alpha", ctypes.c_float), ("gamma", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("enable_gqa", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("estimate_diagonal", ctypes.c_int32), ("sigma", ctypes.c_float),
+        ("topk", ctypes.c_int32),
     ]
 
 
@@ -98,11 +99,11 @@ def _check(rc: int):
 
 def make_params(B, Hq, Hkv, T, D, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=None,
                 enable_gqa=False, dtype=torch.bfloat16, estimate_diagonal=False,
-                sigma=1.0) -> DashParams:
+                sigma=1.0, topk=0) -> DashParams:
     return DashParams(B=B, Hq=Hq, Hkv=Hkv, T=T, D=D, chunk_size=chunk_size, alpha=alpha,
                       gamma=gamma, sm_scale=0.0 if sm_scale is None else sm_scale,
                       enable_gqa=int(bool(enable_gqa)), dtype=DTYPES.get(dtype, 99),
-                      estimate_diagonal=int(bool(estimate_diagonal)), sigma=sigma)
+                      estimate_diagonal=int(bool(estimate_diagonal)), sigma=sigma, topk=topk)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -134,7 +135,8 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=None,
-            sigma=1.0, enable_gqa=False, estimate_diagonal=False, return_active_blocks=False,
+            sigma=1.0, topk=0, enable_gqa=False, estimate_diagonal=False,
+            return_active_blocks=False,
             return_block_weights=False, return_summaries=False, out=None, workspace=None,
             stream=None):
     """Causal prefill.  q [B,Hq,T,D]; k, v [B,Hkv,T,D]; head_cls [Hkv,D].
@@ -145,7 +147,7 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
     Hkv = k.shape[1]
     p = make_params(B, Hq, Hkv, T, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
                     sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype,
-                    estimate_diagonal=estimate_diagonal, sigma=sigma)
+                    estimate_diagonal=estimate_diagonal, sigma=sigma, topk=topk)
     nc = -(-T // 64)
     W = -(-nc // 64)
     dev = q.device
@@ -164,14 +166,14 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
 
 
 def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=1.0,
-                  sm_scale=None, sigma=1.0, enable_gqa=False, active_blocks=None,
+                  sm_scale=None, sigma=1.0, topk=0, enable_gqa=False, active_blocks=None,
                   block_weights=None,
                   summaries=None, stream=None):
     """Run one prefill stage (0, 1 or 2) from the intermediates a full `prefill` call with
     the same tensors and workspace left behind (profiling aid)."""
     B, Hq, T, D = q.shape
     p = make_params(B, Hq, k.shape[1], T, D, alpha=alpha, gamma=gamma, sm_scale=sm_scale,
-                    enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
+                    enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma, topk=topk)
     _check(load().dash_prefill_stage(ctypes.byref(p), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(head_cls), _ptr(out), _ptr(active_blocks),
                                      _ptr(block_weights), _ptr(summaries), _ptr(workspace),

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = _lib()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.dash_abi_version() == 101
+    assert lib.dash_abi_version() == 102
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
@@ -41,7 +41,7 @@ MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
 
 def _params(**kw):
     base = dict(B=1, Hq=4, Hkv=2, T=256, D=128, chunk_size=64, alpha=1.5, gamma=1.0,
-                sm_scale=0.0, enable_gqa=1, dtype=0, estimate_diagonal=0, sigma=1.0)
+                sm_scale=0.0, enable_gqa=1, dtype=0, estimate_diagonal=0, sigma=1.0, topk=0)
     base.update(kw)
     return dash.DashParams(**base)
 
@@ -73,6 +73,7 @@ def _ws(p):
     (dict(sigma=-0.5), -1),
     (dict(sigma=float("nan")), -1),
     (dict(sigma=float("inf")), -1),
+    (dict(topk=-1), -1),
     (dict(T=64 * 2049 + 1), -4),
 ])
 def test_param_validation(kw, code):
@@ -144,6 +145,12 @@ def test_decode_append_dense_validation():
                                        None) == -1
     assert lib.dash_append_chunk_paged(ctypes.byref(p), FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        None) == -1
+    # the top-k comparison router: bf16 prefill only
+    pt = _params(T=65792, Hq=32, Hkv=2, topk=8)
+    assert lib.dash_decode(ctypes.byref(pt), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                           n.value, None) == -4
+    assert lib.dash_prefill(ctypes.byref(_params(dtype=1, topk=8)), FAKE, FAKE, FAKE, FAKE,
+                            FAKE, None, None, None, FAKE, 1 << 30, None) == -4
     # the dense comparator is bf16 only
     pf = _params(dtype=1)
     assert lib.dash_dense_causal_workspace_size(ctypes.byref(pf), ctypes.byref(n)) == -3

@@ -26,19 +26,19 @@ def dash():
     return d
 
 
-def run_prefill(dash, w: Workload, rows=None, alpha=None, sigma=1.0):
+def run_prefill(dash, w: Workload, rows=None, alpha=None, sigma=1.0, topk=0):
     alpha = w.alpha if alpha is None else alpha
     x = synth.prefill_inputs(w)
     say(f"[parity] prefill {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} "
         f"{w.dtype} alpha={alpha} sigma={sigma}")
     q, k, v, hc = (to_dev(x[n], w.dtype) for n in ("q", "k", "v", "head_cls"))
-    out, ab, bw, sm = dash.prefill(q, k, v, hc, alpha=alpha, gamma=w.gamma, sigma=sigma,
+    out, ab, bw, sm = dash.prefill(q, k, v, hc, alpha=alpha, gamma=w.gamma, sigma=sigma, topk=topk,
                                    enable_gqa=w.enable_gqa, return_active_blocks=True,
                                    return_block_weights=True, return_summaries=True)
     torch.cuda.synchronize()
     rows = np.arange(w.T) if rows is None else np.asarray(rows)
     ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=alpha, gamma=w.gamma,
-                    sigma=sigma, rows=rows)
+                    sigma=sigma, rows=rows, topk=topk)
     nc = -(-w.T // 64)
     g_out = out.float().cpu().numpy()[:, :, rows]
     g_bits = unpack_words(ab.cpu().numpy(), nc)[:, :, rows]
@@ -108,6 +108,45 @@ def test_decode_prior_strength(dash):
         ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
                         sigma=2.0, rows=[lens[b] - 1])
         compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"decode sigma b={b}")
+
+
+@pytest.mark.parametrize("G,k,T,rows", [
+    (16, 8, 2000, list(range(0, 2000, 7)) + [1999]),   # the 128K workload's head ratio
+    (4, 1, 1100, None),                                 # argmax routing, every row
+    (8, 40, 1500, list(range(0, 1500, 5)) + [1499]),   # k above the early rows' lengths
+    (16, 64, 16384, [64, 4095, 9000, 16383]),
+])
+def test_prefill_topk_router(dash, G, k, T, rows):
+    """The top-k comparison router: mask bits equal the oracle's outside the 1e-4 score
+    margin, weight 1 at every set bit, and every row's output equals the oracle's attention
+    over the chunks the GPU selected (equal to the oracle's own selection where no chunk
+    sits within the margin of the k-th score)."""
+    w = Workload(name=f"topk_g{G}", kind="prefill", B=1, Hq=2 * G, Hkv=2, T=T, D=128,
+                 dtype="bf16", seed=970 + G, needle_amp=1.0)
+    r = run_prefill(dash, w, rows=rows, topk=k)
+    ref, rows = r["ref"], r["rows"]
+    amb = compare_mask(r["bits"], ref["mask"], ref["margin"], rows)
+    nc = r["nc"]
+    # weights: exactly 1 at set bits, 0 elsewhere
+    np.testing.assert_array_equal(r["w"][r["bits"][..., :r["w"].shape[-1]]], 1.0)
+    # selection size: k per row (all routed chunks when there are at most k), ties aside
+    for i, t in enumerate(rows):
+        n = r["bits"][0, :, i, :t // 64].sum(axis=-1)
+        assert np.all(n >= min(k, t // 64)), (t, n)
+    # outputs against the oracle's attention over the GPU's own selection
+    x = r["x"]
+    scale = 1.0 / np.sqrt(w.D)
+    err = 0.0
+    for i, t in enumerate(rows):
+        for kvh in range(w.Hkv):
+            wb = r["bits"][0, kvh, i, :t // 64].astype(np.float64)
+            for g in range(G):
+                h = kvh * G + g
+                o = O.attend_row(x["q"][0, h, t], x["k"][0, kvh], x["v"][0, kvh], int(t), wb,
+                                 scale=scale)
+                err = max(err, compare_out(r["out"][0, h, i], o, "bf16", what=f"topk row {t}"))
+    flips = int((r["bits"][..., :nc] != ref["mask"]).sum())
+    say(f"[parity]   topk k={k}: out err {err:.2e}, near-threshold flips {amb} (all flips {flips})")
 
 
 def test_prefill_fp32_gqa_and_scale(dash):
