@@ -387,6 +387,69 @@ def bench_sweep(args, dash, torch):
         torch.cuda.empty_cache()
 
 
+def bench_short(args, dash, torch):
+    """Short contexts (a report, not the benchmark line): the 16K workload's shape (32/8 heads,
+    D = 128, bf16, needles +3 sigma) at T = 2K..16K; per T, the entmax prefill, the same
+    prefill with the top-k comparison router at k = entmax's mean active chunks per row, and
+    the dense causal kernel.  One JSON line per T on stdout."""
+    import dataclasses
+    from long_context_sparse_stage0_amd import synth
+    from long_context_sparse_stage0_amd.workloads import PREFILL_16K_GQA as base
+    dev = torch.device("cuda:0")
+    for T in (2048, 4096, 8192, 16384):
+        w = dataclasses.replace(base, name=f"prefill_{T // 1024}k_gqa32x8", T=T)
+        x = synth.prefill_inputs(w)
+        q, k, v, hc = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev)
+                       for n in ("q", "k", "v", "head_cls"))
+        del x
+        B, Hq, _, D = q.shape
+        W = -(-(-(-T // 64)) // 64)
+        out = torch.empty_like(q)
+        ab = torch.empty((B, w.Hkv, T, W), dtype=torch.int64, device=dev)
+        p = dash.make_params(B, Hq, w.Hkv, T, D, alpha=w.alpha, enable_gqa=True,
+                             dtype=torch.bfloat16)
+        ws = dash.alloc_workspace(dash.workspace_size("prefill", p), dev)
+        dash.prefill_stage(0, q, k, v, hc, out, ws, enable_gqa=True)
+        dash.prefill_stage(1, q, k, v, hc, out, ws, enable_gqa=True, active_blocks=ab)
+        torch.cuda.synchronize()
+        routed = float((torch.arange(T, device=dev) // 64).sum()) * B * w.Hkv
+        act = float(popcount64(ab).sum())
+        kk = max(1, int(round(act / (B * w.Hkv * T))))
+
+        def timed(fn, n):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        def prefill(topk):
+            for s in range(3):
+                dash.prefill_stage(s, q, k, v, hc, out, ws, enable_gqa=True, topk=topk)
+
+        def stage1(topk):
+            dash.prefill_stage(1, q, k, v, hc, out, ws, enable_gqa=True, topk=topk)
+        n = max(3, args.steps)
+        ms_e, s1_e = timed(lambda: prefill(0), n), timed(lambda: stage1(0), n)
+        ms_k, s1_k = timed(lambda: prefill(kk), n), timed(lambda: stage1(kk), n)
+        pd = dash.make_params(B, Hq, w.Hkv, T, D, enable_gqa=True, dtype=torch.bfloat16)
+        wsd = dash.alloc_workspace(dash.workspace_size("dense", pd), dev)
+        ms_d = timed(lambda: dash.dense_causal(q, k, v, enable_gqa=True, out=out, workspace=wsd), n)
+        line = {"workload": w.name, "T": T, "entmax_active_fraction": act / routed,
+                "entmax_prefill_ms": ms_e, "entmax_stage1_ms": s1_e,
+                "topk_k": kk, "topk_prefill_ms": ms_k, "topk_stage1_ms": s1_k,
+                "dense_ms": ms_d, "speedup_entmax_over_dense": ms_d / ms_e}
+        print(json.dumps(line), flush=True)
+        log(f"{w.name}: entmax {ms_e:.3f} ms (stage 1 {s1_e:.3f}), top-{kk} {ms_k:.3f} ms "
+            f"(stage 1 {s1_k:.3f}), dense {ms_d:.3f} ms, active {act / routed:.3f}")
+        del q, k, v, hc, out, ws, wsd, ab
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +463,8 @@ def main():
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the top-k comparison router")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--short", action="store_true",
+                    help="report entmax / top-k / dense at T = 2K..16K (one JSON line per T)")
     ap.add_argument("--sweep", action="store_true",
                     help="report the 64K sparsity sweep (one JSON line per cell) instead")
     args = ap.parse_args()
@@ -416,6 +481,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sweep:
         bench_sweep(args, dash, torch)
+        return
+    if args.short:
+        bench_short(args, dash, torch)
         return
     w = ALL[args.workload]
     pre = bench_prefill(args, w, dash, torch)
