@@ -76,7 +76,7 @@ typedef struct dash_params {
                          over the G heads is at least the k-th largest (every routed chunk
                          when there are at most k), each with weight 1 (no prior).  Not on the
                          pages as part of the method: they compare against top-k routers
-                         (NSA, InfLLMv2; aixai.ru, experiments).  bf16 prefill only */
+                         (NSA, InfLLMv2; aixai.ru, experiments).  bf16 only */
 } dash_params;
 
 /* Version of this ABI (major * 100 + minor). */

@@ -330,8 +330,8 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
                 size_t workspace_bytes, void* stream) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
-  if (p->topk > 0)
-    return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for prefill only");
+  if (p->topk > 0 && d.dtype != DASH_BF16)
+    return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
   if (block_table) {
     if (d.dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "paged caches are bf16 only");
     if (num_pages <= 0) return fail(DASH_ERR_INVALID_ARG, "num_pages must be positive");
@@ -369,6 +369,7 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
   ra.tcap = d.T;
   ra.alpha = d.alpha;
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
+  ra.topk = p->topk;
   ra.dtype = d.dtype;
   ra.list = reinterpret_cast<int32_t*>(ws + L.list);
   ra.list_ld = d.nc + 2;

@@ -9,7 +9,8 @@
 //                    wave over many workgroups, so the summary reads are spread over the
 //                    whole GPU rather than one CU per (b, kv head).
 //   k_decode_route   one 16-wave workgroup per (b, kv head): wave g solves head g's entmax
-//                    threshold with wave-only reductions; then a fixed-order sum over the
+//                    threshold with wave-only reductions (or, for the top-k comparison
+//                    router, wave 0 selects on the heads' summed scores); then a fixed-order sum over the
 //                    heads, a ballot per 64 chunks for the mask word, w_bar at set bits and
 //                    the attend kernel's work list.
 //   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
@@ -140,6 +141,55 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   auto solve = [&](auto nr_tag) {
     constexpr int NRU = decltype(nr_tag)::value;
     float y[NRU];
+    if constexpr (MODE == kTopK) {
+      // top-k comparison router (wave 0): group score = the G heads' scores summed in head
+      // order; the chunks at or above the k-th largest get weight 1 for every head (so their
+      // mean is 1).  The k-th largest is the largest order-preserving key u with
+      // count(key >= u) >= k, built from the top bit down; it stops once that count is k.
+      constexpr uint32_t kKeyFinite = 0x00800000u;   // every finite score's key is above it
+#pragma unroll
+      for (int r = 0; r < NRU; ++r) y[r] = 0.f;
+      for (int g = 0; g < G; ++g) {
+        const float* sg = a.sco + ((size_t)bk * G + g) * a.sco_ld;
+#pragma unroll
+        for (int r = 0; r < NRU; ++r) {
+          const int c = lane + 64 * r;
+          if (c < it) y[r] += sg[c];
+        }
+      }
+      uint32_t key[NRU];
+#pragma unroll
+      for (int r = 0; r < NRU; ++r) {
+        const uint32_t u = __float_as_uint(y[r]);
+        key[r] = lane + 64 * r < it ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
+      }
+      uint32_t thr = 0u;
+      float have = (float)it;
+      if (it > a.topk) {
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = max(thr | (1u << bit), kKeyFinite);
+          float cnt = 0.f;
+#pragma unroll
+          for (int r = 0; r < NRU; ++r) cnt += key[r] >= cand ? 1.f : 0.f;
+          cnt = wave_sum(cnt);
+          if (cnt >= (float)a.topk) {
+            thr |= 1u << bit;
+            have = cnt;
+          }
+          if (have == (float)a.topk) break;
+        }
+      }
+      const uint32_t lim = max(thr, kKeyFinite);
+#pragma unroll
+      for (int r = 0; r < NRU; ++r) {
+        const int c = lane + 64 * r;
+        if (c < it) {
+          const float v = key[r] >= lim ? 1.f : 0.f;
+          for (int g = 0; g < G; ++g) sc[g * ld + c] = v;
+        }
+      }
+      return;
+    } else {
 #pragma unroll
     for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
@@ -153,8 +203,9 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
       const int c = lane + 64 * r;
       if (c < it) sc[wv * ld + c] = entmax_weight<MODE>(y[r], tau, inv, rz);
     }
+    }
   };
-  if (wv < G && it > 0) {
+  if ((MODE == kTopK ? wv == 0 : wv < G) && it > 0) {
     if (it <= 256) solve(std::integral_constant<int, 4>{});
     else if (it <= 512) solve(std::integral_constant<int, 8>{});
     else if (it <= 768) solve(std::integral_constant<int, 12>{});
@@ -564,11 +615,13 @@ hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   dim3 grid(a.B * a.Hkv);
   if (a.D == 128) {
-    if (a.alpha == 1.5f) k_decode_route<128, kAlpha15><<<grid, 1024, 0, s>>>(a);
+    if (a.topk > 0) k_decode_route<128, kTopK><<<grid, 1024, 0, s>>>(a);
+    else if (a.alpha == 1.5f) k_decode_route<128, kAlpha15><<<grid, 1024, 0, s>>>(a);
     else if (a.alpha == 2.0f) k_decode_route<128, kAlpha2><<<grid, 1024, 0, s>>>(a);
     else k_decode_route<128, kAlphaGeneral><<<grid, 1024, 0, s>>>(a);
   } else {
-    if (a.alpha == 1.5f) k_decode_route<64, kAlpha15><<<grid, 1024, 0, s>>>(a);
+    if (a.topk > 0) k_decode_route<64, kTopK><<<grid, 1024, 0, s>>>(a);
+    else if (a.alpha == 1.5f) k_decode_route<64, kAlpha15><<<grid, 1024, 0, s>>>(a);
     else if (a.alpha == 2.0f) k_decode_route<64, kAlpha2><<<grid, 1024, 0, s>>>(a);
     else k_decode_route<64, kAlphaGeneral><<<grid, 1024, 0, s>>>(a);
   }

@@ -181,14 +181,15 @@ def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=
 
 
 def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha=1.5,
-           gamma=1.0, sm_scale=None, sigma=1.0, enable_gqa=False, return_active_blocks=False,
-           out=None, workspace=None, stream=None):
+           gamma=1.0, sm_scale=None, sigma=1.0, topk=0, enable_gqa=False,
+           return_active_blocks=False, out=None, workspace=None, stream=None):
     """One decode step.  q [B,Hq,D]; caches [B,Hkv,T_max,D]; seq_lens [B] int32 (device);
     summary_cache [B,Hkv,ceil(T_max/64),D] fp32."""
     B, Hq, D = q.shape
     Hkv, T_max = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
-                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
+                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma,
+                    topk=topk)
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     nc = -(-T_max // 64)
@@ -216,7 +217,7 @@ def append_chunk(k_cache, head_cls, seq_lens, summary_cache, n_summarized, *, ch
 
 
 def _paged_params(q_or_none, k_pages, block_table, Hq, chunk_size, alpha, gamma, sm_scale,
-                  sigma, enable_gqa):
+                  sigma, enable_gqa, topk=0):
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise ValueError("block_table must be an int32 [B, ceil(T_max/64)] tensor")
     num_pages, Hkv, C, D = k_pages.shape
@@ -225,18 +226,19 @@ def _paged_params(q_or_none, k_pages, block_table, Hq, chunk_size, alpha, gamma,
     B = block_table.shape[0]
     T_max = block_table.shape[1] * chunk_size
     p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
-                    sm_scale=sm_scale, sigma=sigma, enable_gqa=enable_gqa, dtype=k_pages.dtype)
+                    sm_scale=sm_scale, sigma=sigma, enable_gqa=enable_gqa, dtype=k_pages.dtype,
+                    topk=topk)
     return p, num_pages
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, summary_cache, *, chunk_size=64,
-                 alpha=1.5, gamma=1.0, sm_scale=None, sigma=1.0, enable_gqa=False,
+                 alpha=1.5, gamma=1.0, sm_scale=None, sigma=1.0, topk=0, enable_gqa=False,
                  return_active_blocks=False, out=None, workspace=None, stream=None):
     """One decode step over paged caches.  q [B,Hq,D]; k_pages, v_pages [num_pages,Hkv,64,D];
     block_table [B, ceil(T_max/64)] int32 (device); the rest as for `decode`."""
     B, Hq, D = q.shape
     p, num_pages = _paged_params(q, k_pages, block_table, Hq, chunk_size, alpha, gamma, sm_scale,
-                                 sigma, enable_gqa)
+                                 sigma, enable_gqa, topk)
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     W = -(-block_table.shape[1] // 64)

@@ -145,10 +145,10 @@ def test_decode_append_dense_validation():
                                        None) == -1
     assert lib.dash_append_chunk_paged(ctypes.byref(p), FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        None) == -1
-    # the top-k comparison router: bf16 prefill only
-    pt = _params(T=65792, Hq=32, Hkv=2, topk=8)
+    # the top-k comparison router: bf16 only
+    pt = _params(T=65792, Hq=32, Hkv=2, topk=8, dtype=1)
     assert lib.dash_decode(ctypes.byref(pt), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
-                           n.value, None) == -4
+                           1 << 30, None) == -4
     assert lib.dash_prefill(ctypes.byref(_params(dtype=1, topk=8)), FAKE, FAKE, FAKE, FAKE,
                             FAKE, None, None, None, FAKE, 1 << 30, None) == -4
     # the dense comparator is bf16 only

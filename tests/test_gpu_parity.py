@@ -149,6 +149,44 @@ def test_prefill_topk_router(dash, G, k, T, rows):
     say(f"[parity]   topk k={k}: out err {err:.2e}, near-threshold flips {amb} (all flips {flips})")
 
 
+@pytest.mark.parametrize("k", [1, 16, 200])
+def test_decode_topk_router(dash, k):
+    """Decode with the top-k comparison router: mask bits equal the oracle's prefill row
+    outside the 1e-4 score margin, and the output equals the oracle's attention over the
+    chunks the GPU selected."""
+    w = Workload(name="dec_topk", kind="prefill", B=3, Hq=32, Hkv=2, T=9000, D=128,
+                 dtype="bf16", seed=980, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say(f"[parity] decode top-{k}")
+    kk, vv, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    lens = [9000, 4100, 700]
+    nc = -(-w.T // 64)
+    summ = torch.zeros((3, 2, nc, 128), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(3, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dash.append_chunk(kk, hc, lens_t, summ, nsum, Hq=32, enable_gqa=True)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(3)]).contiguous()
+    out, ab = dash.decode(q, kk, vv, lens_t, summ, topk=k, enable_gqa=True,
+                          return_active_blocks=True)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    bits = unpack_words(ab.cpu().numpy(), nc)
+    scale = 1.0 / np.sqrt(128)
+    for b in range(3):
+        t = lens[b] - 1
+        ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                        rows=[t], topk=k)
+        compare_mask(bits[b][:, None], ref["mask"][0], ref["margin"][0], [t])
+        for kvh in range(2):
+            wb = bits[b, kvh, :t // 64].astype(np.float64)
+            assert wb.sum() >= min(k, t // 64)
+            for hh in range(16):
+                h = kvh * 16 + hh
+                o = O.attend_row(x["q"][b, h, t], x["k"][b, kvh], x["v"][b, kvh], t, wb,
+                                 scale=scale)
+                compare_out(g[b, h], o, "bf16", what=f"decode topk b={b} h={h}")
+
+
 def test_prefill_fp32_gqa_and_scale(dash):
     w = Workload(name="fp32_gqa", kind="prefill", B=1, Hq=8, Hkv=2, T=390, D=128,
                  dtype="fp32", gamma=2.0, seed=77, needle_amp=1.5)
