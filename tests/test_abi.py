@@ -167,3 +167,15 @@ def test_binding_fails_loudly_without_library(tmp_path):
             dash.load(str(tmp_path / "missing.so"))
     finally:
         dash._lib = saved
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits with a message before touching
+    torch or a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
