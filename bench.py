@@ -100,6 +100,16 @@ def bench_prefill(args, w, dash, torch):
     flops_dense = float(B * Hq * 4 * D * T * (T + 1) / 2)
     log(f"zero-weight fraction {zero_frac:.4f}; stage-2 algorithmic flops {flops2:.3e}")
     k_match = max(1, int(round(float(active.sum()) / (B * Hkv * T))))   # mean active per row
+    # Stage 0 and Stage 1 algorithmic work: Stage 0 reads K and writes the fp32 summaries
+    # (the bf16 split planes and the chunk-transposed V are this implementation's extras);
+    # Stage 1 reads Q and the summaries once, writes the mask and w_bar at set bits, and
+    # does 2 D flops per (query vector, routed chunk) score (twice, for the hi and lo planes)
+    nfull = T // 64
+    s0_bytes = float(B * Hkv * (T * D * 2 + nfull * D * 4))
+    s0_extra = float(B * Hkv * (nfull * D * 2 * 2 + 2 * T * D * 2))
+    s1_bytes = float(B * Hq * T * D * 2 + B * Hkv * nc * D * 4 + B * Hkv * T * W * 8
+                     + active.sum() * 4)
+    s1_flops = float(2 * D * Hq * B * routed.sum())
     del pc, active
 
     def step(evs=None):
@@ -141,6 +151,19 @@ def bench_prefill(args, w, dash, torch):
             "kernel_ms": st[2]}
     res = dict(ms=ms, tokens_s=tokens_s, stages_ms=st, roofline=roof, zero_frac=zero_frac,
                flops2=flops2, flops_dense=flops_dense, x=x)
+    res["stage0"] = {"ms": st[0], "algorithmic_bytes": s0_bytes,
+                     "gbs": s0_bytes / (st[0] / 1e3) / 1e9,
+                     "frac_of_hbm_peak": s0_bytes / (st[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "extra_bytes_split_and_vT": s0_extra,
+                     "gbs_with_extras": (s0_bytes + s0_extra) / (st[0] / 1e3) / 1e9}
+    s1_lb = {"mfma_ms": 2 * s1_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
+             "hbm_ms": s1_bytes / (PEAK_HBM_GBS * 1e9) * 1e3}
+    res["stage1"] = {"ms": st[1], "algorithmic_bytes": s1_bytes,
+                     "gbs": s1_bytes / (st[1] / 1e3) / 1e9,
+                     "frac_of_hbm_peak": s1_bytes / (st[1] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "score_flops": s1_flops, "executed_score_flops_hi_lo": 2 * s1_flops,
+                     "lower_bound_ms": s1_lb,
+                     "frac_of_lower_bound": max(s1_lb.values()) / st[1]}
 
     if not args.no_topk:
         # the top-k comparison router on the same inputs, k = entmax's mean active chunks per
@@ -502,6 +525,8 @@ def main():
         "cpu_baseline": cpu,
         "stages_ms": {"stage0_summaries_and_vT": pre["stages_ms"][0],
                       "stage1_route": pre["stages_ms"][1], "stage2_attend": pre["stages_ms"][2]},
+        "stage0": pre["stage0"],
+        "stage1": pre["stage1"],
         "dense": pre.get("dense"),
         "topk_router": pre.get("topk"),
         "decode": dec,
