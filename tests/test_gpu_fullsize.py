@@ -143,6 +143,53 @@ def test_decode_64k_all_steps_sampled(dash):
             f"active fraction {act:.3f}")
 
 
+def test_decode_64k_paged_equals_contiguous(dash):
+    """The 64K decode workload over paged caches (every chunk of every sequence in a
+    shuffled page of one pool): 24 steps across a chunk boundary with the paged append give
+    outputs and masks bit-identical to the contiguous caches."""
+    w = DECODE_64K_B16
+    x = synth.decode_inputs(w)
+    say(f"[fullsize] paged decode {w.name} B={w.B}")
+    kc, vc, hc = (to_dev(x[n], "bf16") for n in ("k_cache", "v_cache", "head_cls"))
+    qs = to_dev(x["q_steps"][40:64 + 40], "bf16")        # steps 40..63 cross a chunk boundary
+    del x
+    B, Hkv, TT, D = kc.shape
+    Hq = qs.shape[2]
+    nc = -(-TT // 64)
+    perm = torch.randperm(B * nc, generator=torch.Generator().manual_seed(77)).cuda()
+
+    def pages(cache):
+        pad = torch.zeros((B, Hkv, nc * 64, D), dtype=cache.dtype, device="cuda")
+        pad[:, :, :TT] = cache
+        pool = torch.empty((B * nc, Hkv, 64, D), dtype=cache.dtype, device="cuda")
+        pool[perm] = pad.view(B, Hkv, nc, 64, D).permute(0, 2, 1, 3, 4).reshape(B * nc, Hkv, 64, D)
+        return pool
+    kp, vp = pages(kc), pages(vc)
+    table = perm.view(B, nc).to(torch.int32).contiguous()
+    L0 = w.T + 40
+    s_c = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device="cuda")
+    s_p = torch.zeros_like(s_c)
+    n_c = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n_p = torch.zeros_like(n_c)
+    init = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    dash.append_chunk(kc, hc, init, s_c, n_c, Hq=Hq, enable_gqa=True)
+    dash.append_chunk_paged(kp, table, hc, init, s_p, n_p, Hq=Hq, enable_gqa=True)
+    for s in range(24):
+        L = L0 + 1 + s
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        o_c, a_c = dash.decode(qs[s], kc, vc, lens, s_c, alpha=w.alpha, enable_gqa=True,
+                               return_active_blocks=True)
+        o_p, a_p = dash.decode_paged(qs[s], kp, vp, table, lens, s_p, alpha=w.alpha,
+                                     enable_gqa=True, return_active_blocks=True)
+        assert torch.equal(o_c, o_p), f"step {s}: outputs differ"
+        assert torch.equal(a_c, a_p[..., :a_c.shape[-1]]), f"step {s}: masks differ"
+        if L % 64 == 0:
+            dash.append_chunk(kc, hc, lens, s_c, n_c, Hq=Hq, enable_gqa=True)
+            dash.append_chunk_paged(kp, table, hc, lens, s_p, n_p, Hq=Hq, enable_gqa=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s_c, s_p) and torch.equal(n_c, n_p)
+
+
 @pytest.mark.parametrize("alpha,lam", [(1.25, 32.0), (2.0, 2.0)])
 def test_sweep_64k_sampled_rows(dash, alpha, lam):
     """Two corners of the 64K sparsity sweep (32/8 heads, Poisson needle counts): the
