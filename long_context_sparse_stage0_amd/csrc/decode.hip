@@ -24,6 +24,7 @@
 //   k_decode_combine log-sum-exp merge of the segment partials, one workgroup per (b, kv
 //                    head).
 // Decoding is HBM-bound: the active K/V chunks (32 KiB each at D = 128) dominate the bytes.
+#include <atomic>
 #include <type_traits>
 
 #include "route_common.h"
@@ -628,18 +629,21 @@ hipError_t launch_decode_route(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Workgroup slots of the device (two attend workgroups per CU), looked up once per device.
+// Workgroup slots of the device (two attend workgroups per CU), looked up once per device
+// (callers on several host threads may race to fill the entry; they store the same value).
 static int attend_slots() {
-  static int slots[64] = {0};
+  static std::atomic<int> slots[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (slots[dev] == 0) {
+  int n = slots[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    slots[dev] = 2 * cus;
+    n = 2 * cus;
+    slots[dev].store(n, std::memory_order_relaxed);
   }
-  return slots[dev];
+  return n;
 }
 
 hipError_t launch_decode_attend(const AttendArgs& a, float* pml, float* po, hipStream_t s) {
