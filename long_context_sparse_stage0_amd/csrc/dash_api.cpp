@@ -125,7 +125,7 @@ PrefillLayout prefill_layout(const Dims& d) {
 }
 
 struct DecodeLayout {
-  size_t mask, wbar, list, sco, pml, po, total;
+  size_t mask, wbar, list, sco, pml, po, segsz, total;
 };
 
 DecodeLayout decode_layout(const Dims& d) {
@@ -144,6 +144,8 @@ DecodeLayout decode_layout(const Dims& d) {
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 32 * 4) : 0;
   L.po = off;
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hkv * nseg * 16 * d.D * 4) : 0;
+  L.segsz = off;
+  off += d.dtype == DASH_BF16 ? 256 : 0;
   L.total = off;
   return L;
 }
@@ -402,6 +404,7 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
   aa.dense = 0;
   aa.list = reinterpret_cast<const int32_t*>(ws + L.list);
   aa.list_ld = d.nc + 2;
+  aa.seg_size = reinterpret_cast<int32_t*>(ws + L.segsz);
   aa.block_table = block_table;
   aa.bt_ld = d.nc;
   aa.num_pages = num_pages;

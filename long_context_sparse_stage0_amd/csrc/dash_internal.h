@@ -103,6 +103,7 @@ struct AttendArgs {
   const int32_t* block_table;  // decode, paged caches: [B][bt_ld] page of each chunk, or
   int bt_ld;                   // nullptr for contiguous [B, Hkv, Tk, D] caches; pages are
   int num_pages;               // [num_pages][Hkv][64][D] (ids outside [0, num_pages) read as 0)
+  int32_t* seg_size;           // decode: the attend kernel's common segment size, for the combine
   const int32_t* list;    // decode: the route kernel's item lists (see RouteArgs)
   int list_ld;
 };

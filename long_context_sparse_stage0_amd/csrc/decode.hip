@@ -14,9 +14,10 @@
 //                    heads, a ballot per 64 chunks for the mask word, w_bar at set bits and
 //                    the attend kernel's work list.
 //   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
-//                    chunk form a list, cut into as many equal segments as keep every
-//                    workgroup slot of the GPU busy in one round; each of a workgroup's 4
-//                    waves takes every fourth item of its segment.  S^T = K Q^T with K rows
+//                    chunk form a list; all lists are cut into segments of one common
+//                    size, as many as keep every workgroup slot of the GPU busy in one
+//                    round, so that long and short lists are balanced; each of a
+//                    workgroup's 4 waves takes every fourth item of its segment.  S^T = K Q^T with K rows
 //                    loaded straight from global as MFMA operands, V staged through
 //                    wave-private LDS in [d][key] order for the V^T P^T product; the waves'
 //                    (max, sum, O) partials are merged in LDS and written once per
@@ -266,6 +267,24 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
 }
 
 // ------------------------------------------------------------------------------ attend
+// Global segmentation of the work lists (one wave): all B * Hkv lists are cut into segments
+// of one common size per = max(kSeg, ceil(N / (S - B Hkv))), N the total number of items
+// and S the number of attend workgroups, so that a (b, kv head) with n items gets
+// ceil(n / per) <= n / per + 1 segments and all of them fit in S.  Returns per.
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int segment_size(const AttendArgs& a, int S, int lane) {
+  const int BH = a.B * a.Hkv;
+  int n = 0;
+  for (int i = lane; i < BH; i += 64) n += a.list[(size_t)i * a.list_ld];
+  n = wave_isum(n);
+  const int room = max(1, S - BH);
+  return max(kSeg, (n + room - 1) / room);
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // V^T operand of the 16x16x32 MFMA for d rows d0 + (l % 16) and keys k0 + [0, 8), read from
@@ -289,7 +308,7 @@ __device__ __forceinline__ bf16x8 vt_operand(const bf16* tile, int pitch, int k0
 template <int D>
 __global__ __launch_bounds__(kAttWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ po, int nseg_max,
-                     int seg_target) {
+                     int seg_total) {
   constexpr int NT = kAttWaves * 64;
   constexpr int KS = D / 32, NDT = D / 16;
   constexpr int VP = D + 16;                      // V row pitch in LDS (bf16 elements)
@@ -301,7 +320,47 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int seg = blockIdx.x, bk = blockIdx.y;
+  // ---- this workgroup's (b, kv head) and segment: wave 0 finds the (b, kv head) whose run
+  // of segments holds this workgroup's index, by a prefix over the lists' segment counts
+  __shared__ int smap[4];
+  if (wv == 0) {
+    const int BH = a.B * a.Hkv;
+    const int per = segment_size(a, seg_total, lane);
+    const int wg = blockIdx.x;
+    int base = 0, fbk = -1, fseg = 0, fnt = 0;
+    for (int i0 = 0; i0 < BH; i0 += 64) {
+      const int i = i0 + lane;
+      const int nt = i < BH ? a.list[(size_t)i * a.list_ld] : 0;
+      const int ns = (nt + per - 1) / per;
+      int incl = ns;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += x;
+      }
+      const int excl = base + incl - ns;
+      const uint64_t hit = __ballot(i < BH && wg >= excl && wg < excl + ns);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        fbk = i0 + src;
+        fseg = wg - __shfl(excl, src, 64);
+        fnt = __shfl(nt, src, 64);
+        break;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      smap[0] = fbk;
+      smap[1] = fseg;
+      smap[2] = fnt;
+      smap[3] = per;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) *a.seg_size = smap[3];     // for the combine kernel
+  const int bk = smap[0];
+  if (bk < 0) return;                             // past the last segment (whole workgroup)
+  const int seg = smap[1];
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int t = a.seq_lens[b] - 1;
   if (t < 0 || t >= a.Tk) {                       // no valid query row: NaN outputs
@@ -313,12 +372,10 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   const int it = t / kChunk;
 
   // ---- this workgroup's segment of the route kernel's list (active chunks + the diagonal
-  // chunk): seg_target segments of at least kSeg items each
+  // chunk)
   const int32_t* lst = a.list + (size_t)bk * a.list_ld;
-  const int ntot = lst[0];
-  const int per = max(kSeg, (ntot + seg_target - 1) / seg_target);
-  const int nsegb = (ntot + per - 1) / per;
-  if (seg >= nsegb) return;                       // (whole workgroup)
+  const int ntot = smap[2];
+  const int per = smap[3];
   const int lo = seg * per;
   const int nitems = min(per, ntot - lo);
   // wave wv takes items lo + wv + kAttWaves j; lane j of myc holds the chunk of item j
@@ -536,7 +593,7 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
 template <int D>
 __global__ __launch_bounds__(256) void k_decode_combine(AttendArgs a, const float* __restrict__ pml,
                                                         const float* __restrict__ po, int nseg_max,
-                                                        int seg_target) {
+                                                        int seg_total) {
   constexpr int NT = 256, NSMAX = (kMaxRouted + 1 + kSeg) / kSeg + 1;
   constexpr int kPre = 16;                        // segments whose partials are loaded at once
   static_assert(2 * D <= NT, "one thread per (query column, 8 d)");
@@ -544,16 +601,15 @@ __global__ __launch_bounds__(256) void k_decode_combine(AttendArgs a, const floa
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x;
   const int bk = blockIdx.x, b = bk / a.Hkv, kvh = bk % a.Hkv;
-  const int t = a.seq_lens[b] - 1;
-  if (t < 0 || t >= a.Tk) return;                 // the attend kernel wrote NaN
   const size_t pbase = (size_t)bk * nseg_max;
-  // every load is issued before the segment count is known: the partials of up to kPre
-  // segments and the (max, sum) pairs of all seg_target, all inside the partial buffers;
-  // those of segments past the count are never used
+  // one round of loads: the sequence length, the list length, the segment size, and
+  // the partials and (max, sum) pairs of up to kPre segments before their count is known
+  // (all inside the partial buffers; those of segments past the count are never used)
+  const int t = a.seq_lens[b] - 1;
   const int q = tid / (D / 8), d0 = (tid % (D / 8)) * 8;
   const bool act = tid < 2 * D && q < G;
   const float* src = po + (pbase * 16 + (act ? q : 0)) * D + d0;
-  const int npre = min(seg_target, kPre);
+  const int npre = min(nseg_max, kPre);
   float4 u[kPre][2];
 #pragma unroll
   for (int s2 = 0; s2 < kPre; ++s2)
@@ -561,15 +617,24 @@ __global__ __launch_bounds__(256) void k_decode_combine(AttendArgs a, const floa
       u[s2][0] = *reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D);
       u[s2][1] = *reinterpret_cast<const float4*>(src + (size_t)s2 * 16 * D + 4);
     }
-  for (int i = tid; i < seg_target * 16; i += NT) {
+  for (int i = tid; i < npre * 16; i += NT) {
     const size_t pi = pbase + i / 16;
     fsm[i] = pml[pi * 32 + (i & 15)];
     fsl[i] = pml[pi * 32 + 16 + (i & 15)];
   }
-  const int ntot = a.list[(size_t)bk * a.list_ld];
-  const int per = max(kSeg, (ntot + seg_target - 1) / seg_target);
-  const int nsegb = (ntot + per - 1) / per;
+  const int nt = a.list[(size_t)bk * a.list_ld];
+  const int per = *a.seg_size;                    // written by the attend kernel
   __syncthreads();
+  if (t < 0 || t >= a.Tk) return;                 // the attend kernel wrote NaN
+  const int nsegb = (nt + per - 1) / per;
+  if (nsegb > npre) {                             // more segments than the first round held
+    for (int i = npre * 16 + tid; i < nsegb * 16; i += NT) {
+      const size_t pi = pbase + i / 16;
+      fsm[i] = pml[pi * 32 + (i & 15)];
+      fsl[i] = pml[pi * 32 + 16 + (i & 15)];
+    }
+    __syncthreads();
+  }
   if (tid < 16) {
     float mx = kNegBig;
     for (int s2 = 0; s2 < nsegb; ++s2) mx = fmaxf(mx, fsm[s2 * 16 + tid]);
@@ -647,18 +712,20 @@ static int attend_slots() {
 }
 
 hipError_t launch_decode_attend(const AttendArgs& a, float* pml, float* po, hipStream_t s) {
+  if (a.seg_size == nullptr || a.list == nullptr || pml == nullptr || po == nullptr)
+    return hipErrorInvalidValue;                  // workspace pieces the kernels write
   const int nseg = decode_nseg_max(a.nc);
   const int bh = a.B * a.Hkv;
-  // segments per (b, kv head): enough to occupy every slot once, never more than the
-  // partial buffers hold (each segment has at least kSeg items)
-  const int target = max(1, min(nseg, attend_slots() / bh));
-  dim3 grid(target, bh);
-  if (a.D == 128) k_decode_attend<128><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, target);
-  else k_decode_attend<64><<<grid, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, target);
+  // one workgroup per segment: as many as fill every slot once (at least one per (b, kv
+  // head)); the common segment size keeps every (b, kv head) within the partial buffers
+  // (each segment has at least kSeg items)
+  const int total = max(attend_slots(), bh);
+  if (a.D == 128) k_decode_attend<128><<<total, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, total);
+  else k_decode_attend<64><<<total, kAttWaves * 64, 0, s>>>(a, pml, po, nseg, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.D == 128) k_decode_combine<128><<<bh, 256, 0, s>>>(a, pml, po, nseg, target);
-  else k_decode_combine<64><<<bh, 256, 0, s>>>(a, pml, po, nseg, target);
+  if (a.D == 128) k_decode_combine<128><<<bh, 256, 0, s>>>(a, pml, po, nseg, total);
+  else k_decode_combine<64><<<bh, 256, 0, s>>>(a, pml, po, nseg, total);
   return hipGetLastError();
 }
 
