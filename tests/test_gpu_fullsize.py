@@ -95,6 +95,39 @@ def test_prefill_longest_sequence(dash):
     _prefill_bench_config(dash, w, rows)
 
 
+def test_decode_longest_sequence(dash):
+    """Decode at the longest supported sequence (2049 chunks, the last row routing over 2048):
+    the largest solver register set, and (with one sequence) more attend segments than the
+    combine kernel's first round of loads holds; equals the oracle's prefill row."""
+    T = 64 * 2049
+    w = Workload(name="dec_longest", kind="prefill", B=1, Hq=32, Hkv=2, T=T, D=128,
+                 dtype="bf16", seed=990, needle_amp=0.5)
+    x = synth.prefill_inputs(w)
+    say(f"[fullsize] decode at T = {T}")
+    k, v, hc = (to_dev(x[n], "bf16") for n in ("k", "v", "head_cls"))
+    nc = -(-T // 64)
+    summ = torch.zeros((1, 2, nc, 128), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for L in (T, T - 100):
+        lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+        summ.zero_()
+        nsum.zero_()
+        dash.append_chunk(k, hc, lens, summ, nsum, Hq=32, enable_gqa=True)
+        q = to_dev(x["q"][:, :, L - 1], "bf16").contiguous()
+        out, ab = dash.decode(q, k, v, lens, summ, enable_gqa=True, return_active_blocks=True)
+        torch.cuda.synchronize()
+        ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], rows=[L - 1])
+        e = compare_out(out.float().cpu().numpy()[0], ref["out"][0, :, 0], "bf16",
+                        what=f"decode at {L}")
+        bits = unpack_words(ab.cpu().numpy(), nc)
+        amb = compare_mask(bits[0][:, None], ref["mask"][0], ref["margin"][0], [L - 1])
+        act = bits[0].sum(axis=-1)                            # per kv head
+        say(f"[fullsize]   L={L}: out err {e:.2e}, near-threshold flips {amb}, "
+            f"active chunks {act.tolist()}")
+        if L == T:     # a list longer than 16 segments of 16 items
+            assert int(act.max()) + 1 > 16 * 16, act
+
+
 def test_decode_64k_all_steps_sampled(dash):
     """The 64K decode workload (B = 16, 32/2 heads): all 256 steps in order, appending a
     summary whenever a chunk fills; steps around the append are checked in full against the
