@@ -139,7 +139,7 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   const float* srow = a.sco + ((size_t)bk * G + (wv < G ? wv : 0)) * a.sco_ld;
 
   // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...; the
-  // register count follows the routed length
+  // register count follows the routed length (in steps of 128 chunks past 1024)
   auto solve = [&](auto nr_tag) {
     constexpr int NRU = decltype(nr_tag)::value;
     float y[NRU];
@@ -212,9 +212,13 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
     else if (it <= 512) solve(std::integral_constant<int, 8>{});
     else if (it <= 768) solve(std::integral_constant<int, 12>{});
     else if (it <= 1024) solve(std::integral_constant<int, 16>{});
+    else if (it <= 1152) solve(std::integral_constant<int, 18>{});
     else if (it <= 1280) solve(std::integral_constant<int, 20>{});
+    else if (it <= 1408) solve(std::integral_constant<int, 22>{});
     else if (it <= 1536) solve(std::integral_constant<int, 24>{});
+    else if (it <= 1664) solve(std::integral_constant<int, 26>{});
     else if (it <= 1792) solve(std::integral_constant<int, 28>{});
+    else if (it <= 1920) solve(std::integral_constant<int, 30>{});
     else solve(std::integral_constant<int, NR>{});
   }
   __syncthreads();
