@@ -52,7 +52,7 @@ __device__ __forceinline__ float xg_sum(float v) {
   return xg_reduce(v, [](float x, float y) { return x + y; });
 }
 
-constexpr int kSeg = 16;        // list items per attend workgroup
+constexpr int kSeg = 16;        // the fewest list items an attend segment (workgroup) takes
 // dword 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format, offsets in
 // bytes, bounds checked against the record count)
 constexpr int kBufferRsrcWord3 = 0x00020000;
