@@ -393,6 +393,36 @@ def test_decode_paged_matches_contiguous(dash):
         compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"paged decode b={b}")
 
 
+def test_decode_many_sequences(dash):
+    """More (b, kv head) pairs than attend workgroup slots (300 sequences of mixed lengths,
+    2 KV heads): every list is one segment; sampled sequences equal the oracle's rows."""
+    B, T = 300, 400
+    w = Workload(name="dec_many", kind="prefill", B=B, Hq=8, Hkv=2, T=T, D=128, dtype="bf16",
+                 seed=36, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say(f"[parity] decode with {B} sequences")
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    rng = np.random.default_rng(37)
+    lens = rng.integers(1, T + 1, size=B)
+    lens[:4] = [T, 1, 64, 129]
+    nc = -(-T // 64)
+    summ = torch.zeros((B, 2, nc, 128), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dash.append_chunk(k, hc, lens_t, summ, nsum, Hq=8, enable_gqa=True)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(B)]).contiguous()
+    out, ab = dash.decode(q, k, v, lens_t, summ, enable_gqa=True, return_active_blocks=True)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    bits = unpack_words(ab.cpu().numpy(), nc)
+    for b in list(range(4)) + list(rng.choice(np.arange(4, B), size=12, replace=False)):
+        t = int(lens[b]) - 1
+        ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                        rows=[t])
+        compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"decode b={b} len={t + 1}")
+        compare_mask(bits[b][:, None], ref["mask"][0], ref["margin"][0], [t])
+
+
 def test_decode_steps_with_append(dash):
     """Decode 100 consecutive steps from a 600-token prompt (GQA 4), appending each chunk
     as it fills; every step equals the oracle's prefill row of the full sequence."""
