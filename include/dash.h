@@ -22,7 +22,8 @@
  *   - Tensor pointers are DEVICE pointers unless stated; tensors are dense, row-major,
  *     with the shapes given below; they must be 16-byte aligned.  The caller owns all
  *     memory; the library never allocates device memory and keeps no state besides the
- *     loaded kernels and a thread-local error string.
+ *     loaded kernels, a thread-local error string and a per-device cache of the CU count
+ *     (read once, to size decode launches).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *     returns without waiting.  Arguments are validated on the host first; on any
  *     failure nothing is launched and a negative dash_status is returned, with a message
@@ -31,6 +32,9 @@
  *   - kv(h) = h / (Hq / Hkv): consecutive query heads share a KV head (enable_gqa).
  *   - Only complete chunks are summarised.  Row t routes over chunks c < t / C and always
  *     attends causally inside its own chunk with log-prior 0 (estimate_diagonal = 0).
+ *   - Beyond the method's defaults: a prior strength sigma, a top-k comparison router
+ *     (topk) in place of entmax, and paged K/V caches for decoding (dash_decode_paged,
+ *     dash_append_chunk_paged).
  */
 #ifndef DASH_H_
 #define DASH_H_
