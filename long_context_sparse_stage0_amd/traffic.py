@@ -3,16 +3,16 @@
 Run once under each of four rocprofv3 passes (one counter group per pass), then summarise:
 
     cd /tmp && export TMPDIR=/tmp && cd <repo>
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o fetch \\
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/traffic/fetch -o fetch \\
         -- python3 -m long_context_sparse_stage0_amd.traffic run
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o write \\
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/traffic/write -o write \\
         -- python3 -m long_context_sparse_stage0_amd.traffic run
-    rocprofv3 --kernel-trace --output-format csv -d gpurun_out/traffic/trace -o trace \\
+    rocprofv3 --kernel-trace --output-format csv -d <out>/traffic/trace -o trace \\
         -- python3 -m long_context_sparse_stage0_amd.traffic run
     rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE \\
-        --output-format csv -d gpurun_out/traffic/mfma -o mfma \\
+        --output-format csv -d <out>/traffic/mfma -o mfma \\
         -- python3 -m long_context_sparse_stage0_amd.traffic run
-    python3 -m long_context_sparse_stage0_amd.traffic summarize gpurun_out/traffic
+    python3 -m long_context_sparse_stage0_amd.traffic summarize <out>/traffic
 
 `run` launches, on the 128K prefill workload, the full prefill once (to build the mask and
 the weights), then Stage 2 alone three times; then, on the 64K decode workload, the bulk
@@ -159,11 +159,11 @@ def summarize(base):
         "",
         "Commands (repo root; rocprofv3 needs `cd /tmp && export TMPDIR=/tmp` first):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/traffic/fetch -o fetch "
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {base}/fetch -o fetch "
         "-- python3 -m long_context_sparse_stage0_amd.traffic run",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/traffic/write -o write "
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {base}/write -o write "
         "-- python3 -m long_context_sparse_stage0_amd.traffic run",
-        "    python3 -m long_context_sparse_stage0_amd.traffic summarize gpurun_out/traffic",
+        f"    python3 -m long_context_sparse_stage0_amd.traffic summarize {base}",
         "",
         f"Stage 2 source hash {doc['source_sha256_16']}.",
         "",
@@ -264,7 +264,7 @@ def report(base, factors):
         "that module's docstring (FETCH_SIZE; WRITE_SIZE; --kernel-trace; SQ_INSTS_VALU_MFMA_MOPS_BF16",
         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE), then",
         "",
-        "    python3 -m long_context_sparse_stage0_amd.traffic summarize gpurun_out/traffic",
+        f"    python3 -m long_context_sparse_stage0_amd.traffic summarize {base}",
         "",
         f"Counter bytes are scaled by the calibration copy (FETCH_SIZE x{factors['FETCH_SIZE']:.4f}, "
         f"WRITE_SIZE x{factors['WRITE_SIZE']:.4f}).  The run holds one full 128K prefill plus three",
