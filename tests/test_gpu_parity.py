@@ -423,6 +423,38 @@ def test_decode_many_sequences(dash):
         compare_mask(bits[b][:, None], ref["mask"][0], ref["margin"][0], [t])
 
 
+def test_decode_paged_with_options(dash):
+    """The options compose: paged caches with the top-k router, and with a prior strength
+    sigma != 1, give outputs and masks bit-identical to the contiguous caches."""
+    w = Workload(name="dec_paged_opts", kind="prefill", B=2, Hq=16, Hkv=2, T=2200, D=128,
+                 dtype="bf16", seed=965, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    say("[parity] paged decode with top-k and sigma")
+    B, Hkv, T, D = w.B, w.Hkv, w.T, w.D
+    lens = [2200, 1400]
+    k, v, hc = to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"), to_dev(x["head_cls"], "bf16")
+    nc = -(-T // 64)
+    rng = np.random.default_rng(966)
+    num_pages = B * nc + 3
+    perm = rng.permutation(num_pages)[:B * nc]
+    gen = torch.Generator().manual_seed(967)
+    kp, table = _page_pool(k, perm, num_pages, lens, gen)
+    vp, _ = _page_pool(v, perm, num_pages, lens, gen)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    summ = torch.zeros((B, Hkv, nc, D), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(B, dtype=torch.int32, device="cuda")
+    dash.append_chunk(k, hc, lens_t, summ, nsum, Hq=w.Hq, enable_gqa=True)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(B)]).contiguous()
+    for opts in (dict(topk=12), dict(sigma=0.5), dict(topk=5, sigma=2.0)):
+        o_c, a_c = dash.decode(q, k, v, lens_t, summ, enable_gqa=True, return_active_blocks=True,
+                               **opts)
+        o_p, a_p = dash.decode_paged(q, kp, vp, table, lens_t, summ, enable_gqa=True,
+                                     return_active_blocks=True, **opts)
+        torch.cuda.synchronize()
+        assert torch.equal(o_c, o_p), opts
+        assert torch.equal(a_c, a_p[..., :a_c.shape[-1]]), opts
+
+
 def test_decode_steps_with_append(dash):
     """Decode 100 consecutive steps from a 600-token prompt (GQA 4), appending each chunk
     as it fills; every step equals the oracle's prefill row of the full sequence."""
