@@ -239,18 +239,36 @@ def chunk_summaries(k: np.ndarray, head_cls: np.ndarray, scale: float,
 # Stage 1: routing of one row (all G heads of one KV head)
 # ---------------------------------------------------------------------------------------
 
+def diagonal_summary(k_head: np.ndarray, head_cls_vec: np.ndarray, t: int, scale: float,
+                     chunk: int = CHUNK) -> np.ndarray:
+    """Summary of the query's own, partial chunk: Stage 0's formula over its keys up to t
+    (keys i_t C .. t of one KV head; k_head [>= t+1, D])."""
+    it = t // chunk
+    kc = np.asarray(k_head[it * chunk: t + 1], np.float64)
+    a = scale * (kc @ np.asarray(head_cls_vec, np.float64))
+    return softmax(a) @ kc
+
+
 def route_row(q_group: np.ndarray, summ: np.ndarray, t: int, *, alpha: float,
-              gamma: float, scale: float, chunk: int = CHUNK):
+              gamma: float, scale: float, chunk: int = CHUNK,
+              diag: Optional[np.ndarray] = None):
     """q_group [G, D]: the G query heads of one KV head at row t; summ [>= t//C, D].
 
+    diag (estimate_diagonal): the summary of the query's own chunk, which then joins the
+    alpha-entmax normalisation as one more entry; only the routed chunks' weights are
+    returned (the own chunk stays attended with log-prior 0).
     Returns (w_bar [i_t], group_margin [i_t], p [G, i_t]) where i_t = t // C,
     group_margin_c = max_h (y_{h,c} - tau_h).  Empty arrays when i_t = 0."""
     it = t // chunk
     G = q_group.shape[0]
     if it == 0:
         return np.zeros(0), np.zeros(0), np.zeros((G, 0))
-    x = gamma * scale * (np.asarray(q_group, np.float64) @ np.asarray(summ[:it], np.float64).T)
+    keys = np.asarray(summ[:it], np.float64)
+    if diag is not None:
+        keys = np.concatenate([keys, np.asarray(diag, np.float64)[None, :]], axis=0)
+    x = gamma * scale * (np.asarray(q_group, np.float64) @ keys.T)
     p, tau, y = entmax(x, alpha, return_tau=True)
+    p, y = p[:, :it], y[:, :it]
     w_bar = p.mean(axis=0)
     margin = (y - tau[:, None]).max(axis=0)
     return w_bar, margin, p
@@ -307,11 +325,12 @@ def attend_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, w_bar: np.nd
 def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
             scale: Optional[float] = None, sigma: float = 1.0, chunk: int = CHUNK,
             rows: Optional[Sequence[int]] = None, summaries: Optional[np.ndarray] = None,
-            topk: int = 0) -> Dict[str, np.ndarray]:
+            topk: int = 0, estimate_diagonal: bool = False) -> Dict[str, np.ndarray]:
     """Causal prefill.  q [B, Hq, T, D]; k, v [B, Hkv, T, D]; head_cls [Hkv, D].
 
     kv(h) = h // (Hq / Hkv).  `rows` restricts the rows computed (all by default).
     topk > 0 routes with `route_row_topk` instead of entmax (margin: score - k-th score).
+    estimate_diagonal: the own chunk's partial summary joins each row's entmax.
     Returns out [B, Hq, R, D], w_bar [B, Hkv, R, n_c], margin [B, Hkv, R, n_c]
     (nan where c >= t // C), mask [B, Hkv, R, n_c] (w_bar > 0), rows [R], summaries."""
     B, Hq, T, D = q.shape
@@ -338,8 +357,10 @@ def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
                     wb, mg = route_row_topk(qg, summaries[b, kvh], t, k=topk, gamma=gamma,
                                             scale=scale, chunk=chunk)
                 else:
+                    dg = (diagonal_summary(kk, head_cls[kvh], t, scale, chunk)
+                          if estimate_diagonal else None)
                     wb, mg, _ = route_row(qg, summaries[b, kvh], t, alpha=alpha, gamma=gamma,
-                                          scale=scale, chunk=chunk)
+                                          scale=scale, chunk=chunk, diag=dg)
                 it = t // chunk
                 w_bar[b, kvh, r, :it] = wb
                 margin[b, kvh, r, :it] = mg
@@ -356,7 +377,7 @@ def prefill(q, k, v, head_cls, *, alpha: float = 1.5, gamma: float = 1.0,
 
 def prefill_dense_formulation(q, k, v, head_cls, *, alpha: float, gamma: float = 1.0,
                               scale: Optional[float] = None, sigma: float = 1.0,
-                              chunk: int = CHUNK) -> np.ndarray:
+                              chunk: int = CHUNK, estimate_diagonal: bool = False) -> np.ndarray:
     """Same result as `prefill(...)["out"]`, written as one masked softmax per head.
 
     Summaries by explicit loops, routing weights by the sorted-support entmax, and the
@@ -384,15 +405,23 @@ def prefill_dense_formulation(q, k, v, head_cls, *, alpha: float, gamma: float =
             for t in range(T):
                 it = t // chunk
                 if it > 0:
+                    keys = summ[:it]
+                    if estimate_diagonal:             # the own chunk's keys up to t, looped
+                        n = t + 1 - it * chunk
+                        a = np.array([scale * float(hc[kvh] @ k[b, kvh, it * chunk + j])
+                                      for j in range(n)])
+                        e = np.exp(a - a.max())
+                        dg = sum((e[j] / e.sum()) * k[b, kvh, it * chunk + j] for j in range(n))
+                        keys = np.vstack([keys, dg])
                     wsum = np.zeros(it)
                     for g in range(G):
-                        x = gamma * scale * (summ[:it] @ q[b, kvh * G + g, t])
+                        x = gamma * scale * (keys @ q[b, kvh * G + g, t])
                         if alpha == 2.0:
-                            wsum += sparsemax_sorted(x)
+                            wsum += sparsemax_sorted(x)[:it]
                         elif alpha == 1.5:
-                            wsum += entmax15_sorted(x)
+                            wsum += entmax15_sorted(x)[:it]
                         else:
-                            wsum += entmax_sorted_general(x, alpha)
+                            wsum += entmax_sorted_general(x, alpha)[:it]
                     wbar = wsum / G
                     for c in range(it):
                         if wbar[c] > 0.0:
@@ -424,7 +453,8 @@ def causal_attention(q, k, v, scale: Optional[float] = None) -> np.ndarray:
 
 def decode_step(q_step, k_cache, v_cache, seq_lens, summary_cache, *, alpha: float = 1.5,
                 gamma: float = 1.0, scale: Optional[float] = None, sigma: float = 1.0,
-                chunk: int = CHUNK) -> Dict[str, np.ndarray]:
+                chunk: int = CHUNK, head_cls: Optional[np.ndarray] = None,
+                estimate_diagonal: bool = False) -> Dict[str, np.ndarray]:
     """q_step [B, Hq, D]; caches [B, Hkv, T_max, D]; seq_lens [B] (tokens in the cache,
     the current one included); summary_cache [B, Hkv, >= n, D] holding at least the
     summaries of every complete chunk before the current one.
@@ -445,8 +475,10 @@ def decode_step(q_step, k_cache, v_cache, seq_lens, summary_cache, *, alpha: flo
         t = int(seq_lens[b]) - 1
         for kvh in range(Hkv):
             qg = np.asarray(q_step[b, kvh * G:(kvh + 1) * G], np.float64)
+            dg = (diagonal_summary(k_cache[b, kvh], head_cls[kvh], t, scale, chunk)
+                  if estimate_diagonal else None)
             wb, mg, _ = route_row(qg, summary_cache[b, kvh], t, alpha=alpha, gamma=gamma,
-                                  scale=scale, chunk=chunk)
+                                  scale=scale, chunk=chunk, diag=dg)
             it = t // chunk
             w_bar[b, kvh, :it] = wb
             margin[b, kvh, :it] = mg

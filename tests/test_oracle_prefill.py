@@ -211,3 +211,40 @@ def test_topk_with_every_chunk_is_dense_causal():
     for h in range(4):
         ref = O.causal_attention(q[0, h], k[0, h // 2], v[0, h // 2])
         np.testing.assert_allclose(out[0, h], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# estimate_diagonal: the own chunk's partial summary joins the entmax normalisation
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+@pytest.mark.parametrize("G", [1, 4])
+def test_estimate_diagonal_block_walk_equals_dense_formulation(alpha, G):
+    T, D = 300, 8
+    q, k, v, hc = _rand(1, 2 * G, 2, T, D, seed=int(alpha * 10) + G + 50, needle=2.0)
+    walk = O.prefill(q, k, v, hc, alpha=alpha, estimate_diagonal=True)
+    dense = O.prefill_dense_formulation(q, k, v, hc, alpha=alpha, estimate_diagonal=True)
+    np.testing.assert_allclose(walk["out"], dense, rtol=0, atol=1e-12)
+    plain = O.prefill(q, k, v, hc, alpha=alpha)
+    assert np.abs(walk["out"] - plain["out"]).max() > 1e-6      # the correction matters
+    np.testing.assert_array_equal(walk["out"][:, :, :64], plain["out"][:, :, :64])  # no routing
+
+
+def test_estimate_diagonal_weights_leave_room_for_the_diagonal():
+    """With the own chunk in the normalisation the routed weights of each head sum to
+    1 - p_diagonal, so their GQA mean sums to at most 1, and below 1 when the own chunk
+    keeps weight."""
+    q, k, v, hc = _rand(1, 8, 2, 500, 8, seed=61, needle=1.0)
+    r = O.prefill(q, k, v, hc, estimate_diagonal=True)
+    s = r["w_bar"].sum(axis=-1)[:, :, 64:]                     # rows that route
+    assert np.all(s <= 1.0 + 1e-12) and np.any(s < 1.0 - 1e-6)
+    r0 = O.prefill(q, k, v, hc)
+    np.testing.assert_allclose(r0["w_bar"].sum(axis=-1)[:, :, 64:], 1.0, atol=1e-12)
+
+
+def test_diagonal_summary_with_zero_query_is_the_mean_of_the_keys_so_far():
+    rng = np.random.default_rng(62)
+    k = rng.normal(size=(200, 6))
+    for t in (128, 130, 191):
+        dg = O.diagonal_summary(k, np.zeros(6), t, 0.5)
+        np.testing.assert_allclose(dg, k[128:t + 1].mean(axis=0), atol=1e-14)
