@@ -31,7 +31,7 @@
  *     synchronisation.
  *   - kv(h) = h / (Hq / Hkv): consecutive query heads share a KV head (enable_gqa).
  *   - Only complete chunks are summarised.  Row t routes over chunks c < t / C and always
- *     attends causally inside its own chunk with log-prior 0 (estimate_diagonal = 0).
+ *     attends causally inside its own chunk with log-prior 0.
  *   - Beyond the method's defaults: a prior strength sigma, a top-k comparison router
  *     (topk) in place of entmax, and paged K/V caches for decoding (dash_decode_paged,
  *     dash_append_chunk_paged).
@@ -70,7 +70,13 @@ typedef struct dash_params {
   float sm_scale;     /* logit scale of Stages 0-2; <= 0 selects 1/sqrt(D) */
   int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
-  int32_t estimate_diagonal; /* must be 0: the diagonal chunk is always kept at prior 1 */
+  int32_t estimate_diagonal; /* 0: the own (diagonal) chunk takes no part in routing.  1
+                         (fp32 dash_prefill only, T <= 64 * 2048; else DASH_ERR_UNSUPPORTED):
+                         the own chunk is summarised by Stage 0's formula over its keys up to
+                         the query and joins each head's alpha-entmax normalisation as one more
+                         entry (aiexpert.news, interface paragraph: a diagonal correction of
+                         the normalisation); its weight is then dropped and the routed chunks
+                         keep theirs.  The own chunk is attended at prior 1 either way */
   float sigma;        /* prior strength, finite >= 0: keys of a routed chunk c get the logit
                          bias sigma * log w_bar_c.  1 is the prior itself, 0 a uniform prior
                          over the active chunks (gist.science, "Stufe 2": a hyperparameter

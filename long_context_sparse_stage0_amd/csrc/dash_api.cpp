@@ -67,8 +67,6 @@ int check_params(const dash_params* p, Dims* d, bool need_bf16 = false) {
   if (!(p->sigma >= 0.0f) || !std::isfinite(p->sigma))
     return fail(DASH_ERR_INVALID_ARG, "sigma (prior strength) must be finite and >= 0");
   if (!std::isfinite(p->sm_scale)) return fail(DASH_ERR_INVALID_ARG, "sm_scale is not finite");
-  if (p->estimate_diagonal != 0)
-    return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is not built");
   if (p->T > kMaxT)
     return fail(DASH_ERR_UNSUPPORTED, "T=%d exceeds %d (at most %d routed chunks per row)", p->T,
                 kMaxT, dash::kMaxRouted);
@@ -202,6 +200,13 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   if (int rc = check_params(p, &d)) return rc;
   if (p->topk > 0 && d.dtype != DASH_BF16)
     return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
+  if (p->estimate_diagonal != 0) {
+    if (d.dtype != DASH_FP32 || p->topk > 0)
+      return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is built for the fp32 entmax router only");
+    if (d.T > dash::kChunk * dash::kMaxRouted)
+      return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1: T=%d exceeds %d", d.T,
+                  dash::kChunk * dash::kMaxRouted);
+  }
   if (int rc = check_ptr(q, "q")) return rc;
   if (int rc = check_ptr(k, "k")) return rc;
   if (int rc = check_ptr(v, "v")) return rc;
@@ -255,6 +260,12 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
   ra.topk = p->topk;
   ra.dtype = d.dtype;
+  if (p->estimate_diagonal != 0) {
+    ra.kdiag = k;
+    ra.head_cls = head_cls;
+    ra.kdiag_ld = d.T;
+    ra.s0_scale_log2 = d.scale * 1.4426950408889634f;
+  }
   if (stages & 2) {
     if (d.dtype == DASH_BF16)
       e = dash::launch_route_mfma(ra, ws + L.ssplit, s);
@@ -334,6 +345,8 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
   if (int rc = check_params(p, &d)) return rc;
   if (p->topk > 0 && d.dtype != DASH_BF16)
     return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
+  if (p->estimate_diagonal != 0)
+    return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is built for prefill only");
   if (block_table) {
     if (d.dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "paged caches are bf16 only");
     if (num_pages <= 0) return fail(DASH_ERR_INVALID_ARG, "num_pages must be positive");

@@ -84,6 +84,10 @@ struct RouteArgs {
   int list_ld;            // increasing order followed by the diagonal chunk (or nullptr)
   float* sco;             // decode: [B * Hkv][G][sco_ld] scaled scores (or nullptr)
   int sco_ld;
+  const void* kdiag;      // estimate_diagonal (generic router): keys [B, Hkv, kdiag_ld, D]
+  const void* head_cls;   // and head_cls [Hkv, D] for the own chunk's summary, or nullptr
+  int kdiag_ld;
+  float s0_scale_log2;    // Stage 0 logit scale * log2(e)
 };
 
 struct AttendArgs {

@@ -11,7 +11,9 @@
 // Method: gist.science summary of arXiv 2605.18753, "Stufe 1: Entmax-Chunk-Routing"
 // (w_hat = alpha-entmax(gamma z_bar); in GQA the probabilities of the heads that share a
 // KV head are averaged into one shared sparse support); aixai.ru blog,
-// "Трёхстадийная архитектура" (mask packed in 64-bit words).
+// "Трёхстадийная архитектура" (mask packed in 64-bit words).  estimate_diagonal follows the
+// aiexpert.news interface paragraph (a diagonal correction of the entmax normalisation),
+// read as the own chunk's partial summary joining each head's normalisation.
 #include "route_common.h"
 
 namespace dash {
@@ -21,6 +23,7 @@ __global__ __launch_bounds__(1024) void k_route_valu(RouteArgs a) {
   constexpr int NR = kMaxRoutedRegs;
   __shared__ float qs[16][D];
   __shared__ float wsum[kMaxRouted];
+  __shared__ float kdg[D];
   const int G = a.Hq / a.Hkv;
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int row = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -36,7 +39,38 @@ __global__ __launch_bounds__(1024) void k_route_valu(RouteArgs a) {
   const TIn* qp = (const TIn*)a.q + ((size_t)(b * a.Hq + h) * a.Tq + tq) * D;
   for (int d = lane; d < D; d += 64) qs[g][d] = to_f32(qp[d]);
   for (int c = threadIdx.x; c < kMaxRouted; c += blockDim.x) wsum[c] = 0.f;
+  // estimate_diagonal: the own chunk (keys i_t C .. t) gets a summary by Stage 0's formula
+  // over the keys seen so far and joins the normalisation as entry i_t.  Wave 0 builds it:
+  // lane j scores key j against head_cls, softmax across lanes, then lane l accumulates
+  // columns l, l + 64, ... over the keys (coalesced row reads).
+  const bool diag = a.kdiag != nullptr && valid && it > 0 && it < NR * 64;
+  if (diag && g == 0) {
+    const TIn* kb =
+        (const TIn*)a.kdiag + ((size_t)(b * a.Hkv + kvh) * a.kdiag_ld + (size_t)it * kChunk) * D;
+    const TIn* hc = (const TIn*)a.head_cls + (size_t)kvh * D;
+    const int nk = t - it * kChunk + 1;
+    float lg = -INFINITY;
+    if (lane < nk) {
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(to_f32(hc[d]), to_f32(kb[(size_t)lane * D + d]), acc);
+      lg = acc * a.s0_scale_log2;
+    }
+    const float m = wave_max(lg);
+    const float e = lane < nk ? fast_exp2(lg - m) : 0.f;
+    const float pj = e / wave_sum(e);
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+      for (int j = 0; j < nk; ++j) acc = fmaf(__shfl(pj, j), to_f32(kb[(size_t)j * D + d]), acc);
+      kdg[d] = acc;
+    }
+  }
   __syncthreads();
+  float ydiag = -INFINITY;
+  if (diag) {
+    float acc = 0.f;
+    for (int d = lane; d < D; d += 64) acc = fmaf(qs[g][d], kdg[d], acc);
+    ydiag = a.zscale * wave_sum(acc);
+  }
 
   float y[NR];
   const float* sb = a.summ + (size_t)(b * a.Hkv + kvh) * a.nc_alloc * D;
@@ -56,12 +90,14 @@ __global__ __launch_bounds__(1024) void k_route_valu(RouteArgs a) {
         acc = fmaf(qs[g][4 * d4 + 3], s4.w, acc);
       }
       y[r] = a.zscale * acc;
+    } else if (c == it && diag) {
+      y[r] = ydiag;
     }
   }
   float p[NR];
   if (it > 0) {
     float z;
-    const float tau = entmax_threshold<MODE, NR>(y, it, a.alpha, WaveReduce(), &z);
+    const float tau = entmax_threshold<MODE, NR>(y, diag ? it + 1 : it, a.alpha, WaveReduce(), &z);
     const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
 #pragma unroll
     for (int r = 0; r < NR; ++r) p[r] = entmax_weight<MODE>(y[r], tau, inv, rz);
@@ -69,7 +105,8 @@ __global__ __launch_bounds__(1024) void k_route_valu(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) p[r] = 0.f;
   }
-  // fixed-order sum over the G heads
+  // fixed-order sum over the G heads (the own chunk's weight, at c = i_t, is dropped below:
+  // it stays attended with log-prior 0)
   for (int gg = 0; gg < G; ++gg) {
     if (g == gg) {
 #pragma unroll

@@ -69,7 +69,6 @@ def _ws(p):
     (dict(T=-5), -1),
     (dict(B=0), -1),
     (dict(dtype=7), -3),
-    (dict(estimate_diagonal=1), -4),
     (dict(sigma=-0.5), -1),
     (dict(sigma=float("nan")), -1),
     (dict(sigma=float("inf")), -1),
@@ -151,6 +150,14 @@ def test_decode_append_dense_validation():
                            1 << 30, None) == -4
     assert lib.dash_prefill(ctypes.byref(_params(dtype=1, topk=8)), FAKE, FAKE, FAKE, FAKE,
                             FAKE, None, None, None, FAKE, 1 << 30, None) == -4
+    # estimate_diagonal: the fp32 entmax prefill only, at most 2048 chunks per sequence
+    for kw in (dict(dtype=0), dict(dtype=1, topk=4), dict(dtype=1, T=64 * 2048 + 1)):
+        pe = _params(estimate_diagonal=1, **kw)
+        assert lib.dash_prefill(ctypes.byref(pe), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                None, FAKE, 1 << 40, None) == -4, kw
+    pe = _params(estimate_diagonal=1, dtype=1)
+    assert lib.dash_decode(ctypes.byref(pe), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                           1 << 30, None) == -4
     # the dense comparator is bf16 only
     pf = _params(dtype=1)
     assert lib.dash_dense_causal_workspace_size(ctypes.byref(pf), ctypes.byref(n)) == -3

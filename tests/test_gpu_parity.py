@@ -26,19 +26,21 @@ def dash():
     return d
 
 
-def run_prefill(dash, w: Workload, rows=None, alpha=None, sigma=1.0, topk=0):
+def run_prefill(dash, w: Workload, rows=None, alpha=None, sigma=1.0, topk=0,
+                estimate_diagonal=False):
     alpha = w.alpha if alpha is None else alpha
     x = synth.prefill_inputs(w)
     say(f"[parity] prefill {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} "
-        f"{w.dtype} alpha={alpha} sigma={sigma}")
+        f"{w.dtype} alpha={alpha} sigma={sigma} topk={topk} diag={estimate_diagonal}")
     q, k, v, hc = (to_dev(x[n], w.dtype) for n in ("q", "k", "v", "head_cls"))
     out, ab, bw, sm = dash.prefill(q, k, v, hc, alpha=alpha, gamma=w.gamma, sigma=sigma, topk=topk,
+                                   estimate_diagonal=estimate_diagonal,
                                    enable_gqa=w.enable_gqa, return_active_blocks=True,
                                    return_block_weights=True, return_summaries=True)
     torch.cuda.synchronize()
     rows = np.arange(w.T) if rows is None else np.asarray(rows)
     ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=alpha, gamma=w.gamma,
-                    sigma=sigma, rows=rows, topk=topk)
+                    sigma=sigma, rows=rows, topk=topk, estimate_diagonal=estimate_diagonal)
     nc = -(-w.T // 64)
     g_out = out.float().cpu().numpy()[:, :, rows]
     g_bits = unpack_words(ab.cpu().numpy(), nc)[:, :, rows]
@@ -85,6 +87,22 @@ def test_prefill_prior_strength(dash, dtype, sigma):
     w = Workload(name=f"sigma_{dtype}", kind="prefill", B=1, Hq=8, Hkv=2, T=900, D=128,
                  dtype=dtype, seed=950, needle_amp=1.0)
     check_prefill(run_prefill(dash, w, sigma=sigma), w)
+
+
+@pytest.mark.parametrize("G,alpha,T,D", [
+    (4, 1.5, 1000, 128),     # ragged tail
+    (1, 2.0, 520, 64),
+    (16, 1.25, 700, 128),
+])
+def test_prefill_estimate_diagonal(dash, G, alpha, T, D):
+    """estimate_diagonal: the own chunk's partial summary joins each row's entmax (fp32
+    router); only the routed chunks' weights are kept."""
+    w = Workload(name=f"diag_g{G}", kind="prefill", B=1, Hq=2 * G, Hkv=2, T=T, D=D,
+                 dtype="fp32", alpha=alpha, seed=970 + G, needle_amp=1.0)
+    r = run_prefill(dash, w, estimate_diagonal=True)
+    check_prefill(r, w)
+    plain = run_prefill(dash, w, rows=r["rows"])
+    assert np.abs(r["w"] - plain["w"]).max() > 1e-2    # the flag changes the weights
 
 
 def test_decode_prior_strength(dash):
