@@ -71,7 +71,8 @@ typedef struct dash_params {
   int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
   int32_t estimate_diagonal; /* 0: the own (diagonal) chunk takes no part in routing.  1
-                         (fp32 dash_prefill only, T <= 64 * 2048; else DASH_ERR_UNSUPPORTED):
+                         (dash_prefill with entmax routing, T <= 64 * 2048; decode and top-k
+                         return DASH_ERR_UNSUPPORTED; Stage 1 then runs on the generic router):
                          the own chunk is summarised by Stage 0's formula over its keys up to
                          the query and joins each head's alpha-entmax normalisation as one more
                          entry (aiexpert.news, interface paragraph: a diagonal correction of

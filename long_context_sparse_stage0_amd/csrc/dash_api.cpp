@@ -201,8 +201,8 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   if (p->topk > 0 && d.dtype != DASH_BF16)
     return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
   if (p->estimate_diagonal != 0) {
-    if (d.dtype != DASH_FP32 || p->topk > 0)
-      return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is built for the fp32 entmax router only");
+    if (p->topk > 0)
+      return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 applies to the entmax router only");
     if (d.T > dash::kChunk * dash::kMaxRouted)
       return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1: T=%d exceeds %d", d.T,
                   dash::kChunk * dash::kMaxRouted);
@@ -267,7 +267,9 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
     ra.s0_scale_log2 = d.scale * 1.4426950408889634f;
   }
   if (stages & 2) {
-    if (d.dtype == DASH_BF16)
+    // estimate_diagonal runs on the generic router for either dtype: it writes the same mask
+    // and weight layout that the MFMA Stage 2 reads
+    if (d.dtype == DASH_BF16 && p->estimate_diagonal == 0)
       e = dash::launch_route_mfma(ra, ws + L.ssplit, s);
     else
       e = dash::launch_route_valu(ra, s);

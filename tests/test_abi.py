@@ -150,8 +150,8 @@ def test_decode_append_dense_validation():
                            1 << 30, None) == -4
     assert lib.dash_prefill(ctypes.byref(_params(dtype=1, topk=8)), FAKE, FAKE, FAKE, FAKE,
                             FAKE, None, None, None, FAKE, 1 << 30, None) == -4
-    # estimate_diagonal: the fp32 entmax prefill only, at most 2048 chunks per sequence
-    for kw in (dict(dtype=0), dict(dtype=1, topk=4), dict(dtype=1, T=64 * 2048 + 1)):
+    # estimate_diagonal: entmax prefill only, at most 2048 chunks per sequence
+    for kw in (dict(dtype=0, topk=4), dict(dtype=1, T=64 * 2048 + 1), dict(dtype=0, T=64 * 2049)):
         pe = _params(estimate_diagonal=1, **kw)
         assert lib.dash_prefill(ctypes.byref(pe), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                 None, FAKE, 1 << 40, None) == -4, kw

@@ -89,16 +89,19 @@ def test_prefill_prior_strength(dash, dtype, sigma):
     check_prefill(run_prefill(dash, w, sigma=sigma), w)
 
 
-@pytest.mark.parametrize("G,alpha,T,D", [
-    (4, 1.5, 1000, 128),     # ragged tail
-    (1, 2.0, 520, 64),
-    (16, 1.25, 700, 128),
+@pytest.mark.parametrize("dtype,G,alpha,T,D", [
+    ("fp32", 4, 1.5, 1000, 128),     # ragged tail
+    ("fp32", 1, 2.0, 520, 64),
+    ("fp32", 16, 1.25, 700, 128),
+    ("bf16", 16, 1.5, 1000, 128),    # generic router feeding the MFMA Stage 2
+    ("bf16", 2, 2.0, 450, 64),
 ])
-def test_prefill_estimate_diagonal(dash, G, alpha, T, D):
-    """estimate_diagonal: the own chunk's partial summary joins each row's entmax (fp32
-    router); only the routed chunks' weights are kept."""
-    w = Workload(name=f"diag_g{G}", kind="prefill", B=1, Hq=2 * G, Hkv=2, T=T, D=D,
-                 dtype="fp32", alpha=alpha, seed=970 + G, needle_amp=1.0)
+def test_prefill_estimate_diagonal(dash, dtype, G, alpha, T, D):
+    """estimate_diagonal: the own chunk's partial summary joins each row's entmax; only the
+    routed chunks' weights are kept."""
+    w = Workload(name=f"diag_{dtype}_g{G}", kind="prefill", B=2 if dtype == "bf16" else 1,
+                 Hq=2 * G, Hkv=2, T=T, D=D, dtype=dtype, alpha=alpha, seed=970 + G,
+                 needle_amp=1.0)
     r = run_prefill(dash, w, estimate_diagonal=True)
     check_prefill(r, w)
     plain = run_prefill(dash, w, rows=r["rows"])
