@@ -71,8 +71,9 @@ typedef struct dash_params {
   int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
   int32_t estimate_diagonal; /* 0: the own (diagonal) chunk takes no part in routing.  1
-                         (dash_prefill with entmax routing, T <= 64 * 2048; decode and top-k
-                         return DASH_ERR_UNSUPPORTED; Stage 1 then runs on the generic router):
+                         (dash_prefill and dash_decode_diag with entmax routing, T <= 64 *
+                         2048; elsewhere DASH_ERR_UNSUPPORTED; bf16 prefill then runs Stage 1
+                         on the generic router):
                          the own chunk is summarised by Stage 0's formula over its keys up to
                          the query and joins each head's alpha-entmax normalisation as one more
                          entry (aiexpert.news, interface paragraph: a diagonal correction of
@@ -148,6 +149,18 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* seq_lens, const float* summary_cache,
                 void* out, uint64_t* active_blocks, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* dash_decode with the KV heads' head_cls [Hkv, D] (dtype, device), which
+ * estimate_diagonal = 1 needs: the own chunk of the query at t is summarised over its keys
+ * i_t C .. t of k_cache (Stage 0's formula) and joins each head's alpha-entmax
+ * normalisation (aiexpert.news, interface paragraph), exactly as in dash_prefill.  With
+ * estimate_diagonal = 0 it equals dash_decode.  Errors as dash_decode; a NULL head_cls with
+ * the flag set is DASH_ERR_INVALID_ARG, the flag with topk > 0 or T_max > 64 * 2048 is
+ * DASH_ERR_UNSUPPORTED (as is the flag in dash_decode and dash_decode_paged). */
+int dash_decode_diag(const dash_params* p, const void* q, const void* k_cache,
+                     const void* v_cache, const void* head_cls, const int32_t* seq_lens,
+                     const float* summary_cache, void* out, uint64_t* active_blocks,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Chunk-summary cache append.  A summary, once its chunk is complete, is frozen and

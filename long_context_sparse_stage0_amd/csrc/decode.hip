@@ -138,6 +138,44 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   const int it = valid ? t / kChunk : 0;
   const float* srow = a.sco + ((size_t)bk * G + (wv < G ? wv : 0)) * a.sco_ld;
 
+  // estimate_diagonal: the own chunk's summary over its keys i_t C .. t (Stage 0's formula),
+  // built by wave 0 (lane j scores key j, softmax across lanes, lane l accumulates columns
+  // l, l + 64, ...); every head then scores it as routed entry i_t, which joins the
+  // threshold but never the mask, the weights or the work list
+  __shared__ float kdg[D];
+  const bool diag = a.kdiag != nullptr && MODE != kTopK && it > 0 && it < kMaxRouted;
+  float ydiag = -INFINITY;
+  if (diag) {
+    const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+    if (wv == 0) {
+      const bf16* kb = (const bf16*)a.kdiag + ((size_t)bk * a.kdiag_ld + (size_t)it * kChunk) * D;
+      const bf16* hc = (const bf16*)a.head_cls + (size_t)kvh * D;
+      const int nk = t - it * kChunk + 1;
+      float lg = -INFINITY;
+      if (lane < nk) {
+        float acc = 0.f;
+        for (int d = 0; d < D; ++d) acc = fmaf((float)hc[d], (float)kb[(size_t)lane * D + d], acc);
+        lg = acc * a.s0_scale_log2;
+      }
+      const float m = wave_max(lg);
+      const float e = lane < nk ? fast_exp2(lg - m) : 0.f;
+      const float pj = e / wave_sum(e);
+      for (int d = lane; d < D; d += 64) {
+        float acc = 0.f;
+        for (int j = 0; j < nk; ++j) acc = fmaf(__shfl(pj, j), (float)kb[(size_t)j * D + d], acc);
+        kdg[d] = acc;
+      }
+    }
+    __syncthreads();
+    if (wv < G) {
+      const bf16* qh = (const bf16*)a.q + (size_t)(b * a.Hq + kvh * G + wv) * D;
+      float acc = 0.f;
+      for (int d = lane; d < D; d += 64) acc = fmaf((float)qh[d], kdg[d], acc);
+      ydiag = a.zscale * wave_sum(acc);
+    }
+  }
+  const int nent = diag ? it + 1 : it;   // entries of the normalisation
+
   // per-head threshold: wave g owns head g, lane l holds chunks l, l + 64, ...; the
   // register count follows the routed length (in steps of 128 chunks past 1024)
   auto solve = [&](auto nr_tag) {
@@ -195,10 +233,10 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
-      y[r] = c < it ? srow[c] : -INFINITY;
+      y[r] = c < it ? srow[c] : (c == it ? ydiag : -INFINITY);
     }
     float z;
-    const float tau = entmax_threshold<MODE, NRU>(y, it, a.alpha, WaveReduce(), &z);
+    const float tau = entmax_threshold<MODE, NRU>(y, nent, a.alpha, WaveReduce(), &z);
     const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
 #pragma unroll
     for (int r = 0; r < NRU; ++r) {
@@ -208,17 +246,17 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
     }
   };
   if ((MODE == kTopK ? wv == 0 : wv < G) && it > 0) {
-    if (it <= 256) solve(std::integral_constant<int, 4>{});
-    else if (it <= 512) solve(std::integral_constant<int, 8>{});
-    else if (it <= 768) solve(std::integral_constant<int, 12>{});
-    else if (it <= 1024) solve(std::integral_constant<int, 16>{});
-    else if (it <= 1152) solve(std::integral_constant<int, 18>{});
-    else if (it <= 1280) solve(std::integral_constant<int, 20>{});
-    else if (it <= 1408) solve(std::integral_constant<int, 22>{});
-    else if (it <= 1536) solve(std::integral_constant<int, 24>{});
-    else if (it <= 1664) solve(std::integral_constant<int, 26>{});
-    else if (it <= 1792) solve(std::integral_constant<int, 28>{});
-    else if (it <= 1920) solve(std::integral_constant<int, 30>{});
+    if (nent <= 256) solve(std::integral_constant<int, 4>{});
+    else if (nent <= 512) solve(std::integral_constant<int, 8>{});
+    else if (nent <= 768) solve(std::integral_constant<int, 12>{});
+    else if (nent <= 1024) solve(std::integral_constant<int, 16>{});
+    else if (nent <= 1152) solve(std::integral_constant<int, 18>{});
+    else if (nent <= 1280) solve(std::integral_constant<int, 20>{});
+    else if (nent <= 1408) solve(std::integral_constant<int, 22>{});
+    else if (nent <= 1536) solve(std::integral_constant<int, 24>{});
+    else if (nent <= 1664) solve(std::integral_constant<int, 26>{});
+    else if (nent <= 1792) solve(std::integral_constant<int, 28>{});
+    else if (nent <= 1920) solve(std::integral_constant<int, 30>{});
     else solve(std::integral_constant<int, NR>{});
   }
   __syncthreads();

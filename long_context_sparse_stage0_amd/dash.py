@@ -29,7 +29,7 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 EXPORTS = [
     "dash_abi_version", "dash_last_error",
     "dash_prefill_workspace_size", "dash_prefill", "dash_prefill_stage",
-    "dash_decode_workspace_size", "dash_decode",
+    "dash_decode_workspace_size", "dash_decode", "dash_decode_diag",
     "dash_append_chunk", "dash_decode_paged", "dash_append_chunk_paged",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
 ]
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_prefill_stage.restype = ctypes.c_int
     lib.dash_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_decode.restype = ctypes.c_int
+    lib.dash_decode_diag.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_decode_diag.restype = ctypes.c_int
     lib.dash_append_chunk.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.dash_append_chunk.restype = ctypes.c_int
     i32 = ctypes.c_int32
@@ -182,14 +184,16 @@ def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=
 
 def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha=1.5,
            gamma=1.0, sm_scale=None, sigma=1.0, topk=0, enable_gqa=False,
+           estimate_diagonal=False, head_cls=None,
            return_active_blocks=False, out=None, workspace=None, stream=None):
     """One decode step.  q [B,Hq,D]; caches [B,Hkv,T_max,D]; seq_lens [B] int32 (device);
-    summary_cache [B,Hkv,ceil(T_max/64),D] fp32."""
+    summary_cache [B,Hkv,ceil(T_max/64),D] fp32.  estimate_diagonal needs head_cls [Hkv,D]
+    (dash_decode_diag)."""
     B, Hq, D = q.shape
     Hkv, T_max = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
                     sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma,
-                    topk=topk)
+                    topk=topk, estimate_diagonal=estimate_diagonal)
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     nc = -(-T_max // 64)
@@ -199,9 +203,15 @@ def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha
     ab = torch.empty((B, Hkv, W), dtype=torch.int64, device=q.device) if return_active_blocks else None
     if workspace is None:
         workspace = alloc_workspace(workspace_size("decode", p), q.device)
-    _check(load().dash_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                              _ptr(seq_lens), _ptr(summary_cache), _ptr(out), _ptr(ab),
-                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    if head_cls is not None:
+        _check(load().dash_decode_diag(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(head_cls), _ptr(seq_lens), _ptr(summary_cache),
+                                       _ptr(out), _ptr(ab), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+    else:
+        _check(load().dash_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(seq_lens), _ptr(summary_cache), _ptr(out), _ptr(ab),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return (out, ab) if return_active_blocks else out
 
 

@@ -131,6 +131,40 @@ def test_decode_prior_strength(dash):
         compare_out(g[b], ref["out"][0, :, 0], "bf16", what=f"decode sigma b={b}")
 
 
+@pytest.mark.parametrize("dtype,G,alpha", [("bf16", 16, 1.5), ("bf16", 4, 2.0), ("fp32", 8, 1.5)])
+def test_decode_estimate_diagonal(dash, dtype, G, alpha):
+    """dash_decode_diag with estimate_diagonal: each decode row equals the oracle's prefill
+    row with the flag (mask bits outside the margin, outputs); lengths mid-chunk, at a chunk
+    boundary, one past it, and in the first chunk."""
+    T = 1500
+    w = Workload(name=f"dec_diag_{dtype}", kind="prefill", B=4, Hq=2 * G, Hkv=2, T=T, D=128,
+                 dtype=dtype, seed=960 + G, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    lens = [1500, 1024, 1025, 40]
+    say(f"[parity] decode estimate_diagonal {dtype} G={G} alpha={alpha} lens={lens}")
+    k, v, hc = (to_dev(x[n], dtype) for n in ("k", "v", "head_cls"))
+    nc = -(-T // 64)
+    summ = torch.zeros((4, 2, nc, 128), dtype=torch.float32, device="cuda")
+    nsum = torch.zeros(4, dtype=torch.int32, device="cuda")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dash.append_chunk(k, hc, lens_t, summ, nsum, Hq=2 * G, enable_gqa=True)
+    q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], dtype) for b in range(4)]).contiguous()
+    out, ab = dash.decode(q, k, v, lens_t, summ, alpha=alpha, enable_gqa=True,
+                          estimate_diagonal=True, head_cls=hc, return_active_blocks=True)
+    plain = dash.decode(q, k, v, lens_t, summ, alpha=alpha, enable_gqa=True)
+    torch.cuda.synchronize()
+    g, bits = out.float().cpu().numpy(), unpack_words(ab.cpu().numpy(), nc)
+    moved = 0.0
+    for b in range(4):
+        t = lens[b] - 1
+        ref = O.prefill(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], x["head_cls"],
+                        alpha=alpha, rows=[t], estimate_diagonal=True)
+        compare_out(g[b], ref["out"][0, :, 0], dtype, what=f"decode diag b={b}")
+        compare_mask(bits[b][None, :, None, :], ref["mask"], ref["margin"], [t])
+        moved = max(moved, float((out[b].float() - plain[b].float()).abs().max()))
+    assert moved > 1e-5        # the flag reaches the kernels (same inputs, deterministic)
+
+
 @pytest.mark.parametrize("G,k,T,rows", [
     (16, 8, 2000, list(range(0, 2000, 7)) + [1999]),   # the 128K workload's head ratio
     (4, 1, 1100, None),                                 # argmax routing, every row
