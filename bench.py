@@ -13,6 +13,7 @@ Prints ONE JSON line on stdout:
   dense      a dense causal flash-style kernel on the same inputs (the pages' comparator);
   topk_router  the same prefill with a top-k comparison router (k = entmax's mean active
              chunks per row) in place of entmax: Stage 1 and Stage 2 times;
+  estimate_diagonal  the same prefill with the own chunk's partial summary in the entmax;
   cpu_baseline  the float64 oracle timed on host cores over a bounded sample of rows.
 Progress lines go to stderr.
 """
@@ -190,6 +191,30 @@ def bench_prefill(args, w, dash, torch):
                        "entmax_stage1_ms": st[1], "entmax_active_fraction": 1.0 - zero_frac}
         log(f"top-k router (k={k_match}): stage 1 {stk[1]:.2f} ms (entmax {st[1]:.2f}), "
             f"stage 2 {stk[2]:.2f} ms, active {res['topk']['active_fraction']:.3f}")
+
+    if not args.no_diag:
+        # estimate_diagonal: the own chunk's partial summary in every head's entmax
+        dash.prefill_stage(1, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                           enable_gqa=True, estimate_diagonal=True, active_blocks=ab)
+        torch.cuda.synchronize()
+        act_d = float(popcount64(ab).sum())
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(-1, args.steps):
+            if i >= 0:
+                evd[i][0].record()
+            for s in range(3):
+                dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
+                                   enable_gqa=True, estimate_diagonal=True)
+                if i >= 0:
+                    evd[i][s + 1].record()
+        torch.cuda.synchronize()
+        sd = [float(np.mean([evd[i][s].elapsed_time(evd[i][s + 1]) for i in range(args.steps)]))
+              for s in range(3)]
+        res["diag"] = {"stage1_ms": sd[1], "stage2_ms": sd[2], "prefill_ms": sum(sd),
+                       "active_fraction": act_d / float(routed.sum() * B * Hkv),
+                       "without_flag_stage1_ms": st[1]}
+        log(f"estimate_diagonal: stage 1 {sd[1]:.2f} ms (without {st[1]:.2f}), "
+            f"stage 2 {sd[2]:.2f} ms, active {res['diag']['active_fraction']:.3f}")
 
     if not args.no_dense:
         pd = dash.make_params(B, Hq, Hkv, T, D, enable_gqa=True, dtype=torch.bfloat16)
@@ -485,6 +510,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true",
                     help="skip timing the top-k comparison router")
+    ap.add_argument("--no-diag", action="store_true",
+                    help="skip timing the prefill with estimate_diagonal")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--short", action="store_true",
                     help="report entmax / top-k / dense at T = 2K..16K (one JSON line per T)")
@@ -529,6 +556,7 @@ def main():
         "stage1": pre["stage1"],
         "dense": pre.get("dense"),
         "topk_router": pre.get("topk"),
+        "estimate_diagonal": pre.get("diag"),
         "decode": dec,
     }
     print(json.dumps(line), flush=True)

@@ -72,8 +72,7 @@ typedef struct dash_params {
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
   int32_t estimate_diagonal; /* 0: the own (diagonal) chunk takes no part in routing.  1
                          (dash_prefill and dash_decode_diag with entmax routing, T <= 64 *
-                         2048; elsewhere DASH_ERR_UNSUPPORTED; bf16 prefill then runs Stage 1
-                         on the generic router):
+                         2048; elsewhere DASH_ERR_UNSUPPORTED):
                          the own chunk is summarised by Stage 0's formula over its keys up to
                          the query and joins each head's alpha-entmax normalisation as one more
                          entry (aiexpert.news, interface paragraph: a diagonal correction of

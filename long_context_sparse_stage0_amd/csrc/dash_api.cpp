@@ -100,7 +100,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillLayout {
-  size_t summ, ssplit, vt, mask, wbar, ctr, total;
+  size_t summ, ssplit, vt, mask, wbar, ctr, ydiag, total;
 };
 
 PrefillLayout prefill_layout(const Dims& d) {
@@ -118,6 +118,8 @@ PrefillLayout prefill_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.T * d.nc * 4);
   L.ctr = off;
   off += 256;
+  L.ydiag = off;   // estimate_diagonal: the own chunk's Stage 1 score per (b, head, row)
+  off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hq * d.T * 4) : 0;
   L.total = off;
   return L;
 }
@@ -267,12 +269,18 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
     ra.s0_scale_log2 = d.scale * 1.4426950408889634f;
   }
   if (stages & 2) {
-    // estimate_diagonal runs on the generic router for either dtype: it writes the same mask
-    // and weight layout that the MFMA Stage 2 reads
-    if (d.dtype == DASH_BF16 && p->estimate_diagonal == 0)
+    if (d.dtype == DASH_BF16) {
+      if (p->estimate_diagonal != 0) {
+        float* yd = reinterpret_cast<float*>(ws + L.ydiag);
+        if ((e = dash::launch_diag_scores(k, head_cls, q, yd, d.B, d.Hq, d.Hkv, d.T, d.D, d.nc,
+                                          d.scale, ra.zscale, s)) != hipSuccess)
+          return hip_fail(e, "diagonal score launch");
+        ra.ydiag = yd;
+      }
       e = dash::launch_route_mfma(ra, ws + L.ssplit, s);
-    else
+    } else {
       e = dash::launch_route_valu(ra, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "stage 1 launch");
   }
   if (!(stages & 4)) return ok();

@@ -88,6 +88,8 @@ struct RouteArgs {
   const void* head_cls;   // and head_cls [Hkv, D] for the own chunk's summary, or nullptr
   int kdiag_ld;
   float s0_scale_log2;    // Stage 0 logit scale * log2(e)
+  const float* ydiag;     // estimate_diagonal (MFMA router): [B, Hq, Tq] scaled score of each
+                          // row's own chunk (k_diag_scores), or nullptr
 };
 
 struct AttendArgs {
@@ -118,6 +120,10 @@ struct AttendArgs {
 // (see split_offset), so one wave-wide 16-byte load reads 1 KiB of contiguous memory.
 // block_table (nullable): paged K, [num_pages][Hkv][64][D], chunk c of sequence b in page
 // block_table[b * bt_ld + c] (chunks whose page id is out of range are skipped).
+// ydiag [B, Hq, T] for estimate_diagonal on the MFMA router (bf16 inputs)
+hipError_t launch_diag_scores(const void* k, const void* head_cls, const void* q, float* ydiag,
+                              int B, int Hq, int Hkv, int T, int D, int nc, float scale,
+                              float zscale, hipStream_t s);
 hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
                          int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,

@@ -13,6 +13,10 @@
 // registers (at most 8 tiles x 2 query tiles x 4 = 64 values per lane; 16 waves cover
 // 2048 chunks).
 //
+// estimate_diagonal (aiexpert.news, interface paragraph): the own chunk's score of each
+// query vector, precomputed by k_diag_scores, is one more entry of the max, of every solver
+// pass and of the normaliser; it never gets a weight or a mask bit.
+//
 // Scores: S^T = K_bar Q^T on v_mfma_f32_16x16x32_bf16.  Q is bf16 exactly; the fp32
 // summaries are split once (by Stage 0) into bf16 hi + lo planes and both products are
 // accumulated in fp32, so a score carries about 16 mantissa bits of the summary instead
@@ -105,12 +109,17 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
   // queries of this lane: column l16 of query tiles 0 and 1
   bf16x8 qop[QTR][KS];
   int qrow[QTR];
+  // estimate_diagonal: the own chunk's score of each query vector joins the normalisation as
+  // one more entry, held by the lanes of wave 0's first 16-lane group only
+  const bool dsel = a.ydiag != nullptr && wv == 0 && lg == 0;
+  float yd[QTR];
 #pragma unroll
   for (int qt = 0; qt < QTR; ++qt) {
     const int n = 16 * qt + l16;
     const int r = n / G, g = n % G;
     qrow[qt] = r;
     const int t = min(row0 + r, T - 1);
+    yd[qt] = dsel ? a.ydiag[(size_t)(b * a.Hq + kvh * G + g) * T + t] : -INFINITY;
     const bf16* qp = (const bf16*)a.q + ((size_t)(b * a.Hq + kvh * G + g) * T + t) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qop[qt][ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
@@ -165,7 +174,8 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     probe[qt] = false;
   }
   // long rows (alpha = 1.5) take a moment-based start after the first pass
-  const bool model_start = MODE == kAlpha15 && it >= kEntmaxModelMinN;
+  const int nent = a.ydiag != nullptr ? it + 1 : it;   // entries of the normalisation
+  const bool model_start = MODE == kAlpha15 && nent >= kEntmaxModelMinN;
   const float inv = 1.0f / (a.alpha - 1.0f);
   int buf = 0;
   if (MODE == kTopK && it > 0) {
@@ -248,7 +258,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     // pass 0: max
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) {
-      float m = -INFINITY;
+      float m = yd[qt];
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         if (j < nj) {
@@ -260,7 +270,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
       if (lg == 0) part[buf][qt][0][l16][wv] = m;
     }
     __syncthreads();
-    const float n = (float)it;
+    const float n = (float)nent;
     const float hoff = (MODE == kAlpha15) ? rsqrtf(n) : (MODE == kAlpha2 ? 1.0f / n : pow_pos(n, 1.0f - a.alpha));
 #pragma unroll
     for (int qt = 0; qt < QTR; ++qt) {
@@ -277,11 +287,12 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
       for (int qt = 0; qt < QTR; ++qt) {
         float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
+        for (int j = -1; j < MT; ++j) {
           if (j >= nj) continue;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const float d = y[j][qt][jj] - tau[qt];
+            if (j < 0 && jj > 0) continue;
+            const float d = (j < 0 ? yd[qt] : y[j][qt][jj]) - tau[qt];
             const bool in = d > 0.f;
             const float dp = fmaxf(d, 0.f);
             cnt += in ? 1.f : 0.f;
@@ -380,11 +391,12 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
     for (int qt = 0; qt < QTR; ++qt) {
       float z = 0.f;
 #pragma unroll
-      for (int j = 0; j < MT; ++j) {
+      for (int j = -1; j < MT; ++j) {
         if (j >= nj) continue;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float d = y[j][qt][jj] - tau[qt];
+          if (j < 0 && jj > 0) continue;
+          const float d = (j < 0 ? yd[qt] : y[j][qt][jj]) - tau[qt];
           if (d > 0.f) z += (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
         }
       }

@@ -136,6 +136,88 @@ __global__ __launch_bounds__(256) void k_vtranspose(const uint16_t* __restrict__
   }
 }
 
+// estimate_diagonal on the MFMA router: the Stage 1 score of each row's own chunk,
+// ydiag[b, h, t] = zscale <q_{h,t}, kbar_t>, where kbar_t is Stage 0's summary of the keys
+// i_t C .. t (the chunk's keys seen so far).  One 256-thread workgroup per (b, kv head,
+// chunk): the chunk's keys go to LDS in fp32 and wave 0 scores them against head_cls; thread
+// (r, dq) = (tid / 4, tid % 4) then forms row r's prefix-softmax weights, accumulates its
+// quarter of kbar_r in registers (column pairs 2 dq + 8 p, so the four threads of a row hit
+// distinct LDS banks and read each query row contiguously together) and the G dot products
+// are reduced over those four threads.
+template <int D>
+__global__ __launch_bounds__(256) void k_diag_scores(const bf16* __restrict__ k,
+                                                     const bf16* __restrict__ head_cls,
+                                                     const bf16* __restrict__ q,
+                                                     float* __restrict__ ydiag, int Hq, int Hkv,
+                                                     int T, float scale_log2, float zscale) {
+  constexpr int NP = D / 8;                  // column pairs per thread
+  __shared__ float kl[64][D + 1];
+  __shared__ float al[64];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int t0 = c * kChunk;
+  const int nrow = min(kChunk, T - t0);
+  const bf16* kc = k + ((size_t)(b * Hkv + kvh) * T + t0) * D;
+  for (int i = tid; i < 64 * D; i += 256) {
+    const int j = i / D, d = i % D;
+    kl[j][d] = j < nrow ? (float)kc[(size_t)j * D + d] : 0.f;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float acc = 0.f;
+    for (int d = 0; d < D; ++d) acc = fmaf((float)head_cls[kvh * D + d], kl[tid][d], acc);
+    al[tid] = acc * scale_log2;
+  }
+  __syncthreads();
+  const int r = tid >> 2, dq = tid & 3;
+  if (r >= nrow) return;                     // the four threads of a row leave together
+  float m = -INFINITY;
+  for (int j = 0; j <= r; ++j) m = fmaxf(m, al[j]);
+  float acc[NP][2];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) acc[p][0] = acc[p][1] = 0.f;
+  float sum = 0.f;
+  for (int j = 0; j <= r; ++j) {
+    const float w = fast_exp2(al[j] - m);
+    sum += w;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      acc[p][0] = fmaf(w, kl[j][2 * dq + 8 * p], acc[p][0]);
+      acc[p][1] = fmaf(w, kl[j][2 * dq + 8 * p + 1], acc[p][1]);
+    }
+  }
+  const float rs = zscale / sum;
+  const int t = t0 + r;
+  for (int g = 0; g < G; ++g) {
+    const size_t qi = (size_t)(b * Hq + kvh * G + g) * T + t;
+    const bf16* qp = q + qi * D + 2 * dq;
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      s = fmaf((float)qp[8 * p], acc[p][0], s);
+      s = fmaf((float)qp[8 * p + 1], acc[p][1], s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (dq == 0) ydiag[qi] = s * rs;
+  }
+}
+
+hipError_t launch_diag_scores(const void* k, const void* head_cls, const void* q, float* ydiag,
+                              int B, int Hq, int Hkv, int T, int D, int nc, float scale,
+                              float zscale, hipStream_t s) {
+  dim3 grid(nc, Hkv, B);
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    k_diag_scores<128><<<grid, 256, 0, s>>>((const bf16*)k, (const bf16*)head_cls, (const bf16*)q,
+                                            ydiag, Hq, Hkv, T, sl2, zscale);
+  else
+    k_diag_scores<64><<<grid, 256, 0, s>>>((const bf16*)k, (const bf16*)head_cls, (const bf16*)q,
+                                           ydiag, Hq, Hkv, T, sl2, zscale);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void* summ_split,
                          int B, int Hkv, int T_stride, int D, int nc_alloc, int n_full,
                          const int32_t* lo_b, const int32_t* seq_lens, float scale,

@@ -169,13 +169,14 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
 
 def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=1.0,
                   sm_scale=None, sigma=1.0, topk=0, enable_gqa=False, active_blocks=None,
-                  block_weights=None,
+                  block_weights=None, estimate_diagonal=False,
                   summaries=None, stream=None):
     """Run one prefill stage (0, 1 or 2) from the intermediates a full `prefill` call with
     the same tensors and workspace left behind (profiling aid)."""
     B, Hq, T, D = q.shape
     p = make_params(B, Hq, k.shape[1], T, D, alpha=alpha, gamma=gamma, sm_scale=sm_scale,
-                    enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma, topk=topk)
+                    enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma, topk=topk,
+                    estimate_diagonal=estimate_diagonal)
     _check(load().dash_prefill_stage(ctypes.byref(p), int(stage), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(head_cls), _ptr(out), _ptr(active_blocks),
                                      _ptr(block_weights), _ptr(summaries), _ptr(workspace),

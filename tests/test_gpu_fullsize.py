@@ -33,7 +33,7 @@ def _sample_rows(T, n, seed, fixed):
     return np.unique(rows[(rows >= 0) & (rows < T)])
 
 
-def _prefill_bench_config(dash, w, rows):
+def _prefill_bench_config(dash, w, rows, estimate_diagonal=False):
     """Run the prefill exactly as the benchmark does (Stages 0, 1, 2 on one workspace),
     then again with the block weights returned; compare sampled rows with the oracle."""
     x = synth.prefill_inputs(w)
@@ -49,7 +49,8 @@ def _prefill_bench_config(dash, w, rows):
     ws = dash.alloc_workspace(dash.workspace_size("prefill", p), "cuda")
     out = torch.empty_like(q)
     ab = torch.empty((B, Hkv, T, W), dtype=torch.int64, device="cuda")
-    kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=w.enable_gqa)
+    kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=w.enable_gqa,
+              estimate_diagonal=estimate_diagonal)
     for s in range(3):                       # the timed step of the benchmark
         dash.prefill_stage(s, q, k, v, hc, out, ws, **kw)
     # the mask as the benchmark reads it (Stage 1 again, mask into the caller's buffer)
@@ -68,7 +69,7 @@ def _prefill_bench_config(dash, w, rows):
     torch.cuda.empty_cache()
     summ = O.chunk_summaries(x["k"], x["head_cls"], 1.0 / np.sqrt(w.D))
     ref = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, gamma=w.gamma,
-                    rows=rows, summaries=summ)
+                    rows=rows, summaries=summ, estimate_diagonal=estimate_diagonal)
     e_out = compare_out(g_out, ref["out"], w.dtype)
     e_w = compare_weights(g_w, ref["w_bar"])
     amb = compare_mask(g_bits, ref["mask"], ref["margin"], rows)
@@ -85,6 +86,15 @@ def test_prefill_128k_sampled_rows(dash):
     rows = _sample_rows(w.T, 20, 1, [0, 63, 64, 65, 4095, 65536, 131007, 131008, w.T - 1])
     frac = _prefill_bench_config(dash, w, rows)
     assert 0.5 < frac < 0.95
+
+
+def test_prefill_128k_estimate_diagonal(dash):
+    """The 128K workload with estimate_diagonal (the own chunk's partial summary in every
+    head's entmax, on the MFMA router) on sampled rows: first, middle and last rows of chunks
+    and the final row."""
+    w = PREFILL_128K_GQA
+    rows = _sample_rows(w.T, 8, 3, [64, 65, 127, 65536 + 31, 131008, w.T - 1])
+    _prefill_bench_config(dash, w, rows, estimate_diagonal=True)
 
 
 def test_prefill_longest_sequence(dash):
