@@ -71,8 +71,10 @@ typedef struct dash_params {
   int32_t enable_gqa; /* 0: Hq must equal Hkv; 1: Hq % Hkv == 0 */
   int32_t dtype;      /* dash_dtype of q, k, v, head_cls and out */
   int32_t estimate_diagonal; /* 0: the own (diagonal) chunk takes no part in routing.  1
-                         (dash_prefill and dash_decode_diag with entmax routing, T <= 64 *
-                         2048; elsewhere DASH_ERR_UNSUPPORTED):
+                         (dash_prefill, dash_decode_diag and dash_decode_paged_diag with
+                         entmax routing, T <= 64 * 2048; with topk > 0 DASH_ERR_UNSUPPORTED;
+                         dash_decode and dash_decode_paged, which take no head_cls, return
+                         DASH_ERR_INVALID_ARG):
                          the own chunk is summarised by Stage 0's formula over its keys up to
                          the query and joins each head's alpha-entmax normalisation as one more
                          entry (aiexpert.news, interface paragraph: a diagonal correction of
@@ -154,8 +156,8 @@ int dash_decode(const dash_params* p, const void* q, const void* k_cache,
  * i_t C .. t of k_cache (Stage 0's formula) and joins each head's alpha-entmax
  * normalisation (aiexpert.news, interface paragraph), exactly as in dash_prefill.  With
  * estimate_diagonal = 0 it equals dash_decode.  Errors as dash_decode; a NULL head_cls with
- * the flag set is DASH_ERR_INVALID_ARG, the flag with topk > 0 or T_max > 64 * 2048 is
- * DASH_ERR_UNSUPPORTED (as is the flag in dash_decode and dash_decode_paged). */
+ * the flag set is DASH_ERR_INVALID_ARG (so is the flag in dash_decode and dash_decode_paged),
+ * the flag with topk > 0 or T_max > 64 * 2048 is DASH_ERR_UNSUPPORTED. */
 int dash_decode_diag(const dash_params* p, const void* q, const void* k_cache,
                      const void* v_cache, const void* head_cls, const int32_t* seq_lens,
                      const float* summary_cache, void* out, uint64_t* active_blocks,
@@ -195,6 +197,14 @@ int dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
                       const int32_t* seq_lens, const float* summary_cache, void* out,
                       uint64_t* active_blocks, void* workspace, size_t workspace_bytes,
                       void* stream);
+/* dash_decode_paged with head_cls [Hkv, D] (bf16), for estimate_diagonal = 1, as
+ * dash_decode_diag: the own chunk's keys are read from its page (an id outside the pool
+ * reads as zero keys). */
+int dash_decode_paged_diag(const dash_params* p, const void* q, const void* k_pages,
+                           const void* v_pages, int32_t num_pages, const int32_t* block_table,
+                           const void* head_cls, const int32_t* seq_lens,
+                           const float* summary_cache, void* out, uint64_t* active_blocks,
+                           void* workspace, size_t workspace_bytes, void* stream);
 int dash_append_chunk_paged(const dash_params* p, const void* k_pages, int32_t num_pages,
                             const int32_t* block_table, const void* head_cls,
                             const int32_t* seq_lens, float* summary_cache,

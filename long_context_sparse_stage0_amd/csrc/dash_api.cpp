@@ -182,7 +182,7 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
 
 extern "C" {
 
-int dash_abi_version(void) { return 103; }
+int dash_abi_version(void) { return 104; }
 
 const char* dash_last_error(void) { return g_err.c_str(); }
 
@@ -356,15 +356,13 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
   if (p->topk > 0 && d.dtype != DASH_BF16)
     return fail(DASH_ERR_UNSUPPORTED, "the top-k comparison router is built for bf16 only");
   if (p->estimate_diagonal != 0) {
-    if (block_table)
-      return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 is not built for paged caches");
     if (p->topk > 0)
       return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1 applies to the entmax router only");
     if (d.T > dash::kChunk * dash::kMaxRouted)
       return fail(DASH_ERR_UNSUPPORTED, "estimate_diagonal=1: T=%d exceeds %d", d.T,
                   dash::kChunk * dash::kMaxRouted);
     if (!head_cls)
-      return fail(DASH_ERR_INVALID_ARG, "estimate_diagonal=1 needs head_cls (dash_decode_diag)");
+      return fail(DASH_ERR_INVALID_ARG, "estimate_diagonal=1 needs head_cls (dash_decode_diag, dash_decode_paged_diag)");
     if (int rc = check_ptr(head_cls, "head_cls")) return rc;
   }
   if (block_table) {
@@ -415,6 +413,9 @@ int decode_impl(const dash_params* p, const void* q, const void* k_cache, const 
     ra.head_cls = head_cls;
     ra.kdiag_ld = d.T;
     ra.s0_scale_log2 = d.scale * 1.4426950408889634f;
+    ra.kdiag_bt = block_table;
+    ra.kdiag_bt_ld = d.nc;
+    ra.kdiag_pages = num_pages;
   }
   e = d.dtype == DASH_BF16 ? dash::launch_decode_route(ra, s) : dash::launch_route_valu(ra, s);
   if (e != hipSuccess) return hip_fail(e, "decode route launch");
@@ -497,6 +498,15 @@ int dash_decode_diag(const dash_params* p, const void* q, const void* k_cache,
                      void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(p, q, k_cache, v_cache, nullptr, 0, seq_lens, summary_cache, out,
                      active_blocks, workspace, workspace_bytes, stream, head_cls);
+}
+
+int dash_decode_paged_diag(const dash_params* p, const void* q, const void* k_pages,
+                           const void* v_pages, int32_t num_pages, const int32_t* block_table,
+                           const void* head_cls, const int32_t* seq_lens,
+                           const float* summary_cache, void* out, uint64_t* active_blocks,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(p, q, k_pages, v_pages, block_table, num_pages, seq_lens, summary_cache,
+                     out, active_blocks, workspace, workspace_bytes, stream, head_cls);
 }
 
 int dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,

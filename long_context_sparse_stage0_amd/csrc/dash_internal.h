@@ -90,6 +90,9 @@ struct RouteArgs {
   float s0_scale_log2;    // Stage 0 logit scale * log2(e)
   const float* ydiag;     // estimate_diagonal (MFMA router): [B, Hq, Tq] scaled score of each
                           // row's own chunk (k_diag_scores), or nullptr
+  const int32_t* kdiag_bt;  // estimate_diagonal, paged decode: block table [B][kdiag_bt_ld] of
+  int kdiag_bt_ld;          // kdiag's page pool [num_pages][Hkv][64][D] (nullptr: contiguous)
+  int kdiag_pages;
 };
 
 struct AttendArgs {

@@ -148,9 +148,15 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   if (diag) {
     const int b = bk / a.Hkv, kvh = bk % a.Hkv;
     if (wv == 0) {
-      const bf16* kb = (const bf16*)a.kdiag + ((size_t)bk * a.kdiag_ld + (size_t)it * kChunk) * D;
+      // paged caches: the own chunk's page; an id outside the pool reads as zero keys
+      int pg = 0;
+      if (a.kdiag_bt) pg = a.kdiag_bt[(size_t)b * a.kdiag_bt_ld + it];
+      const bool pok = a.kdiag_bt == nullptr || (pg >= 0 && pg < a.kdiag_pages);
+      const bf16* kb = a.kdiag_bt
+          ? (const bf16*)a.kdiag + ((size_t)(pok ? pg : 0) * a.Hkv + kvh) * kChunk * D
+          : (const bf16*)a.kdiag + ((size_t)bk * a.kdiag_ld + (size_t)it * kChunk) * D;
       const bf16* hc = (const bf16*)a.head_cls + (size_t)kvh * D;
-      const int nk = t - it * kChunk + 1;
+      const int nk = pok ? t - it * kChunk + 1 : 0;
       float lg = -INFINITY;
       if (lane < nk) {
         float acc = 0.f;
@@ -159,7 +165,8 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
       }
       const float m = wave_max(lg);
       const float e = lane < nk ? fast_exp2(lg - m) : 0.f;
-      const float pj = e / wave_sum(e);
+      const float se = wave_sum(e);
+      const float pj = se > 0.f ? e / se : 0.f;
       for (int d = lane; d < D; d += 64) {
         float acc = 0.f;
         for (int j = 0; j < nk; ++j) acc = fmaf(__shfl(pj, j), (float)kb[(size_t)j * D + d], acc);

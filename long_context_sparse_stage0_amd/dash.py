@@ -30,7 +30,7 @@ EXPORTS = [
     "dash_abi_version", "dash_last_error",
     "dash_prefill_workspace_size", "dash_prefill", "dash_prefill_stage",
     "dash_decode_workspace_size", "dash_decode", "dash_decode_diag",
-    "dash_append_chunk", "dash_decode_paged", "dash_append_chunk_paged",
+    "dash_append_chunk", "dash_decode_paged", "dash_decode_paged_diag", "dash_append_chunk_paged",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
 ]
 
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_append_chunk.restype = ctypes.c_int
     i32 = ctypes.c_int32
     lib.dash_decode_paged.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_decode_paged_diag.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_decode_paged_diag.restype = ctypes.c_int
     lib.dash_decode_paged.restype = ctypes.c_int
     lib.dash_append_chunk_paged.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.dash_append_chunk_paged.restype = ctypes.c_int
@@ -244,12 +246,14 @@ def _paged_params(q_or_none, k_pages, block_table, Hq, chunk_size, alpha, gamma,
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, summary_cache, *, chunk_size=64,
                  alpha=1.5, gamma=1.0, sm_scale=None, sigma=1.0, topk=0, enable_gqa=False,
+                 estimate_diagonal=False, head_cls=None,
                  return_active_blocks=False, out=None, workspace=None, stream=None):
     """One decode step over paged caches.  q [B,Hq,D]; k_pages, v_pages [num_pages,Hkv,64,D];
     block_table [B, ceil(T_max/64)] int32 (device); the rest as for `decode`."""
     B, Hq, D = q.shape
     p, num_pages = _paged_params(q, k_pages, block_table, Hq, chunk_size, alpha, gamma, sm_scale,
                                  sigma, enable_gqa, topk)
+    p.estimate_diagonal = int(bool(estimate_diagonal))
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     W = -(-block_table.shape[1] // 64)
@@ -259,10 +263,17 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, summary_cache, *, c
         if return_active_blocks else None
     if workspace is None:
         workspace = alloc_workspace(workspace_size("decode", p), q.device)
-    _check(load().dash_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_pages), _ptr(v_pages),
-                                    num_pages, _ptr(block_table), _ptr(seq_lens),
-                                    _ptr(summary_cache), _ptr(out), _ptr(ab), _ptr(workspace),
-                                    workspace.numel(), _stream(stream)))
+    if head_cls is not None:
+        _check(load().dash_decode_paged_diag(ctypes.byref(p), _ptr(q), _ptr(k_pages),
+                                             _ptr(v_pages), num_pages, _ptr(block_table),
+                                             _ptr(head_cls), _ptr(seq_lens), _ptr(summary_cache),
+                                             _ptr(out), _ptr(ab), _ptr(workspace),
+                                             workspace.numel(), _stream(stream)))
+    else:
+        _check(load().dash_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                        num_pages, _ptr(block_table), _ptr(seq_lens),
+                                        _ptr(summary_cache), _ptr(out), _ptr(ab), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
     return (out, ab) if return_active_blocks else out
 
 

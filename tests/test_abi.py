@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = _lib()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.dash_abi_version() == 103
+    assert lib.dash_abi_version() == 104
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
@@ -166,7 +166,13 @@ def test_decode_append_dense_validation():
     assert lib.dash_decode_diag(ctypes.byref(_params(estimate_diagonal=1, topk=3)), FAKE, FAKE,
                                 FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == -4
     assert lib.dash_decode_paged(ctypes.byref(_params(estimate_diagonal=1)), FAKE, FAKE, FAKE,
-                                 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == -4
+                                 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.dash_decode_paged_diag(ctypes.byref(_params(estimate_diagonal=1)), FAKE, FAKE,
+                                      FAKE, 4, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                      None) == -1
+    assert lib.dash_decode_paged_diag(ctypes.byref(_params(estimate_diagonal=1, dtype=1)), FAKE,
+                                      FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      1 << 30, None) == -4
     # the dense comparator is bf16 only
     pf = _params(dtype=1)
     assert lib.dash_dense_causal_workspace_size(ctypes.byref(pf), ctypes.byref(n)) == -3

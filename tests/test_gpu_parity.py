@@ -93,7 +93,7 @@ def test_prefill_prior_strength(dash, dtype, sigma):
     ("fp32", 4, 1.5, 1000, 128),     # ragged tail
     ("fp32", 1, 2.0, 520, 64),
     ("fp32", 16, 1.25, 700, 128),
-    ("bf16", 16, 1.5, 1000, 128),    # generic router feeding the MFMA Stage 2
+    ("bf16", 16, 1.5, 1000, 128),    # k_diag_scores feeding the MFMA router
     ("bf16", 2, 2.0, 450, 64),
 ])
 def test_prefill_estimate_diagonal(dash, dtype, G, alpha, T, D):
@@ -479,8 +479,9 @@ def test_decode_many_sequences(dash):
 
 
 def test_decode_paged_with_options(dash):
-    """The options compose: paged caches with the top-k router, and with a prior strength
-    sigma != 1, give outputs and masks bit-identical to the contiguous caches."""
+    """The options compose: paged caches with the top-k router, with a prior strength
+    sigma != 1 and with estimate_diagonal give outputs and masks bit-identical to the
+    contiguous caches."""
     w = Workload(name="dec_paged_opts", kind="prefill", B=2, Hq=16, Hkv=2, T=2200, D=128,
                  dtype="bf16", seed=965, needle_amp=1.0)
     x = synth.prefill_inputs(w)
@@ -500,14 +501,16 @@ def test_decode_paged_with_options(dash):
     nsum = torch.zeros(B, dtype=torch.int32, device="cuda")
     dash.append_chunk(k, hc, lens_t, summ, nsum, Hq=w.Hq, enable_gqa=True)
     q = torch.stack([to_dev(x["q"][b, :, lens[b] - 1], "bf16") for b in range(B)]).contiguous()
-    for opts in (dict(topk=12), dict(sigma=0.5), dict(topk=5, sigma=2.0)):
+    for opts in (dict(topk=12), dict(sigma=0.5), dict(topk=5, sigma=2.0),
+                 dict(estimate_diagonal=True, head_cls=hc),
+                 dict(estimate_diagonal=True, head_cls=hc, sigma=0.5)):
         o_c, a_c = dash.decode(q, k, v, lens_t, summ, enable_gqa=True, return_active_blocks=True,
                                **opts)
         o_p, a_p = dash.decode_paged(q, kp, vp, table, lens_t, summ, enable_gqa=True,
                                      return_active_blocks=True, **opts)
         torch.cuda.synchronize()
-        assert torch.equal(o_c, o_p), opts
-        assert torch.equal(a_c, a_p[..., :a_c.shape[-1]]), opts
+        assert torch.equal(o_c, o_p), list(opts)
+        assert torch.equal(a_c, a_p[..., :a_c.shape[-1]]), list(opts)
 
 
 def test_decode_steps_with_append(dash):
