@@ -266,12 +266,13 @@ def bench_decode(args, w, dash, torch):
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     ab = torch.empty((B, Hkv, W), dtype=torch.int64, device=dev)
 
-    def run(n, with_mask=False):
+    def run(n, with_mask=False, diag=False):
         act = 0.0
+        dkw = dict(estimate_diagonal=True, head_cls=hc) if diag else {}
         for s in range(n):
             L = w.T + 1 + s
             r = dash.decode(qs[s], kc, vc, lens_all[s], summ, alpha=w.alpha, enable_gqa=True,
-                            out=out, workspace=ws, return_active_blocks=with_mask)
+                            out=out, workspace=ws, return_active_blocks=with_mask, **dkw)
             if with_mask:
                 act += float(popcount64(r[1]).sum())
             if L % 64 == 0:
@@ -307,6 +308,21 @@ def bench_decode(args, w, dash, torch):
     log(f"decode {us:.1f} us/step ({(t1 - t0) * 1e6 / S:.1f} wall), {gbs:.0f} GB/s, "
         f"active fraction {frac_active:.3f}")
     o_last = out.clone()
+
+    # the same steps with estimate_diagonal (the own chunk's partial summary in the entmax)
+    us_d = None
+    if not args.no_diag:
+        nsum.fill_(w.T // 64)
+        run(min(S, 8), diag=True)
+        torch.cuda.synchronize()
+        nsum.fill_(w.T // 64)
+        e0.record()
+        run(S, diag=True)
+        e1.record()
+        torch.cuda.synchronize()
+        us_d = e0.elapsed_time(e1) * 1e3 / S
+        nsum.fill_(w.T // 64)
+        log(f"decode with estimate_diagonal {us_d:.1f} us/step")
 
     # the same steps over paged caches: every chunk of every sequence in a shuffled page of
     # one pool [pages, Hkv, 64, D], appends through the block table
@@ -352,7 +368,8 @@ def bench_decode(args, w, dash, torch):
                          "frac": gbs / PEAK_HBM_GBS},
             "active_fraction": frac_active,
             "paged": {"us_per_step": us_p, "achieved_gbs": gbs_p, "frac": gbs_p / PEAK_HBM_GBS,
-                      "pages": B * nc_, "identical_to_contiguous": same}}
+                      "pages": B * nc_, "identical_to_contiguous": same},
+            "estimate_diagonal": {"us_per_step": us_d}}
 
 
 def cpu_baseline(args, w, x):

@@ -138,40 +138,62 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
   const int it = valid ? t / kChunk : 0;
   const float* srow = a.sco + ((size_t)bk * G + (wv < G ? wv : 0)) * a.sco_ld;
 
-  // estimate_diagonal: the own chunk's summary over its keys i_t C .. t (Stage 0's formula),
-  // built by wave 0 (lane j scores key j, softmax across lanes, lane l accumulates columns
-  // l, l + 64, ...); every head then scores it as routed entry i_t, which joins the
-  // threshold but never the mask, the weights or the work list
+  // estimate_diagonal: the own chunk's summary over its keys i_t C .. t (Stage 0's formula);
+  // every head then scores it as routed entry i_t, which joins the threshold but never the
+  // mask, the weights or the work list.  Wave w scores keys 4w .. 4w + 3 against head_cls
+  // (its lanes spanning the columns, so each key row is one coalesced read); then thread
+  // (key group, column) sums its keys' softmax-weighted columns and the groups are added.
+  constexpr int NGD = 1024 / D, KPG = kChunk / NGD;   // key groups, keys per group
   __shared__ float kdg[D];
+  __shared__ float dlg[kChunk];
+  __shared__ float dpart[NGD][D];
   const bool diag = a.kdiag != nullptr && MODE != kTopK && it > 0 && it < kMaxRouted;
   float ydiag = -INFINITY;
   if (diag) {
     const int b = bk / a.Hkv, kvh = bk % a.Hkv;
-    if (wv == 0) {
-      // paged caches: the own chunk's page; an id outside the pool reads as zero keys
-      int pg = 0;
-      if (a.kdiag_bt) pg = a.kdiag_bt[(size_t)b * a.kdiag_bt_ld + it];
-      const bool pok = a.kdiag_bt == nullptr || (pg >= 0 && pg < a.kdiag_pages);
-      const bf16* kb = a.kdiag_bt
-          ? (const bf16*)a.kdiag + ((size_t)(pok ? pg : 0) * a.Hkv + kvh) * kChunk * D
-          : (const bf16*)a.kdiag + ((size_t)bk * a.kdiag_ld + (size_t)it * kChunk) * D;
-      const bf16* hc = (const bf16*)a.head_cls + (size_t)kvh * D;
-      const int nk = pok ? t - it * kChunk + 1 : 0;
-      float lg = -INFINITY;
-      if (lane < nk) {
-        float acc = 0.f;
-        for (int d = 0; d < D; ++d) acc = fmaf((float)hc[d], (float)kb[(size_t)lane * D + d], acc);
-        lg = acc * a.s0_scale_log2;
+    // paged caches: the own chunk's page; an id outside the pool reads as zero keys
+    int pg = 0;
+    if (a.kdiag_bt) pg = a.kdiag_bt[(size_t)b * a.kdiag_bt_ld + it];
+    const bool pok = a.kdiag_bt == nullptr || (pg >= 0 && pg < a.kdiag_pages);
+    const bf16* kb = a.kdiag_bt
+        ? (const bf16*)a.kdiag + ((size_t)(pok ? pg : 0) * a.Hkv + kvh) * kChunk * D
+        : (const bf16*)a.kdiag + ((size_t)bk * a.kdiag_ld + (size_t)it * kChunk) * D;
+    const bf16* hc = (const bf16*)a.head_cls + (size_t)kvh * D;
+    const int nk = pok ? t - it * kChunk + 1 : 0;
+    constexpr int E = D / 64;
+    float hv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) hv[e] = (float)hc[lane * E + e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * wv + i;
+      float part = 0.f;
+      if (j < nk) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) part = fmaf(hv[e], (float)kb[(size_t)j * D + lane * E + e], part);
       }
-      const float m = wave_max(lg);
-      const float e = lane < nk ? fast_exp2(lg - m) : 0.f;
-      const float se = wave_sum(e);
-      const float pj = se > 0.f ? e / se : 0.f;
-      for (int d = lane; d < D; d += 64) {
-        float acc = 0.f;
-        for (int j = 0; j < nk; ++j) acc = fmaf(__shfl(pj, j), (float)kb[(size_t)j * D + d], acc);
-        kdg[d] = acc;
-      }
+      part = wave_sum(part);
+      if (lane == 0) dlg[j] = j < nk ? part * a.s0_scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    float m = -INFINITY;
+    for (int j = 0; j < nk; ++j) m = fmaxf(m, dlg[j]);
+    float se = 0.f;
+    for (int j = 0; j < nk; ++j) se += fast_exp2(dlg[j] - m);
+    const int dc = tid % D, kg = tid / D;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < KPG; ++i) {
+      const int j = kg * KPG + i;
+      if (j < nk) acc = fmaf(fast_exp2(dlg[j] - m), (float)kb[(size_t)j * D + dc], acc);
+    }
+    dpart[kg][dc] = se > 0.f ? acc / se : 0.f;
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < NGD; ++g2) sum += dpart[g2][tid];
+      kdg[tid] = sum;
     }
     __syncthreads();
     if (wv < G) {
