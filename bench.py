@@ -52,6 +52,19 @@ def popcount64(x):
     return out
 
 
+# dash_prefill_stage order of one full prefill: summaries, the chunk-transposed V copy that
+# bf16 Stage 2 reads, routing, sparse attention
+STAGES = (0, 3, 1, 2)
+
+
+def stage_times(ev):
+    """Mean ms per prefill stage, keyed by dash_prefill_stage index, from per-step event
+    lists [start, after STAGES[0], after STAGES[1], ...]."""
+    n = len(ev)
+    return {s: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)]))
+            for j, s in enumerate(STAGES)}
+
+
 def source_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -107,24 +120,26 @@ def bench_prefill(args, w, dash, torch):
     # does 2 D flops per (query vector, routed chunk) score (twice, for the hi and lo planes)
     nfull = T // 64
     s0_bytes = float(B * Hkv * (T * D * 2 + nfull * D * 4))
-    s0_extra = float(B * Hkv * (nfull * D * 2 * 2 + 2 * T * D * 2))
+    s0_split = float(B * Hkv * nfull * D * 2 * 2)
+    vt_bytes = float(B * Hkv * 2 * nc * 64 * D * 2)      # V read, V^T written
     s1_bytes = float(B * Hq * T * D * 2 + B * Hkv * nc * D * 4 + B * Hkv * T * W * 8
                      + active.sum() * 4)
     s1_flops = float(2 * D * Hq * B * routed.sum())
     del pc, active
 
     def step(evs=None):
-        for s in range(3):
+        for i, s in enumerate(STAGES):
             dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
                                enable_gqa=True)
             if evs is not None:
-                evs[s + 1].record()
+                evs[i + 1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -133,9 +148,9 @@ def bench_prefill(args, w, dash, torch):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    st = [float(np.mean([ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(args.steps)]))
-          for s in range(3)]
-    log(f"prefill {ms:.2f} ms/step; stages {st[0]:.3f} / {st[1]:.3f} / {st[2]:.3f} ms")
+    st = stage_times(ev)
+    log(f"prefill {ms:.2f} ms/step; summaries {st[0]:.3f}, V^T copy {st[3]:.3f}, "
+        f"stage 1 {st[1]:.3f}, stage 2 {st[2]:.3f} ms")
     tokens_s = B * T / (ms / 1e3)
 
     traffic = None
@@ -152,11 +167,14 @@ def bench_prefill(args, w, dash, torch):
             "kernel_ms": st[2]}
     res = dict(ms=ms, tokens_s=tokens_s, stages_ms=st, roofline=roof, zero_frac=zero_frac,
                flops2=flops2, flops_dense=flops_dense, x=x)
-    res["stage0"] = {"ms": st[0], "algorithmic_bytes": s0_bytes,
+    res["stage0"] = {"kernel": "k_stage0", "ms": st[0], "algorithmic_bytes": s0_bytes,
                      "gbs": s0_bytes / (st[0] / 1e3) / 1e9,
                      "frac_of_hbm_peak": s0_bytes / (st[0] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                     "extra_bytes_split_and_vT": s0_extra,
-                     "gbs_with_extras": (s0_bytes + s0_extra) / (st[0] / 1e3) / 1e9}
+                     "extra_bytes_split_planes": s0_split,
+                     "gbs_with_split_planes": (s0_bytes + s0_split) / (st[0] / 1e3) / 1e9}
+    res["vtranspose"] = {"kernel": "k_vtranspose", "ms": st[3], "bytes": vt_bytes,
+                         "gbs": vt_bytes / (st[3] / 1e3) / 1e9,
+                         "frac_of_hbm_peak": vt_bytes / (st[3] / 1e3) / 1e9 / PEAK_HBM_GBS}
     s1_lb = {"mfma_ms": 2 * s1_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3,
              "hbm_ms": s1_bytes / (PEAK_HBM_GBS * 1e9) * 1e3}
     res["stage1"] = {"ms": st[1], "algorithmic_bytes": s1_bytes,
@@ -173,20 +191,20 @@ def bench_prefill(args, w, dash, torch):
                            enable_gqa=True, topk=k_match, active_blocks=ab)
         torch.cuda.synchronize()
         act_k = float(popcount64(ab).sum())
-        evk = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        evk = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+               for _ in range(args.steps)]
         for i in range(-1, args.steps):
             if i >= 0:
                 evk[i][0].record()
-            for s in range(3):
+            for j, s in enumerate(STAGES):
                 dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
                                    enable_gqa=True, topk=k_match)
                 if i >= 0:
-                    evk[i][s + 1].record()
+                    evk[i][j + 1].record()
         torch.cuda.synchronize()
-        stk = [float(np.mean([evk[i][s].elapsed_time(evk[i][s + 1]) for i in range(args.steps)]))
-               for s in range(3)]
+        stk = stage_times(evk)
         res["topk"] = {"k": k_match, "stage1_ms": stk[1], "stage2_ms": stk[2],
-                       "prefill_ms": sum(stk),
+                       "prefill_ms": sum(stk.values()),
                        "active_fraction": act_k / float(routed.sum() * B * Hkv),
                        "entmax_stage1_ms": st[1], "entmax_active_fraction": 1.0 - zero_frac}
         log(f"top-k router (k={k_match}): stage 1 {stk[1]:.2f} ms (entmax {st[1]:.2f}), "
@@ -198,19 +216,19 @@ def bench_prefill(args, w, dash, torch):
                            enable_gqa=True, estimate_diagonal=True, active_blocks=ab)
         torch.cuda.synchronize()
         act_d = float(popcount64(ab).sum())
-        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+               for _ in range(args.steps)]
         for i in range(-1, args.steps):
             if i >= 0:
                 evd[i][0].record()
-            for s in range(3):
+            for j, s in enumerate(STAGES):
                 dash.prefill_stage(s, q, k, v, hc, out, ws, alpha=w.alpha, gamma=w.gamma,
                                    enable_gqa=True, estimate_diagonal=True)
                 if i >= 0:
-                    evd[i][s + 1].record()
+                    evd[i][j + 1].record()
         torch.cuda.synchronize()
-        sd = [float(np.mean([evd[i][s].elapsed_time(evd[i][s + 1]) for i in range(args.steps)]))
-              for s in range(3)]
-        res["diag"] = {"stage1_ms": sd[1], "stage2_ms": sd[2], "prefill_ms": sum(sd),
+        sd = stage_times(evd)
+        res["diag"] = {"stage1_ms": sd[1], "stage2_ms": sd[2], "prefill_ms": sum(sd.values()),
                        "active_fraction": act_d / float(routed.sum() * B * Hkv),
                        "without_flag_stage1_ms": st[1]}
         log(f"estimate_diagonal: stage 1 {sd[1]:.2f} ms (without {st[1]:.2f}), "
@@ -372,31 +390,84 @@ def bench_decode(args, w, dash, torch):
             "estimate_diagonal": {"us_per_step": us_d}}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _LIMITS
+    _LIMITS = threadpool_limits(limits=1)      # one BLAS thread per worker process
+
+
+def _oracle_worker(task):
+    """One worker's share of the sampled rows: the oracle's prefill on them, over inputs
+    memory-mapped from the files the parent wrote.  Returns (rows done, seconds)."""
+    d, rows, alpha = task
+    from oracle import dash_oracle as O
+    x = {n: np.load(os.path.join(d, n + ".npy"), mmap_mode="r")
+         for n in ("q", "k", "v", "head_cls", "summ")}
+    t0 = time.perf_counter()
+    O.prefill(x["q"], x["k"], x["v"], np.asarray(x["head_cls"]), alpha=alpha, rows=rows,
+              summaries=np.asarray(x["summ"]))
+    return len(rows), time.perf_counter() - t0
+
+
 def cpu_baseline(args, w, x):
-    """The float64 oracle on a bounded, uniformly sampled set of rows; extrapolated to the
-    whole sequence (Stage 0 over every chunk + mean row cost x T)."""
+    """The float64 oracle, as it stands, on the host's cores: Stage 0 over every chunk in the
+    parent, then a uniformly sampled set of rows spread over one worker process per core
+    (one BLAS thread each, inputs memory-mapped), timed from the moment the warmed-up pool
+    gets its tasks; extrapolated to the whole sequence."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
     from threadpoolctl import threadpool_limits
     from oracle import dash_oracle as O
+    cores = max(1, min(args.cpu_workers, os.cpu_count() or 1))
     rng = np.random.default_rng(12345)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         summ = O.chunk_summaries(x["k"], x["head_cls"], 1.0 / math.sqrt(w.D))
         t_s0 = time.perf_counter() - t0
-        rows = rng.integers(0, w.T, size=2)
+        probe = rng.integers(0, w.T, size=2)
         t0 = time.perf_counter()
-        O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, rows=rows, summaries=summ)
-        t_probe = time.perf_counter() - t0
-        n = int(max(4, min(256, args.cpu_seconds / max(t_probe / 2, 1e-3))))
-        rows = rng.integers(0, w.T, size=n)
-        t0 = time.perf_counter()
-        O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, rows=rows, summaries=summ)
-        t_rows = time.perf_counter() - t0
+        O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, rows=probe,
+                  summaries=summ)
+        t_probe = (time.perf_counter() - t0) / 2
+    n = int(max(cores, min(128 * cores, cores * args.cpu_seconds / max(t_probe, 1e-3))))
+    rows = rng.integers(0, w.T, size=n)
+    order = rng.permutation(n)
+    tmp = tempfile.mkdtemp(prefix="dash_oracle_")
+    try:
+        for name, arr in (("q", x["q"]), ("k", x["k"]), ("v", x["v"]),
+                          ("head_cls", x["head_cls"]), ("summ", summ)):
+            np.save(os.path.join(tmp, name + ".npy"), arr)
+        tasks = [(tmp, rows[order[i::cores]], w.alpha) for i in range(cores)]
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores, initializer=_oracle_worker_init) as pool:
+            pool.map(abs, range(cores))                 # workers started and imported
+            t0 = time.perf_counter()
+            done = pool.map(_oracle_worker, tasks)
+            t_rows = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    cpu_s = sum(d[1] for d in done)
     t_full = t_s0 + t_rows / n * w.T
-    log(f"oracle: stage 0 {t_s0:.1f}s, {n} rows {t_rows:.1f}s -> {t_full:.0f}s for the sequence")
-    return {"value": w.B * w.T / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} uniformly sampled rows of the {w.name} workload (all heads) plus "
-                      f"Stage 0 over every chunk, extrapolated to all {w.T} rows; "
-                      f"{t_s0 + t_rows:.1f}s of CPU time, 1 BLAS thread"}
+    log(f"oracle: stage 0 {t_s0:.1f}s; {n} rows on {cores} processes in {t_rows:.1f}s wall "
+        f"({cpu_s:.0f} CPU-s) -> {t_full:.0f}s for the sequence")
+    return {"value": w.B * w.T / t_full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{n} uniformly sampled rows of the {w.name} workload (all heads) on "
+                      f"{cores} worker processes with one BLAS thread each, plus Stage 0 over "
+                      f"every chunk; {t_rows:.1f}s wall for the rows, extrapolated to all "
+                      f"{w.T} rows"}
 
 
 def bench_sweep(args, dash, torch):
@@ -421,6 +492,7 @@ def bench_sweep(args, dash, torch):
         ws = dash.alloc_workspace(dash.workspace_size("prefill", p), dev)
         kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=True)
         dash.prefill_stage(0, q, k, v, hc, out, ws, **kw)
+        dash.prefill_stage(3, q, k, v, hc, out, ws, **kw)
         dash.prefill_stage(1, q, k, v, hc, out, ws, active_blocks=ab, **kw)
         torch.cuda.synchronize()
         pc = popcount64(ab).sum(dim=-1).to(torch.float64)
@@ -431,7 +503,7 @@ def bench_sweep(args, dash, torch):
         del ab, pc
 
         def step():
-            for s in range(3):
+            for s in STAGES:
                 dash.prefill_stage(s, q, k, v, hc, out, ws, **kw)
         for _ in range(max(1, args.warmup)):
             step()
@@ -493,7 +565,7 @@ def bench_short(args, dash, torch):
             return e0.elapsed_time(e1) / n
 
         def prefill(topk):
-            for s in range(3):
+            for s in STAGES:
                 dash.prefill_stage(s, q, k, v, hc, out, ws, enable_gqa=True, topk=topk)
 
         def stage1(topk):
@@ -529,7 +601,10 @@ def main():
                     help="skip timing the top-k comparison router")
     ap.add_argument("--no-diag", action="store_true",
                     help="skip timing the prefill with estimate_diagonal")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall seconds of the CPU oracle's sampled rows")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes (at most the host's CPU count)")
     ap.add_argument("--short", action="store_true",
                     help="report entmax / top-k / dense at T = 2K..16K (one JSON line per T)")
     ap.add_argument("--sweep", action="store_true",
@@ -567,9 +642,11 @@ def main():
                    "zero_weight_fraction": pre["zero_frac"]},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
-        "stages_ms": {"stage0_summaries_and_vT": pre["stages_ms"][0],
+        "stages_ms": {"stage0_summaries": pre["stages_ms"][0],
+                      "vtranspose": pre["stages_ms"][3],
                       "stage1_route": pre["stages_ms"][1], "stage2_attend": pre["stages_ms"][2]},
         "stage0": pre["stage0"],
+        "vtranspose": pre["vtranspose"],
         "stage1": pre["stage1"],
         "dense": pre.get("dense"),
         "topk_router": pre.get("topk"),

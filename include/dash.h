@@ -99,7 +99,12 @@ int dash_abi_version(void);
 const char* dash_last_error(void);
 
 /* ---------------------------------------------------------------------------------
- * Causal prefill (all three stages).
+ * Causal prefill (all three stages): gist.science, "Methodik" and "Stufe 0"-"Stufe 2"
+ * (chunk summaries by a learned query's scaled dot-product attention over each complete
+ * chunk; alpha-entmax over the query-vs-summary logits, averaged over the query heads of a
+ * KV head into one shared support; softmax attention over the active chunks' tokens with
+ * the log of the block weight added to their logits, plus the own chunk); aixai.ru,
+ * "Трёхстадийная архитектура" (three stages, 64-bit mask words walked in one pass).
  *   q        [B, Hq, T, D]   dtype
  *   k, v     [B, Hkv, T, D]  dtype
  *   head_cls [Hkv, D]        dtype   (one classifier query per KV head)
@@ -115,23 +120,30 @@ const char* dash_last_error(void);
  * workspace: device buffer of at least dash_prefill_workspace_size() bytes, 256-byte
  * aligned, not shared with a concurrent call.
  * ------------------------------------------------------------------------------- */
+/* Workspace queries return a dash_status like every other entry point and write the size
+ * to *bytes, so an invalid parameter set is reported the same way everywhere. */
 int dash_prefill_workspace_size(const dash_params* p, size_t* bytes);
 int dash_prefill(const dash_params* p, const void* q, const void* k, const void* v,
                  const void* head_cls, void* out, uint64_t* active_blocks,
                  float* block_weights, float* summary_out, void* workspace,
                  size_t workspace_bytes, void* stream);
 
-/* Profiling aid: run one stage of dash_prefill alone (stage 0: summaries and the
- * chunk-transposed V; 1: routing; 2: sparse attention), reading the intermediates that a
- * complete dash_prefill call with the same arguments and workspace left behind.  Used to
- * time each kernel separately; results equal those of the full call. */
+/* Profiling aid: run one step of dash_prefill alone (stage 0: the chunk summaries; 1:
+ * routing; 2: sparse attention; 3: the chunk-transposed copy of V that bf16 Stage 2 reads,
+ * a no-op for fp32), reading the intermediates that a complete dash_prefill call with the
+ * same arguments and workspace left behind.  Used to time each kernel separately; stages
+ * 0, 3, 1, 2 in that order give the results of the full call. */
 int dash_prefill_stage(const dash_params* p, int stage, const void* q, const void* k,
                        const void* v, const void* head_cls, void* out,
                        uint64_t* active_blocks, float* block_weights, float* summary_out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * One incremental decoding step (one new token per sequence).
+ * One incremental decoding step (one new token per sequence): the incremental decoding
+ * with a cache of chunk representations that gist.science names among the main
+ * contributions ("Hauptbeiträge") and the liuzhao09 note describes in section 2 (the
+ * summary of a complete chunk is computed once, cached and reused by every later query;
+ * gist.science "Stufe 0").  Stages 1 and 2 then run for the single new query row.
  *   p->T          cache capacity T_max
  *   q             [B, Hq, D]            dtype, the new token's queries
  *   k_cache, v_cache [B, Hkv, T_max, D] dtype, holding seq_lens[b] valid tokens, the new

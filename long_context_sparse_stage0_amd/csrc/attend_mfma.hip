@@ -89,7 +89,7 @@ __device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 1) | (((d >> 2) 
 
 template <int D, int NW, int QT, int RMAX, bool DENSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 4 : 2)))
-void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
+void k_attend_mfma(AttendArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KS = D / 32;          // k-steps of the QK^T contraction
   constexpr int NDT = D / 16;         // 16-wide d tiles of the output
@@ -134,7 +134,6 @@ void k_attend_mfma(AttendArgs a, int tiles_per_bk) {
   const int row0 = rt * R;
   const int it = row0 / kChunk;              // diagonal chunk, shared by all R rows
   const int T = a.Tq;
-  (void)tiles_per_bk;
 
   // ---- per-row mask words and the union walk
   const int W = a.W;
@@ -499,19 +498,17 @@ static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int NW = G >= 4 ? 8 : 2 * G;
   const int R = NW * 32 / G;
-  const int tiles = (a.Tq + R - 1) / R;
   const int nunits = ((a.Tq + kChunk - 1) / kChunk) * a.B * a.Hkv;
   dim3 grid(((nunits + kXcds - 1) / kXcds) * kXcds * (kChunk / R));
   switch (NW) {
-    case 8: k_attend_mfma<D, 8, 2, 64, DENSE><<<grid, 512, 0, s>>>(a, tiles); break;
-    case 4: k_attend_mfma<D, 4, 2, 64, DENSE><<<grid, 256, 0, s>>>(a, tiles); break;
-    default: k_attend_mfma<D, 2, 2, 64, DENSE><<<grid, 128, 0, s>>>(a, tiles); break;
+    case 8: k_attend_mfma<D, 8, 2, 64, DENSE><<<grid, 512, 0, s>>>(a); break;
+    case 4: k_attend_mfma<D, 4, 2, 64, DENSE><<<grid, 256, 0, s>>>(a); break;
+    default: k_attend_mfma<D, 2, 2, 64, DENSE><<<grid, 128, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s) {
-  (void)work_counter;
+hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s) {
   if (a.dense)
     return a.D == 128 ? launch_attend_mfma_t<128, true>(a, s) : launch_attend_mfma_t<64, true>(a, s);
   return a.D == 128 ? launch_attend_mfma_t<128, false>(a, s) : launch_attend_mfma_t<64, false>(a, s);

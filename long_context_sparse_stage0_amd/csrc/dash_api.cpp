@@ -100,7 +100,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- prefill workspace
 struct PrefillLayout {
-  size_t summ, ssplit, vt, mask, wbar, ctr, ydiag, total;
+  size_t summ, ssplit, vt, mask, wbar, ydiag, total;
 };
 
 PrefillLayout prefill_layout(const Dims& d) {
@@ -116,8 +116,6 @@ PrefillLayout prefill_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.T * d.W * 8);
   L.wbar = off;
   off += align256((size_t)d.B * d.Hkv * d.T * d.nc * 4);
-  L.ctr = off;
-  off += 256;
   L.ydiag = off;   // estimate_diagonal: the own chunk's Stage 1 score per (b, head, row)
   off += d.dtype == DASH_BF16 ? align256((size_t)d.B * d.Hq * d.T * 4) : 0;
   L.total = off;
@@ -232,10 +230,10 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
     if ((e = dash::launch_stage0(k, head_cls, summ, ss, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull,
                                  nullptr, nullptr, d.scale, d.dtype, s)) != hipSuccess)
       return hip_fail(e, "stage 0 launch");
-    if (d.dtype == DASH_BF16) {
-      if ((e = dash::launch_vtranspose(v, ws + L.vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
-        return hip_fail(e, "V transpose launch");
-    }
+  }
+  if ((stages & 8) && d.dtype == DASH_BF16) {
+    if ((e = dash::launch_vtranspose(v, ws + L.vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
+      return hip_fail(e, "V transpose launch");
   }
   if ((stages & 2) && block_weights) {
     if ((e = fill_f32(block_weights, (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess)
@@ -310,7 +308,7 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   aa.dense = 0;
   if (d.dtype == DASH_BF16) {
     aa.vt = ws + L.vt;
-    if ((e = dash::launch_attend_mfma(aa, nullptr, s)) != hipSuccess)
+    if ((e = dash::launch_attend_mfma(aa, s)) != hipSuccess)
       return hip_fail(e, "stage 2 launch");
   } else {
     if ((e = dash::launch_attend_valu(aa, s)) != hipSuccess) return hip_fail(e, "stage 2 launch");
@@ -322,7 +320,7 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
                  const void* head_cls, void* out, uint64_t* active_blocks,
                  float* block_weights, float* summary_out, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  return prefill_impl(p, 7, q, k, v, head_cls, out, active_blocks, block_weights, summary_out,
+  return prefill_impl(p, 15, q, k, v, head_cls, out, active_blocks, block_weights, summary_out,
                       workspace, workspace_bytes, stream);
 }
 
@@ -330,7 +328,7 @@ int dash_prefill_stage(const dash_params* p, int stage, const void* q, const voi
                        const void* v, const void* head_cls, void* out,
                        uint64_t* active_blocks, float* block_weights, float* summary_out,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage < 0 || stage > 2) return fail(DASH_ERR_INVALID_ARG, "stage must be 0, 1 or 2");
+  if (stage < 0 || stage > 3) return fail(DASH_ERR_INVALID_ARG, "stage must be 0, 1, 2 or 3");
   return prefill_impl(p, 1 << stage, q, k, v, head_cls, out, active_blocks, block_weights,
                       summary_out, workspace, workspace_bytes, stream);
 }
@@ -477,7 +475,7 @@ int append_impl(const dash_params* p, const void* k_cache, const int32_t* block_
                                d.nfull, n_summarized, seq_lens, d.scale, d.dtype, s, block_table,
                                d.nc, num_pages)) != hipSuccess)
     return hip_fail(e, "append launch");
-  if ((e = dash::launch_update_nsum(n_summarized, seq_lens, d.B, s)) != hipSuccess)
+  if ((e = dash::launch_update_nsum(n_summarized, seq_lens, d.B, d.T, s)) != hipSuccess)
     return hip_fail(e, "append bookkeeping launch");
   return ok();
 }
@@ -579,7 +577,7 @@ int dash_dense_causal(const dash_params* p, const void* q, const void* k, const 
   if ((e = dash::launch_vtranspose(v, vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
     return hip_fail(e, "V transpose launch");
   aa.vt = vt;
-  if ((e = dash::launch_attend_mfma(aa, nullptr, s)) != hipSuccess) return hip_fail(e, "dense launch");
+  if ((e = dash::launch_attend_mfma(aa, s)) != hipSuccess) return hip_fail(e, "dense launch");
   return ok();
 }
 

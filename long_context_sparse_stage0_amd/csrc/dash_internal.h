@@ -133,13 +133,13 @@ hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void*
                          int dtype, hipStream_t s, const int32_t* block_table = nullptr,
                          int bt_ld = 0, int num_pages = 0);
 hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
-                              hipStream_t s);
+                              int T_stride, hipStream_t s);
 hipError_t launch_vtranspose(const void* v, void* vt, int B, int Hkv, int T, int D, int nc,
                              hipStream_t s);
 hipError_t launch_route_valu(const RouteArgs& a, hipStream_t s);
 hipError_t launch_route_mfma(const RouteArgs& a, const void* summ_split, hipStream_t s);
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_mfma(const AttendArgs& a, int* work_counter, hipStream_t s);
+hipError_t launch_attend_mfma(const AttendArgs& a, hipStream_t s);
 
 // decode (bf16): route one row per (b, kv head); split-K attend over the active chunks
 // into per-segment partials pml [B*Hkv][nseg][32] (max, sum) and po [B*Hkv][nseg][16][D],

@@ -482,7 +482,7 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
 // workgroups share a CU
 template <int D, int NW, int MT, int QTR, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QTR == 1 ? 4 : 1)))
-void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit, int rt_lo, int rt_n) {
+void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit, int rt_lo) {
   constexpr int NT = NW * 64;
   __shared__ float part[2][QTR][4][16][NW];
   __shared__ uint16_t mbits16[16 * QTR][4 * kRouteMaskWords];
@@ -498,7 +498,6 @@ void k_route_mfma(RouteArgs a, const bf16* __restrict__ ssplit, int rt_lo, int r
   const int T = a.Tq;
   const int W = a.W;
   const int ntile = (it + 15) / 16;
-  (void)rt_n;
 
   uint32_t* m32 = reinterpret_cast<uint32_t*>(&mbits16[0][0]);
   for (int i = tid; i < 16 * QTR * 2 * kRouteMaskWords; i += NT) m32[i] = 0u;
@@ -518,13 +517,13 @@ template <int D, int NW, int MT, int QTR>
 static void launch_mt(const RouteArgs& a, const bf16* ss, int rt_lo, int rt_n, hipStream_t s) {
   dim3 grid(rt_n * a.B * a.Hkv);
   if (a.topk > 0)
-    k_route_mfma<D, NW, MT, QTR, kTopK><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kTopK><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo);
   else if (a.alpha == 1.5f)
-    k_route_mfma<D, NW, MT, QTR, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlpha15><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo);
   else if (a.alpha == 2.0f)
-    k_route_mfma<D, NW, MT, QTR, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlpha2><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo);
   else
-    k_route_mfma<D, NW, MT, QTR, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo, rt_n);
+    k_route_mfma<D, NW, MT, QTR, kAlphaGeneral><<<grid, NW * 64, 0, s>>>(a, ss, rt_lo);
 }
 
 // Workgroup shapes by the number of 16-chunk tiles a row tile routes over.  Up to 64 tiles

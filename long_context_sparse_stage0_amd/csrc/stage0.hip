@@ -97,10 +97,16 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
   }
 }
 
-__global__ void k_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B) {
+// n_summarized[b] = max(n_summarized[b], complete chunks of the cache), with the length
+// clamped to [0, T_stride] as k_stage0 clamps it, so the count never passes the chunks that
+// were actually summarised
+__global__ void k_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
+                              int T_stride) {
   int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) {
-    int n = seq_lens[b] / kChunk;
+    int sl = seq_lens[b];
+    sl = sl < 0 ? 0 : (sl > T_stride ? T_stride : sl);
+    const int n = sl / kChunk;
     if (n > n_summarized[b]) n_summarized[b] = n;
   }
 }
@@ -251,8 +257,8 @@ hipError_t launch_stage0(const void* k, const void* head_cls, float* summ, void*
 }
 
 hipError_t launch_update_nsum(int32_t* n_summarized, const int32_t* seq_lens, int B,
-                              hipStream_t s) {
-  k_update_nsum<<<(B + 63) / 64, 64, 0, s>>>(n_summarized, seq_lens, B);
+                              int T_stride, hipStream_t s) {
+  k_update_nsum<<<(B + 63) / 64, 64, 0, s>>>(n_summarized, seq_lens, B, T_stride);
   return hipGetLastError();
 }
 

@@ -64,3 +64,46 @@ def compare_weights(gpu_w, ref_w):
     err = float(np.abs(gpu_w.astype(np.float64) - ref_w).max()) if gpu_w.size else 0.0
     assert err <= W_TOL, f"block weights: max-abs error {err:.3e} > {W_TOL}"
     return err
+
+
+def oracle_rows_worker(args):
+    """Process-pool task for whole-sequence parity: regenerate a workload's seeded inputs
+    (numpy only, no GPU) and run the oracle's prefill on the given rows.  Returns
+    (rows, out, w_bar, margin, mask) for those rows."""
+    from long_context_sparse_stage0_amd import synth
+    from oracle import dash_oracle as O
+    w, rows = args
+    x = synth.prefill_inputs(w, workers=1)
+    summ = O.chunk_summaries(x["k"], x["head_cls"], 1.0 / np.sqrt(w.D))
+    r = O.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=w.alpha, gamma=w.gamma,
+                  rows=rows, summaries=summ)
+    return rows, r["out"], r["w_bar"], r["margin"], r["mask"]
+
+
+def oracle_all_rows(w, block_rows=64, max_workers=16):
+    """The oracle over every row of workload `w`, with 64-row blocks dealt round-robin to
+    spawned worker processes (each regenerates the inputs from the seeded generator).
+    Returns out [B,Hq,T,D], w_bar, margin, mask [B,Hkv,T,nc]."""
+    import multiprocessing as mp
+    import os
+    T = w.T
+    nb = -(-T // block_rows)
+    nwork = max(1, min(max_workers, os.cpu_count() or 1, nb))
+    tasks = []
+    for i in range(nwork):
+        rows = np.concatenate([np.arange(b * block_rows, min(T, (b + 1) * block_rows))
+                               for b in range(i, nb, nwork)])
+        tasks.append((w, rows))
+    nc = -(-T // 64)
+    out = np.zeros((w.B, w.Hq, T, w.D))
+    wb = np.zeros((w.B, w.Hkv, T, nc))
+    mg = np.full((w.B, w.Hkv, T, nc), np.nan)
+    mk = np.zeros((w.B, w.Hkv, T, nc), bool)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(nwork) as pool:
+        for rows, o, b_, m_, k_ in pool.imap_unordered(oracle_rows_worker, tasks):
+            out[:, :, rows] = o
+            wb[:, :, rows] = b_
+            mg[:, :, rows] = m_
+            mk[:, :, rows] = k_
+    return out, wb, mg, mk

@@ -201,3 +201,15 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_prefill_stage_index_validation():
+    """dash_prefill_stage takes stage 0 (summaries), 1 (routing), 2 (attention) or 3 (the
+    chunk-transposed V copy); anything else is rejected before any launch."""
+    lib = _lib()
+    p = _params()
+    rc, need = _ws(p)
+    for stage in (-1, 4, 7):
+        assert lib.dash_prefill_stage(ctypes.byref(p), stage, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None, None, None, FAKE, need, None) == -1
+        assert b"stage" in lib.dash_last_error()
