@@ -175,6 +175,21 @@ int dash_decode_diag(const dash_params* p, const void* q, const void* k_cache,
                      const float* summary_cache, void* out, uint64_t* active_blocks,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* dash_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step's scratch (mask,
+ * weights, work lists, scores and split-K partials) lives in a fixed 32 MiB device array
+ * inside the library, one per GPU, held until the process ends; this call allocates
+ * nothing.  Shapes whose dash_decode_workspace_size() exceeds 32 MiB are rejected with
+ * DASH_ERR_WORKSPACE before anything is launched (the 64K-token, batch-16, 32/2-head
+ * decode needs about 20 MiB).  Every call on one GPU uses the same array, so calls that
+ * may overlap on one GPU (different streams, different host threads) race: serialise them.
+ * Nothing in the array needs clearing between calls.  Other arguments, results and errors
+ * as dash_decode. */
+int dash_decode_noalloc(const dash_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seq_lens,
+                        const float* summary_cache, void* out, uint64_t* active_blocks,
+                        void* stream);
+
 /* ---------------------------------------------------------------------------------
  * Chunk-summary cache append.  A summary, once its chunk is complete, is frozen and
  * cached (gist.science, "Stufe 0", efficiency remark): for each b this summarises every

@@ -3,6 +3,7 @@
 // Validation is plain host C++ and runs before any HIP call, so every error path can be
 // exercised without a GPU.  The library owns no device memory: callers pass workspaces
 // sized by the *_workspace_size() queries.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -176,11 +177,46 @@ hipError_t fill_f32(float* p, size_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Fixed device scratch for dash_decode_noalloc: one copy per GPU, alive until the process
+// ends.  Host code never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr and a message on failure).
+void* scratch_address(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(DASH_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(DASH_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *status = fail(DASH_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);   // same value from any thread
+  }
+  *status = DASH_OK;
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
 
-int dash_abi_version(void) { return 104; }
+int dash_abi_version(void) { return 105; }
 
 const char* dash_last_error(void) { return g_err.c_str(); }
 
@@ -515,6 +551,24 @@ int dash_decode_paged(const dash_params* p, const void* q, const void* k_pages,
   if (!block_table) return fail(DASH_ERR_INVALID_ARG, "block_table is NULL");
   return decode_impl(p, q, k_pages, v_pages, block_table, num_pages, seq_lens, summary_cache,
                      out, active_blocks, workspace, workspace_bytes, stream);
+}
+
+int dash_decode_noalloc(const dash_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seq_lens,
+                        const float* summary_cache, void* out, uint64_t* active_blocks,
+                        void* stream) {
+  Dims d;
+  if (int rc = check_params(p, &d)) return rc;
+  const size_t need = decode_layout(d).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(DASH_ERR_WORKSPACE,
+                "dash_decode_noalloc: this shape needs %zu bytes of scratch, above the fixed "
+                "%zu (use dash_decode with a workspace)", need, kNoAllocScratchBytes);
+  int st = DASH_OK;
+  void* ws = scratch_address(&st);
+  if (!ws) return st;
+  return decode_impl(p, q, k_cache, v_cache, nullptr, 0, seq_lens, summary_cache, out,
+                     active_blocks, ws, kNoAllocScratchBytes, stream);
 }
 
 int dash_append_chunk(const dash_params* p, const void* k_cache, const void* head_cls,

@@ -29,7 +29,7 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 EXPORTS = [
     "dash_abi_version", "dash_last_error",
     "dash_prefill_workspace_size", "dash_prefill", "dash_prefill_stage",
-    "dash_decode_workspace_size", "dash_decode", "dash_decode_diag",
+    "dash_decode_workspace_size", "dash_decode", "dash_decode_diag", "dash_decode_noalloc",
     "dash_append_chunk", "dash_decode_paged", "dash_decode_paged_diag", "dash_append_chunk_paged",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
 ]
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_decode.restype = ctypes.c_int
     lib.dash_decode_diag.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_decode_diag.restype = ctypes.c_int
+    lib.dash_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dash_decode_noalloc.restype = ctypes.c_int
     lib.dash_append_chunk.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.dash_append_chunk.restype = ctypes.c_int
     i32 = ctypes.c_int32
@@ -216,6 +218,27 @@ def decode(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha
                                   _ptr(seq_lens), _ptr(summary_cache), _ptr(out), _ptr(ab),
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
     return (out, ab) if return_active_blocks else out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, summary_cache, *, chunk_size=64, alpha=1.5,
+                   gamma=1.0, sm_scale=None, sigma=1.0, topk=0, enable_gqa=False, out=None,
+                   active_blocks=None, stream=None):
+    """`decode` through dash_decode_noalloc: the library's fixed device scratch instead of a
+    workspace, so the call allocates nothing itself (pass `out`, and `active_blocks` if
+    wanted, preallocated).  Calls overlapping on one GPU race on that scratch."""
+    B, Hq, D = q.shape
+    Hkv, T_max = k_cache.shape[1], k_cache.shape[2]
+    p = make_params(B, Hq, Hkv, T_max, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
+                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma,
+                    topk=topk)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(load().dash_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(seq_lens), _ptr(summary_cache), _ptr(out),
+                                      _ptr(active_blocks), _stream(stream)))
+    return out
 
 
 def append_chunk(k_cache, head_cls, seq_lens, summary_cache, n_summarized, *, chunk_size=64,

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = _lib()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.dash_abi_version() == 104
+    assert lib.dash_abi_version() == 105
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
@@ -213,3 +213,15 @@ def test_prefill_stage_index_validation():
         assert lib.dash_prefill_stage(ctypes.byref(p), stage, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       None, None, None, FAKE, need, None) == -1
         assert b"stage" in lib.dash_last_error()
+
+
+def test_decode_noalloc_rejects_oversize_on_host():
+    """dash_decode_noalloc checks the shape's scratch need against its fixed array before any
+    HIP call: an oversize shape is DASH_ERR_WORKSPACE even without a GPU."""
+    lib = _lib()
+    p = _params(B=64, Hq=32, Hkv=2, T=64 * 2049)
+    rc = lib.dash_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert rc == -5
+    assert b"scratch" in lib.dash_last_error()
+    assert lib.dash_decode_noalloc(ctypes.byref(_params(alpha=1.0)), FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, None, None) == -1
