@@ -128,6 +128,37 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
                  float* block_weights, float* summary_out, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Training: the forward that keeps what the backward pass needs, and the backward pass.
+ * The pages' central claim is that the hierarchy is differentiable end to end: the routing
+ * distribution is alpha-entmax, whose Jacobian exists almost everywhere, so gradients flow
+ * from the token-level attention through the routing back to the chunk summaries and
+ * Stage 0's classifier query (gist.science, "Stufe 1", remark on differentiability, and
+ * "Hauptbeiträge"; aixai.ru, the section on why top-k routing breaks gradients).  The entmax
+ * Jacobian is that of Peters, Niculae and Martins (2019), to which aixai.ru's FAQ points.
+ *
+ * dash_prefill_train: dash_prefill (same arguments, same out) that also writes
+ *   lse [B, Hq, T] float32: for each head and row, the natural log of the sum over the
+ *   row's attended keys of exp(logit), logit = sm_scale <q, k_j> + the key's log-prior.
+ * dash_prefill_backward: gradients of a loss L given dout = dL/dout [B, Hq, T, D] (dtype),
+ *   the forward's q, k, v, head_cls, out and lse, and the same dash_params:
+ *   dq [B, Hq, T, D], dk, dv [B, Hkv, T, D] (dtype), dhead_cls [Hkv, D] (float32),
+ *   all written (not accumulated).  Stage 0 and Stage 1 are recomputed from q, k and
+ *   head_cls with the forward's kernels, so the routing is the forward's.  A chunk whose
+ *   entmax argument sits exactly on the threshold gets the one-sided gradient with the
+ *   chunk outside the support.  Alpha-entmax routing only: topk > 0 or
+ *   estimate_diagonal = 1 is DASH_ERR_UNSUPPORTED.  workspace: at least
+ *   dash_prefill_backward_workspace_size() bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------------- */
+int dash_prefill_train(const dash_params* p, const void* q, const void* k, const void* v,
+                       const void* head_cls, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int dash_prefill_backward_workspace_size(const dash_params* p, size_t* bytes);
+int dash_prefill_backward(const dash_params* p, const void* q, const void* k, const void* v,
+                          const void* head_cls, const void* out, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* dhead_cls,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Profiling aid: run one step of dash_prefill alone (stage 0: the chunk summaries; 1:
  * routing; 2: sparse attention; 3: the chunk-transposed copy of V that bf16 Stage 2 reads,
  * a no-op for fp32), reading the intermediates that a complete dash_prefill call with the

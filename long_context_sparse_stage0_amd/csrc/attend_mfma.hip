@@ -476,6 +476,9 @@ void k_attend_mfma(AttendArgs a) {
     const float l = lsum[qt];               // full column sum (every lane of the column)
     const float rl = 1.0f / l;
     if (!qok[qt]) continue;
+    if (a.lse != nullptr && lg == 0)
+      a.lse[(size_t)(b * a.Hq + qh[qt]) * T + row0 + qrow[qt]] =
+          (m[qt] + fast_log2(l)) * 0.69314718055994531f;
     bf16* op = (bf16*)a.out + ((size_t)(b * a.Hq + qh[qt]) * T + row0 + qrow[qt]) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {

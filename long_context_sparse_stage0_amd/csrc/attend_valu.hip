@@ -96,6 +96,8 @@ __global__ __launch_bounds__(64) void k_attend_valu(AttendArgs a) {
   const float rl = 1.0f / l;
 #pragma unroll
   for (int e = 0; e < E; ++e) op[lane * E + e] = from_f32<TIn>(o[e] * rl);
+  if (a.lse != nullptr && lane == 0 && a.seq_lens == nullptr)
+    a.lse[(size_t)(b * a.Hq + h) * a.Tq + t] = (m + fast_log2(l)) * 0.69314718055994531f;
 }
 
 hipError_t launch_attend_valu(const AttendArgs& a, hipStream_t s) {

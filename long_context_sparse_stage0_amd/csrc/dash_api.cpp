@@ -231,7 +231,8 @@ int dash_prefill_workspace_size(const dash_params* p, size_t* bytes) {
 static int prefill_impl(const dash_params* p, int stages, const void* q, const void* k,
                         const void* v, const void* head_cls, void* out,
                         uint64_t* active_blocks, float* block_weights, float* summary_out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        float* lse = nullptr) {
   Dims d;
   if (int rc = check_params(p, &d)) return rc;
   if (p->topk > 0 && d.dtype != DASH_BF16)
@@ -342,6 +343,7 @@ static int prefill_impl(const dash_params* p, int stages, const void* q, const v
   aa.sigma = d.sigma;
   aa.dtype = d.dtype;
   aa.dense = 0;
+  aa.lse = lse;
   if (d.dtype == DASH_BF16) {
     aa.vt = ws + L.vt;
     if ((e = dash::launch_attend_mfma(aa, s)) != hipSuccess)
@@ -358,6 +360,170 @@ int dash_prefill(const dash_params* p, const void* q, const void* k, const void*
                  size_t workspace_bytes, void* stream) {
   return prefill_impl(p, 15, q, k, v, head_cls, out, active_blocks, block_weights, summary_out,
                       workspace, workspace_bytes, stream);
+}
+
+int dash_prefill_train(const dash_params* p, const void* q, const void* k, const void* v,
+                       const void* head_cls, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (int rc = check_ptr(lse, "lse")) return rc;
+  return prefill_impl(p, 15, q, k, v, head_cls, out, nullptr, nullptr, nullptr, workspace,
+                      workspace_bytes, stream, lse);
+}
+
+namespace {
+
+struct BackwardLayout {
+  PrefillLayout fwd;
+  size_t tau, z, dq32, dk32, dv32, dwb, dsumm, dhcp, total;
+};
+
+BackwardLayout backward_layout(const Dims& d) {
+  BackwardLayout L;
+  L.fwd = prefill_layout(d);
+  size_t off = L.fwd.total;
+  const size_t rows_q = (size_t)d.B * d.Hq * d.T, rows_kv = (size_t)d.B * d.Hkv * d.T;
+  L.tau = off;
+  off += align256(rows_q * 4);
+  L.z = off;
+  off += align256(rows_q * 4);
+  L.dq32 = off;
+  off += align256(rows_q * d.D * 4);
+  L.dk32 = off;
+  off += align256(rows_kv * d.D * 4);
+  L.dv32 = off;
+  off += align256(rows_kv * d.D * 4);
+  L.dwb = off;
+  off += align256(rows_kv * d.nc * 4);
+  L.dsumm = off;
+  off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
+  L.dhcp = off;
+  off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
+  L.total = off;
+  return L;
+}
+
+int check_backward_params(const dash_params* p, Dims* d) {
+  if (int rc = check_params(p, d)) return rc;
+  if (p->topk > 0)
+    return fail(DASH_ERR_UNSUPPORTED, "the backward pass is built for alpha-entmax routing only (topk = %d)", p->topk);
+  if (p->estimate_diagonal != 0)
+    return fail(DASH_ERR_UNSUPPORTED, "the backward pass is built with estimate_diagonal = 0 only");
+  return DASH_OK;
+}
+
+}  // namespace
+
+int dash_prefill_backward_workspace_size(const dash_params* p, size_t* bytes) {
+  Dims d;
+  if (int rc = check_backward_params(p, &d)) return rc;
+  if (!bytes) return fail(DASH_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = backward_layout(d).total;
+  return ok();
+}
+
+int dash_prefill_backward(const dash_params* p, const void* q, const void* k, const void* v,
+                          const void* head_cls, const void* out, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* dhead_cls,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  if (int rc = check_backward_params(p, &d)) return rc;
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(k, "k")) return rc;
+  if (int rc = check_ptr(v, "v")) return rc;
+  if (int rc = check_ptr(head_cls, "head_cls")) return rc;
+  if (int rc = check_ptr(out, "out")) return rc;
+  if (int rc = check_ptr(dout, "dout")) return rc;
+  if (int rc = check_ptr(lse, "lse")) return rc;
+  if (int rc = check_ptr(dq, "dq")) return rc;
+  if (int rc = check_ptr(dk, "dk")) return rc;
+  if (int rc = check_ptr(dv, "dv")) return rc;
+  if (int rc = check_ptr(dhead_cls, "dhead_cls")) return rc;
+  const BackwardLayout L = backward_layout(d);
+  if (int rc = check_ws(workspace, workspace_bytes, L.total)) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  float* summ = reinterpret_cast<float*>(ws + L.fwd.summ);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(ws + L.fwd.mask);
+  float* wbar = reinterpret_cast<float*>(ws + L.fwd.wbar);
+  float* tau = reinterpret_cast<float*>(ws + L.tau);
+  float* zn = reinterpret_cast<float*>(ws + L.z);
+  // Stages 0 and 1 again, as the forward ran them, keeping each head's threshold
+  void* ss = d.dtype == DASH_BF16 ? (void*)(ws + L.fwd.ssplit) : nullptr;
+  if ((e = dash::launch_stage0(k, head_cls, summ, ss, d.B, d.Hkv, d.T, d.D, d.nc, d.nfull,
+                               nullptr, nullptr, d.scale, d.dtype, s)) != hipSuccess)
+    return hip_fail(e, "stage 0 launch");
+  if (d.dtype == DASH_BF16) {
+    if ((e = dash::launch_vtranspose(v, ws + L.fwd.vt, d.B, d.Hkv, d.T, d.D, d.nc, s)) != hipSuccess)
+      return hip_fail(e, "V transpose launch");
+  }
+  dash::RouteArgs ra{};
+  ra.q = q;
+  ra.summ = summ;
+  ra.mask = mask;
+  ra.wbar = wbar;
+  ra.B = d.B;
+  ra.Hq = d.Hq;
+  ra.Hkv = d.Hkv;
+  ra.D = d.D;
+  ra.Tq = d.T;
+  ra.rows = d.T;
+  ra.nc_alloc = d.nc;
+  ra.W = d.W;
+  ra.wbar_ld = d.nc;
+  ra.tcap = d.T;
+  ra.alpha = d.alpha;
+  ra.zscale = (d.alpha - 1.0f) * d.gamma * d.scale;
+  ra.dtype = d.dtype;
+  ra.tau_out = tau;
+  ra.z_out = zn;
+  e = d.dtype == DASH_BF16 ? dash::launch_route_mfma(ra, ss, s) : dash::launch_route_valu(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "stage 1 launch");
+  // accumulators that the kernels add into
+  if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dk32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+      (e = fill_f32(reinterpret_cast<float*>(ws + L.dv32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+      (e = fill_f32(reinterpret_cast<float*>(ws + L.dwb), (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess ||
+      (e = fill_f32(reinterpret_cast<float*>(ws + L.dsumm), (size_t)d.B * d.Hkv * d.nc * d.D, 0.f, s)) != hipSuccess)
+    return hip_fail(e, "clearing the gradient accumulators");
+  dash::BackwardArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.vt = d.dtype == DASH_BF16 ? ws + L.fwd.vt : nullptr;
+  ba.head_cls = head_cls;
+  ba.out = out;
+  ba.dout = dout;
+  ba.lse = lse;
+  ba.summ = summ;
+  ba.ssplit = reinterpret_cast<const dash::bf16*>(ss);
+  ba.mask = mask;
+  ba.wbar = wbar;
+  ba.tau = tau;
+  ba.z = zn;
+  ba.dq32 = reinterpret_cast<float*>(ws + L.dq32);
+  ba.dk32 = reinterpret_cast<float*>(ws + L.dk32);
+  ba.dv32 = reinterpret_cast<float*>(ws + L.dv32);
+  ba.dwb = reinterpret_cast<float*>(ws + L.dwb);
+  ba.dsumm = reinterpret_cast<float*>(ws + L.dsumm);
+  ba.dhc_part = reinterpret_cast<float*>(ws + L.dhcp);
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dhead_cls = dhead_cls;
+  ba.B = d.B;
+  ba.Hq = d.Hq;
+  ba.Hkv = d.Hkv;
+  ba.T = d.T;
+  ba.D = d.D;
+  ba.nc = d.nc;
+  ba.W = d.W;
+  ba.scale = d.scale;
+  ba.gamma = d.gamma;
+  ba.alpha = d.alpha;
+  ba.sigma = d.sigma;
+  ba.dtype = d.dtype;
+  if ((e = dash::launch_backward_valu(ba, s)) != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
 }
 
 int dash_prefill_stage(const dash_params* p, int stage, const void* q, const void* k,

@@ -93,6 +93,8 @@ struct RouteArgs {
   const int32_t* kdiag_bt;  // estimate_diagonal, paged decode: block table [B][kdiag_bt_ld] of
   int kdiag_bt_ld;          // kdiag's page pool [num_pages][Hkv][64][D] (nullptr: contiguous)
   int kdiag_pages;
+  float* tau_out;         // prefill, entmax (nullable): each head's threshold tau and
+  float* z_out;           // normaliser z = sum [y - tau]_+^(1/(alpha-1)), [B, Hq, Tq] each
 };
 
 struct AttendArgs {
@@ -115,7 +117,42 @@ struct AttendArgs {
   int32_t* seg_size;           // decode: the attend kernel's common segment size, for the combine
   const int32_t* list;    // decode: the route kernel's item lists (see RouteArgs)
   int list_ld;
+  float* lse;             // prefill (nullable): [B, Hq, Tq] natural-log sum of exp of each
+                          // row's biased logits
 };
+
+// Backward pass.  Inputs are the forward's tensors, dL/dout, the forward's log-sum-exp and the
+// recomputed Stage 0 / Stage 1 state; fp32 accumulators live in the backward workspace.
+struct BackwardArgs {
+  const void* q;          // [B, Hq, T, D]   dtype
+  const void* k;          // [B, Hkv, T, D]  dtype
+  const void* v;          // [B, Hkv, T, D]  dtype
+  const void* vt;         // bf16 chunk-transposed V [B, Hkv, nc, D, 64] (MFMA path)
+  const void* head_cls;   // [Hkv, D]        dtype
+  const void* out;        // [B, Hq, T, D]   dtype, the forward's output
+  const void* dout;       // [B, Hq, T, D]   dtype, dL/dout
+  const float* lse;       // [B, Hq, T] natural-log sum of exp of each row's biased logits
+  const float* summ;      // [B, Hkv, nc, D] fp32 summaries
+  const bf16* ssplit;     // bf16 hi/lo split summaries (MFMA path; see split_offset)
+  const uint64_t* mask;   // [B, Hkv, T, W]
+  const float* wbar;      // [B, Hkv, T, nc] (valid at set bits)
+  const float* tau;       // [B, Hq, T] each head's entmax threshold
+  const float* z;         // [B, Hq, T] and normaliser
+  float* dq32;            // [B, Hq, T, D]  Stage 2's part of dq
+  float* dk32;            // [B, Hkv, T, D] Stage 2's part of dk
+  float* dv32;            // [B, Hkv, T, D]
+  float* dwb;             // [B, Hkv, T, nc] dL/dw_bar (valid at set bits)
+  float* dsumm;           // [B, Hkv, nc, D] dL/dk_bar
+  float* dhc_part;        // [B, Hkv, nc, D] per-chunk parts of dL/dhead_cls
+  void* dq;               // [B, Hq, T, D]   dtype (written)
+  void* dk;               // [B, Hkv, T, D]  dtype (written)
+  void* dv;               // [B, Hkv, T, D]  dtype (written)
+  float* dhead_cls;       // [Hkv, D] fp32 (written)
+  int B, Hq, Hkv, T, D, nc, W;
+  float scale, gamma, alpha, sigma;
+  int dtype;
+};
+hipError_t launch_backward_valu(const BackwardArgs& a, hipStream_t s);
 
 // summ_split (nullable, bf16 inputs only): bf16 hi and lo planes of the fp32 summaries
 // (hi = bf16(x), lo = bf16(x - hi)) for the MFMA router, tiled for its operand loads: per

@@ -411,6 +411,18 @@ __device__ __forceinline__ void route_rows(const RouteArgs& a, const bf16* __res
       for (int w = 0; w < NW; ++w) z += part[buf][qt][0][l16][w];
       zs[qt] = z;
     }
+    // thresholds and normalisers kept for the backward pass (one lane per query vector)
+    if (a.tau_out != nullptr && wv == 0 && lg == 0) {
+#pragma unroll
+      for (int qt = 0; qt < QTR; ++qt) {
+        const int n = 16 * qt + l16, t = row0 + n / G;
+        if (t < T) {
+          const size_t hi = (size_t)(b * a.Hq + kvh * G + n % G) * T + t;
+          a.tau_out[hi] = tau[qt];
+          a.z_out[hi] = zs[qt];
+        }
+      }
+    }
   }
 
   // ---- weights, GQA average, w_bar at active chunks, mask bits.  After the head sum all

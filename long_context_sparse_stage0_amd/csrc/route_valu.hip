@@ -99,6 +99,11 @@ __global__ __launch_bounds__(1024) void k_route_valu(RouteArgs a) {
     float z;
     const float tau = entmax_threshold<MODE, NR>(y, diag ? it + 1 : it, a.alpha, WaveReduce(), &z);
     const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
+    if (a.tau_out != nullptr && lane == 0 && a.seq_lens == nullptr) {
+      const size_t hi = (size_t)(b * a.Hq + h) * a.Tq + t;
+      a.tau_out[hi] = tau;
+      a.z_out[hi] = z;
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) p[r] = entmax_weight<MODE>(y[r], tau, inv, rz);
   } else {

@@ -32,6 +32,7 @@ EXPORTS = [
     "dash_decode_workspace_size", "dash_decode", "dash_decode_diag", "dash_decode_noalloc",
     "dash_append_chunk", "dash_decode_paged", "dash_decode_paged_diag", "dash_append_chunk_paged",
     "dash_dense_causal_workspace_size", "dash_dense_causal",
+    "dash_prefill_train", "dash_prefill_backward_workspace_size", "dash_prefill_backward",
 ]
 
 
@@ -69,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_abi_version.restype = ctypes.c_int
     lib.dash_last_error.restype = ctypes.c_char_p
     for name in ("dash_prefill_workspace_size", "dash_decode_workspace_size",
-                 "dash_dense_causal_workspace_size"):
+                 "dash_dense_causal_workspace_size", "dash_prefill_backward_workspace_size"):
         f = getattr(lib, name)
         f.argtypes = [P, ctypes.POINTER(sz)]
         f.restype = ctypes.c_int
@@ -94,6 +95,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_append_chunk_paged.restype = ctypes.c_int
     lib.dash_dense_causal.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dash_dense_causal.restype = ctypes.c_int
+    lib.dash_prefill_train.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dash_prefill_train.restype = ctypes.c_int
+    lib.dash_prefill_backward.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
+    lib.dash_prefill_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -131,7 +136,8 @@ def workspace_size(kind: str, params: DashParams) -> int:
     n = ctypes.c_size_t(0)
     f = {"prefill": load().dash_prefill_workspace_size,
          "decode": load().dash_decode_workspace_size,
-         "dense": load().dash_dense_causal_workspace_size}[kind]
+         "dense": load().dash_dense_causal_workspace_size,
+         "backward": load().dash_prefill_backward_workspace_size}[kind]
     _check(f(ctypes.byref(params), ctypes.byref(n)))
     return n.value
 
@@ -169,6 +175,45 @@ def prefill(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=
                                workspace.numel(), _stream(stream)))
     extras = [x for x in (ab, bw, sm) if x is not None]
     return (out, *extras) if extras else out
+
+
+def prefill_train(q, k, v, head_cls, *, chunk_size=64, alpha=1.5, gamma=1.0, sm_scale=None,
+                  sigma=1.0, enable_gqa=False, out=None, lse=None, workspace=None, stream=None):
+    """Causal prefill that also returns lse [B,Hq,T] fp32, the per-row log-sum-exp that
+    `prefill_backward` needs.  Returns (out, lse)."""
+    B, Hq, T, D = q.shape
+    p = make_params(B, Hq, k.shape[1], T, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
+                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size("prefill", p), q.device)
+    _check(load().dash_prefill_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(head_cls),
+                                     _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+    return out, lse
+
+
+def prefill_backward(q, k, v, head_cls, out, dout, lse, *, chunk_size=64, alpha=1.5,
+                     gamma=1.0, sm_scale=None, sigma=1.0, enable_gqa=False, workspace=None,
+                     stream=None):
+    """Gradients of L with dL/dout = dout through the whole prefill (the same parameters as
+    the forward).  Returns (dq, dk, dv, dhead_cls); dhead_cls is fp32."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    p = make_params(B, Hq, Hkv, T, D, chunk_size=chunk_size, alpha=alpha, gamma=gamma,
+                    sm_scale=sm_scale, enable_gqa=enable_gqa, dtype=q.dtype, sigma=sigma)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dhc = torch.empty((Hkv, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size("backward", p), q.device)
+    _check(load().dash_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(head_cls), _ptr(out), _ptr(dout), _ptr(lse),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dhc),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv, dhc
 
 
 def prefill_stage(stage, q, k, v, head_cls, out, workspace, *, alpha=1.5, gamma=1.0,

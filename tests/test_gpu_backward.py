@@ -1,0 +1,112 @@
+"""GPU parity of the backward pass (dash_prefill_train + dash_prefill_backward through the C
+ABI) against the float64 backward oracle, on seeded inputs and a seeded dL/dout.
+
+Tolerance (a reading: the pages fix none for gradients): the forward's output bar applied
+to each gradient relative to its scale, max |g - ref| / max(1, max |ref|) <= 1e-4 for fp32
+and 2e-2 for bf16.  A gradient is a sum over many rows of terms of the size the forward's
+bar covers, so its error grows with its magnitude; dividing by max(1, max |ref|) keeps the
+bar at the forward's where gradients are of order one.
+"""
+import numpy as np
+import pytest
+
+from long_context_sparse_stage0_amd import synth
+from long_context_sparse_stage0_amd.workloads import PREFILL_1K_FP32, Workload
+from oracle import dash_oracle as F
+from oracle import dash_oracle_backward as BW
+from tests.parity_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GRAD_TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dash():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_stage0_amd import dash as d
+    d.load()
+    return d
+
+
+def _dout(shape, dtype, seed):
+    g = np.random.default_rng(seed).normal(size=shape)
+    return synth.round_bf16(g) if dtype == "bf16" else g.astype(np.float32)
+
+
+def _check_grad(name, got, ref, dtype):
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    err = float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
+    assert err <= GRAD_TOL[dtype], f"{name}: relative max error {err:.3e} > {GRAD_TOL[dtype]}"
+    return err
+
+
+def run_backward(dash, w, *, alpha=None, sigma=1.0, seed=1):
+    alpha = w.alpha if alpha is None else alpha
+    x = synth.prefill_inputs(w)
+    dout = _dout(x["q"].shape, w.dtype, seed)
+    say(f"[backward] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} {w.dtype} "
+        f"alpha={alpha} sigma={sigma}")
+    q, k, v, hc = (to_dev(x[n], w.dtype) for n in ("q", "k", "v", "head_cls"))
+    do = to_dev(dout, w.dtype)
+    kw = dict(alpha=alpha, gamma=w.gamma, sigma=sigma, enable_gqa=w.enable_gqa)
+    out, lse = dash.prefill_train(q, k, v, hc, **kw)
+    plain = dash.prefill(q, k, v, hc, **kw)
+    dq, dk, dv, dhc = dash.prefill_backward(q, k, v, hc, out, do, lse, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain), "the training forward must equal dash_prefill"
+    ref = BW.prefill_backward(x["q"], x["k"], x["v"], x["head_cls"], dout, alpha=alpha,
+                              gamma=w.gamma, sigma=sigma)
+    errs = {n: _check_grad(n, g.float().cpu().numpy(), ref[n], w.dtype)
+            for n, g in (("dq", dq), ("dk", dk), ("dv", dv), ("dhead_cls", dhc))}
+    say("[backward]   " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    return x, ref
+
+
+def test_backward_1k_fp32(dash):
+    """The 1K fp32 workload (2 heads, D = 64, i.i.d. queries), every gradient."""
+    run_backward(dash, PREFILL_1K_FP32)
+
+
+@pytest.mark.parametrize("dtype,G,alpha,sigma,T,D", [
+    ("bf16", 4, 1.5, 1.0, 700, 128),      # ragged tail
+    ("bf16", 16, 1.5, 1.0, 400, 128),     # the 128K workload's head ratio
+    ("bf16", 2, 1.25, 0.5, 333, 64),
+    ("fp32", 2, 1.25, 0.5, 300, 64),      # the general-alpha Jacobian
+    ("fp32", 8, 1.5, 2.0, 450, 128),
+])
+def test_backward_small(dash, dtype, G, alpha, sigma, T, D):
+    w = Workload(name=f"bwd_{dtype}_g{G}", kind="prefill", B=2 if dtype == "bf16" else 1,
+                 Hq=2 * G, Hkv=2, T=T, D=D, dtype=dtype, alpha=alpha, seed=1200 + G,
+                 needle_amp=1.0)
+    _, ref = run_backward(dash, w, sigma=sigma, seed=G)
+    # the routing gradient is really exercised: it reaches Stage 0's classifier query
+    assert np.abs(ref["dhead_cls"]).max() > 1e-3
+
+
+def test_backward_sparsemax_away_from_ties(dash):
+    """alpha = 2 (sparsemax), whose Jacobian jumps where a chunk enters the support: on
+    inputs where no routed chunk lies within 1e-4 of a threshold, GPU and oracle gradients
+    agree."""
+    w = Workload(name="bwd_a2", kind="prefill", B=1, Hq=4, Hkv=2, T=500, D=64, dtype="fp32",
+                 alpha=2.0, seed=1300, needle_amp=1.0)
+    x = synth.prefill_inputs(w)
+    r = F.prefill(x["q"], x["k"], x["v"], x["head_cls"], alpha=2.0)
+    m = r["margin"]
+    assert np.nanmin(np.abs(m)) > 1e-4, "choose another seed: a chunk sits on a threshold"
+    run_backward(dash, w)
+
+
+def test_backward_tiny_sequences(dash):
+    """Degenerate lengths: one chunk with no routing (every gradient from the diagonal
+    branch; d head_cls = 0) and a partial second chunk."""
+    for T in (50, 100):
+        w = Workload(name=f"bwd_tiny{T}", kind="prefill", B=1, Hq=4, Hkv=2, T=T, D=64,
+                     dtype="fp32", seed=1400 + T, needle_amp=1.0)
+        _, ref = run_backward(dash, w)
+        # no routing (T = 50), or one routed chunk whose entmax weight is always 1
+        assert np.abs(ref["dhead_cls"]).max() < 1e-12
