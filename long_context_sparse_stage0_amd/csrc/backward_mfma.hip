@@ -1,0 +1,913 @@
+// Backward pass on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16) for bf16 inputs.
+//
+// Method: the gradient of the three-stage forward taken in reverse (gist.science summary of
+// arXiv 2605.18753, "Stufe 1: Entmax-Chunk-Routing", remark on differentiability, and
+// "Hauptbeiträge"); the alpha-entmax Jacobian is that of Peters, Niculae and Martins (2019):
+// s = p^(2 - alpha) on the support, dx = s (dp - rho), rho = (s . dp) / sum s.
+//
+// Kernels (launch order):
+//   k_bwd_delta     Delta = <dO, O> per (b, head, row).
+//   k_bwd_union     per (b, kv head, 64-row block) the OR of its rows' mask words.
+//   k_bwd_kbart     the fp32 summaries as a bf16 [d][chunk] plane (Stage 1's dq operand).
+//   k_bwd_dq_mfma   query-outer, the forward's work unit and union walk: per visit
+//                   S^T = K Q^T seeded with bias - lse (so the MFMA returns log2 P),
+//                   dP^T = V dO^T, dS = P (dP - Delta), dQ^T += K^T dS^T (K^T read from the
+//                   row-major K tile by transposing LDS reads); the routed chunk's
+//                   dL/dw_bar = sigma / w_bar * (sum of dS over its keys and the row's heads)
+//                   is written by one lane per row.
+//   k_bwd_dkdv_mfma chunk-outer: one workgroup per (b, kv head, chunk), each of its 4 waves
+//                   owning 16 keys; it walks the 64-row query blocks whose rows route to the
+//                   chunk (plus its own block, causally) in spans of 32 query vectors staged in
+//                   LDS: S = Q K^T and dP = dO V^T with the span's rows permuted so that P and
+//                   dS land in the lanes as the A operands of dV += P^T dO and dK += dS^T Q.
+//   k_bwd_route_dq  Stage 1, row-outer (the forward router's work unit, 16 query vectors on
+//                   8 waves): pass 1 recomputes the scores (hi + lo planes) and each head's
+//                   weights from its saved tau, z, and reduces sum s and sum s dp into rho;
+//                   pass 2 recomputes them, forms dx and adds dq += gamma scale dx K_bar on
+//                   MFMA (dx straight from the score registers, K_bar from the [d][chunk]
+//                   plane); writes the final dq and rho.
+//   k_bwd_route_dk  Stage 1, chunk-outer: one workgroup per (b, kv head, 16 chunks); its
+//                   waves take spans of 32 query vectors of the later rows, recompute the
+//                   span's scores as S = Q K_bar^T (rows permuted as in k_bwd_dkdv_mfma), form
+//                   dx with the saved rho and add dK_bar += dX^T Q; waves are summed in LDS.
+// Stage 0 backwards and the head_cls reduction use the generic kernels (backward_valu.hip).
+#include <type_traits>
+
+#include "route_common.h"
+
+namespace dash {
+
+namespace {
+
+constexpr int kXcdsB = 8;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor dword 3 (bounds-checked)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows)
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// sum over the G adjacent lanes of a 16-lane row that hold one row's heads (G a power of 2)
+__device__ __forceinline__ float heads_sum(float v, int G) {
+  if (G >= 2) v += dppf<0xB1>(v);     // quad_perm [1,0,3,2]
+  if (G >= 4) v += dppf<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (G >= 8) v += dppf<0x141>(v);    // row_half_mirror
+  if (G >= 16) v += dppf<0x140>(v);   // row_mirror
+  return v;
+}
+
+// XOR swizzle of the 16-byte chunk index inside a row of a [row][D] bf16 LDS tile (the
+// forward's K-tile swizzle): a quarter wave's 16-byte operand reads hit distinct slots.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int d) {       // byte offset of (row, d)
+  return row * (2 * D) + ((((d >> 3) ^ swz<D>(row))) << 4) + (d & 7) * 2;
+}
+// 16-byte operand read: row `row`, elements d0 .. d0 + 7 (d0 a multiple of 8)
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row8(const uint8_t* tile, int row, int d0) {
+  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D>(row, d0));
+}
+
+typedef short v4i16b __attribute__((ext_vector_type(4)));
+typedef short v8i16b __attribute__((ext_vector_type(8)));
+// Transposed operand from a row-major [row][D] swizzled tile: lane (l16, lg) receives
+// tile[r0 + 8 lg + i][d0 + l16] for i = 0..7, i.e. the 16x16x32 MFMA operand whose 16
+// rows/columns are tile columns d0 .. d0 + 15 and whose k-slots are tile rows.  Two
+// ds_read_b64_tr_b16: within a 16-lane group source lane 4k + q points at
+// tile[r + k][d0 + 4q .. + 3] and output lane i receives tile[r + 0..3][d0 + i].
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr8(const uint8_t* tile, int r0, int d0, int lane) {
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int k = l16 >> 2, q = l16 & 3;
+  const int ra = r0 + 8 * lg + k;
+  typedef __attribute__((address_space(3))) v4i16b lds_v4;
+  const v4i16b x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + tile_off<D>(ra, d0 + 4 * q)));
+  const v4i16b y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + tile_off<D>(ra + 4, d0 + 4 * q)));
+  const v8i16b r = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 v, float s) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * s);
+  return v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ prep
+// Delta[b, h, t] = <dO, O>: 16 lanes per row, D / 16 elements each.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_delta(BackwardArgs a, float* __restrict__ delta) {
+  constexpr int E = D / 16;
+  const size_t rows = (size_t)a.B * a.Hq * a.T;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16* dp = (const bf16*)a.dout + row * D + l * E;
+    const bf16* op = (const bf16*)a.out + row * D + l * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf((float)dp[e], (float)op[e], acc);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (row < rows && l == 0) delta[row] = acc;
+}
+
+// ub[bk][blk][w] = OR over the block's rows t < T of mask[bk][t][w]
+__global__ void k_bwd_union(BackwardArgs a, uint64_t* __restrict__ ub, int nblk) {
+  const int blk = blockIdx.x, bk = blockIdx.y;
+  for (int w = threadIdx.x; w < a.W; w += blockDim.x) {
+    uint64_t u = 0;
+    const int r1 = min(kChunk, a.T - blk * kChunk);
+    for (int r = 0; r < r1; ++r) u |= a.mask[((size_t)bk * a.T + blk * kChunk + r) * a.W + w];
+    ub[((size_t)bk * nblk + blk) * a.W + w] = u;
+  }
+}
+
+// kbt[bk][d][c] = bf16(summ[bk][c][d]) for the complete chunks, zero past them (up to ncp)
+__global__ void k_bwd_kbart(BackwardArgs a, bf16* __restrict__ kbt, int ncp) {
+  const int bk = blockIdx.y;
+  const int nfull = a.T / kChunk;
+  const size_t n = (size_t)a.D * ncp;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int d = (int)(i / ncp), c = (int)(i % ncp);
+    const float v = c < nfull ? a.summ[((size_t)bk * a.nc + c) * a.D + d] : 0.f;
+    kbt[(size_t)bk * n + i] = (bf16)v;
+  }
+}
+
+// ------------------------------------------------------------------------------ dQ, dw_bar
+template <int D, int NW, int RMAX>
+__global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const float* __restrict__ delta) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 32, NDT = D / 16;
+  constexpr int TB = 64 * 2 * D;                  // bytes of one 64-row tile
+  constexpr int SEGR = D / 8, SEG = 64 * SEGR, PT = SEG / NT;
+  static_assert(SEG % NT == 0, "tile segments must divide over the threads");
+  constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][TB];
+  __shared__ uint64_t rowbits[RMAX][MAXW];
+  __shared__ uint16_t visit[kMaxRouted + 2];
+  __shared__ int woff[MAXW + 1];
+
+  const int G = a.Hq / a.Hkv;
+  constexpr int R = RMAX;                          // rows per workgroup = NW * 16 / G
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = a.T;
+  const int BH = a.B * a.Hkv;
+  constexpr int RPB = kChunk / R;
+  const int nunits = ((T + kChunk - 1) / kChunk) * BH;
+  const int grp = kXcdsB * RPB;
+  const int xcd = (blockIdx.x % grp) % kXcdsB, sub = (blockIdx.x % grp) / kXcdsB;
+  const int unit = (blockIdx.x / grp) * kXcdsB + xcd;
+  if (unit >= nunits) return;
+  const int uu = nunits - 1 - unit;
+  const int bk = uu % BH;
+  const int rt = (uu / BH) * RPB + sub;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int row0 = rt * R;
+  const int it = row0 / kChunk;
+  const int W = a.W;
+
+  // ---- the union walk of the forward
+  const int nw_route = (it + 63) / 64;
+  for (int idx = tid; idx < R * nw_route; idx += NT) {
+    const int r = idx / nw_route, w = idx % nw_route;
+    const int t = row0 + r;
+    rowbits[r][w] = (t < T) ? a.mask[((size_t)bk * T + t) * W + w] : 0ull;
+  }
+  __syncthreads();
+  if (tid < nw_route) {
+    uint64_t u = 0;
+    for (int r = 0; r < R; ++r) u |= rowbits[r][tid];
+    woff[tid + 1] = __popcll(u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    woff[0] = 0;
+    for (int w = 0; w < nw_route; ++w) woff[w + 1] += woff[w];
+  }
+  __syncthreads();
+  if (tid < nw_route) {
+    uint64_t u = 0;
+    for (int r = 0; r < R; ++r) u |= rowbits[r][tid];
+    int o = woff[tid] + 1;
+    while (u) {
+      visit[o++] = (uint16_t)(64 * tid + __builtin_ctzll(u));
+      u &= u - 1;
+    }
+  }
+  if (tid == 0) visit[0] = (uint16_t)it;
+  __syncthreads();
+  const int nvis = woff[nw_route] + 1;
+
+  // ---- this lane's query column: one 16-column tile per wave
+  const int n = 16 * wv + l16, r = n / G, g = n % G;
+  const int t = row0 + r;
+  const bool qok = t < T;
+  const size_t qi = (size_t)(b * a.Hq + kvh * G + g) * T + (qok ? t : 0);
+  const float sl2 = a.scale * kLog2e;
+  bf16x8 qop[KS], dop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>((const bf16*)a.q + qi * D + 32 * ks + 8 * lg);
+    const bf16x8 dv = *reinterpret_cast<const bf16x8*>((const bf16*)a.dout + qi * D + 32 * ks + 8 * lg);
+    qop[ks] = qok ? scale_bf16x8(qv, sl2) : bf16x8{};
+    dop[ks] = qok ? dv : bf16x8{};
+  }
+  const float dlt = qok ? delta[qi] : 0.f;
+  const float lse2 = qok ? a.lse[qi] * kLog2e : 0.f;
+  const int tloc = t & 63;
+
+  // ---- K and V tiles: global -> registers -> LDS (both row-major, swizzled)
+  const bf16* kbase = (const bf16*)a.k + (size_t)bk * T * D;
+  const bf16* vbase = (const bf16*)a.v + (size_t)bk * T * D;
+  int goff[PT], loff[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int seg = tid + i * NT;
+    const int row = seg / SEGR, ch = seg % SEGR;
+    goff[i] = (row * D + ch * 8) * 2;
+    loff[i] = tile_off<D>(row, ch * 8);
+  }
+  uint4 kreg[PT], vreg[PT];
+  auto prefetch = [&](int c_any) {
+    const int c = __builtin_amdgcn_readfirstlane(c_any);
+    const int nbytes = min(T - c * kChunk, kChunk) * D * 2;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)c * kChunk * D), (short)0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (size_t)c * kChunk * D), (short)0, nbytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, goff[i], 0, 0));
+      vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, goff[i], 0, 0));
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      *reinterpret_cast<uint4*>(&lds_k[buf][loff[i]]) = kreg[i];
+      *reinterpret_cast<uint4*>(&lds_v[buf][loff[i]]) = vreg[i];
+    }
+  };
+  float wnext = 1.f;
+  bool onnext = false;
+  auto fetch_weight = [&](int c) {
+    onnext = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
+    wnext = a.wbar[((size_t)bk * T + (qok ? t : T - 1)) * a.nc + c];
+  };
+
+  floatx4 dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dq[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto visit_chunk = [&](int buf, int c, float bias2, float wb, auto diag_tag) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
+    asm volatile("" ::: "memory");
+    if (!DIAG && __builtin_amdgcn_ballot_w64(bias2 != -INFINITY) == 0ull) return;
+    const uint8_t* kl = lds_k[buf];
+    const uint8_t* vl = lds_v[buf];
+    const float sd = (DIAG ? 0.f : bias2) - lse2;
+    floatx4 sc[4], dpv[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = tile_row8<D>(kl, key, 32 * ks + 8 * lg);
+        const bf16x8 va = tile_row8<D>(vl, key, 32 * ks + 8 * lg);
+        sc[kt] = mma(ka, qop[ks], ks == 0 ? floatx4{sd, sd, sd, sd} : sc[kt]);
+        dpv[kt] = mma(va, dop[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : dpv[kt]);
+      }
+    }
+    // lane: column q = l16, keys 32 p + 8 lg + 4 half + j for kt = 2 p + half
+    float ds[16];
+    float dsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + j;
+        float x = sc[kt][j];
+        if (DIAG && key > tloc) x = -INFINITY;
+        const float p = fast_exp2(x);
+        const float v = qok ? p * (dpv[kt][j] - dlt) : 0.f;
+        ds[4 * kt + j] = v;
+        dsum += v;
+      }
+    bf16x8 dso[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dso[p][j] = (bf16)ds[8 * p + j];
+        dso[p][4 + j] = (bf16)ds[8 * p + 4 + j];
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dq[dt] = mma(tile_tr8<D>(kl, 32 * p, 16 * dt, lane), dso[p], dq[dt]);
+    if (!DIAG) {
+      // dL/dw_bar of this row and chunk: dS summed over the chunk's keys and the row's heads
+      const float s = heads_sum(rows_sum(dsum), G);
+      if (g == 0 && lg == 0 && qok && bias2 != -INFINITY)
+        a.dwb[((size_t)bk * T + t) * a.nc + c] = a.sigma * s / wb;
+    }
+  };
+
+  prefetch(visit[0]);
+  stash(0);
+  __syncthreads();
+  if (1 < nvis) {
+    prefetch(visit[1]);
+    fetch_weight(visit[1]);
+  }
+  visit_chunk(0, it, 0.f, 0.f, std::true_type{});
+  for (int v = 1; v < nvis; ++v) {
+    const int buf = v & 1;
+    stash(buf);
+    const int c = visit[v];
+    const float wb = wnext;
+    const float bias2 = onnext ? a.sigma * fast_log2(wnext) : -INFINITY;
+    __syncthreads();
+    if (v + 1 < nvis) {
+      prefetch(visit[v + 1]);
+      fetch_weight(visit[v + 1]);
+    }
+    visit_chunk(buf, c, bias2, wb, std::false_type{});
+  }
+  if (qok) {
+    float* dst = a.dq32 + qi * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * lg) =
+          make_float4(a.scale * dq[dt][0], a.scale * dq[dt][1], a.scale * dq[dt][2], a.scale * dq[dt][3]);
+  }
+}
+
+// ------------------------------------------------------------------------------ dK, dV
+// One workgroup per (b, kv head, chunk c); wave w owns keys c*64 + 16 w + [0, 16).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const float* __restrict__ delta,
+                                                       const uint64_t* __restrict__ ub, int nblk) {
+  constexpr int NW = 4, NT = 256;
+  constexpr int KS = D / 32, NDT = D / 16;
+  constexpr int SB = 32 * 2 * D;                  // bytes of a 32-row span tile
+  constexpr int SEGR = D / 8, SEG = 32 * SEGR, PT = SEG / NT;
+  static_assert(SEG % NT == 0, "span segments must divide over the threads");
+  __shared__ __attribute__((aligned(16))) uint8_t lq[2][SB];
+  __shared__ __attribute__((aligned(16))) uint8_t ldo[2][SB];
+  __shared__ float qinfo[2][4][32];               // lse2, delta, bias2, t (as float)
+  __shared__ uint16_t blist[kMaxRouted + 2];
+  __shared__ int nbl_s;
+
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = a.T;
+  const int c = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const float sl2 = a.scale * kLog2e;
+
+  // ---- query blocks whose rows route to chunk c: its own block first, then every later
+  // block whose union mask has bit c
+  if (wv == 0) {
+    int cnt = 1;
+    if (lane == 0) blist[0] = (uint16_t)c;
+    for (int b0 = c + 1; b0 < nblk; b0 += 64) {
+      const int blk = b0 + lane;
+      const bool on = blk < nblk &&
+                      ((ub[((size_t)bk * nblk + blk) * a.W + (c >> 6)] >> (c & 63)) & 1ull);
+      const uint64_t m = __ballot(on);
+      if (on) blist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)blk;
+      cnt += __popcll(m);
+    }
+    if (lane == 0) nbl_s = cnt;
+  }
+  __syncthreads();
+  const int nbl = nbl_s;
+  const int nspan_b = 2 * G;                      // 32-vector spans per 64-row block
+  const int nspan = nbl * nspan_b;
+
+  // ---- this wave's keys as B operands (columns = keys)
+  const int key = c * kChunk + 16 * wv + l16;
+  const bool kok = key < T;
+  bf16x8 kb[KS], vb[KS];
+  {
+    const bf16* kp = (const bf16*)a.k + ((size_t)bk * T + (kok ? key : 0)) * D;
+    const bf16* vp = (const bf16*)a.v + ((size_t)bk * T + (kok ? key : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(kp + 32 * ks + 8 * lg);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(vp + 32 * ks + 8 * lg);
+      kb[ks] = kok ? x : bf16x8{};
+      vb[ks] = kok ? y : bf16x8{};
+    }
+  }
+  const int kloc = 16 * wv + l16;                 // key within the chunk
+
+  // ---- span loads: rows m < 32 of span s of block blk are query vectors n = 32 s' + m of
+  // the block (n = row * G + head); Q scaled by sm_scale * log2 e and rounded to bf16 as in
+  // the forward
+  int srow[PT], scol[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int seg = tid + i * NT;
+    srow[i] = seg / SEGR;
+    scol[i] = (seg % SEGR) * 8;
+  }
+  uint4 qreg[PT], oreg[PT];
+  float inf_next = 0.f;                           // this thread's qinfo entry (tid < 128)
+  auto span_src = [&](int s, int m, int* tt) {    // global row index of span row m
+    const int blk = blist[s / nspan_b], sp = s % nspan_b;
+    const int nn = 32 * sp + m, rr = nn / G, gg = nn % G;
+    const int tr = blk * kChunk + rr;
+    *tt = tr;
+    return (size_t)(b * a.Hq + kvh * G + gg) * T + (tr < T ? tr : 0);
+  };
+  auto prefetch = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      int tr;
+      const size_t gi = span_src(s, srow[i], &tr);
+      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+      if (tr < T) {
+        bf16x8 qv = *reinterpret_cast<const bf16x8*>((const bf16*)a.q + gi * D + scol[i]);
+        x = __builtin_bit_cast(uint4, scale_bf16x8(qv, sl2));
+        y = *reinterpret_cast<const uint4*>((const bf16*)a.dout + gi * D + scol[i]);
+      }
+      qreg[i] = x;
+      oreg[i] = y;
+    }
+    if (tid < 128) {
+      const int kind = tid >> 5, m = tid & 31;
+      int tr;
+      const size_t gi = span_src(s, m, &tr);
+      const int blk = blist[s / nspan_b];
+      float v;
+      if (kind == 0) v = tr < T ? a.lse[gi] * kLog2e : 0.f;
+      else if (kind == 1) v = tr < T ? delta[gi] : 0.f;
+      else if (kind == 2) {
+        if (tr >= T) v = -INFINITY;
+        else if (blk == c) v = 0.f;               // the block's own chunk: no prior
+        else {
+          const size_t ri = (size_t)bk * T + tr;
+          const bool on = (a.mask[ri * a.W + (c >> 6)] >> (c & 63)) & 1ull;
+          v = on ? a.sigma * fast_log2(a.wbar[ri * a.nc + c]) : -INFINITY;
+        }
+      } else v = (float)tr;
+      inf_next = v;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      *reinterpret_cast<uint4*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) = qreg[i];
+      *reinterpret_cast<uint4*>(&ldo[buf][tile_off<D>(srow[i], scol[i])]) = oreg[i];
+    }
+    if (tid < 128) qinfo[buf][tid >> 5][tid & 31] = inf_next;
+  };
+
+  floatx4 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (nspan > 0) prefetch(0);
+  for (int s = 0; s < nspan; ++s) {
+    const int buf = s & 1;
+    stash(buf);
+    const bool own = blist[s / nspan_b] == c;
+    __syncthreads();
+    if (s + 1 < nspan) prefetch(s + 1);
+    const uint8_t* ql = lq[buf];
+    const uint8_t* ol = ldo[buf];
+    // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- span row
+    // 8 (l16 / 4) + 4 h + l16 % 4, so lane (l16, lg) holds span rows 8 lg + 4 h + i
+    floatx4 sv[2], dpv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sv[h] = mma(tile_row8<D>(ql, m, 32 * ks + 8 * lg), kb[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sv[h]);
+        dpv[h] = mma(tile_row8<D>(ol, m, 32 * ks + 8 * lg), vb[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : dpv[h]);
+      }
+    }
+    bf16x8 pa, dsa;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 8 * lg + 4 * h + i;
+        float x = sv[h][i] + qinfo[buf][2][m] - qinfo[buf][0][m];
+        if (own && kloc > (int)qinfo[buf][3][m] - c * kChunk) x = -INFINITY;
+        if (!kok) x = -INFINITY;
+        const float p = fast_exp2(x);
+        pa[4 * h + i] = (bf16)p;
+        dsa[4 * h + i] = (bf16)(p * (dpv[h][i] - qinfo[buf][1][m]));
+      }
+    // dV += P^T dO, dK += dS^T Q (B operands: the span tiles read transposed)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      dv[dt] = mma(pa, tile_tr8<D>(ol, 0, 16 * dt, lane), dv[dt]);
+      dk[dt] = mma(dsa, tile_tr8<D>(ql, 0, 16 * dt, lane), dk[dt]);
+    }
+  }
+  // lane holds rows (keys) 16 wv + 4 lg + i, column d = 16 dt + l16.  dK = s sum dS q
+  // = ln 2 * sum dS (q sm_scale log2 e).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = c * kChunk + 16 * wv + 4 * lg + i;
+    if (kk >= T) continue;
+    const size_t ro = ((size_t)bk * T + kk) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      a.dk32[ro + 16 * dt + l16] = kLn2 * dk[dt][i];
+      ((bf16*)a.dv)[ro + 16 * dt + l16] = (bf16)dv[dt][i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ Stage 1
+// Scores of this lane's column (query vector) against 16 chunks 16 ct + l16 (A rows) on the
+// hi and lo planes, as in the forward router: C[4 lg + i][l16] = chunk 16 ct + 4 lg + i.
+template <int D>
+__device__ __forceinline__ floatx4 route_scores(const bf16* sp, const bf16x8 (&qop)[D / 32], int ct,
+                                                int it, int l16, int lg) {
+  constexpr int KS = D / 32;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int crow = 16 * ct + l16;
+  const bool cok = crow < it;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 hi = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 0, 32 * ks + 8 * lg, D));
+    bf16x8 lo = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 1, 32 * ks + 8 * lg, D));
+    if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
+    acc = mma(hi, qop[ks], acc);
+    acc = mma(lo, qop[ks], acc);
+  }
+  return acc;
+}
+
+template <int MODE>
+__device__ __forceinline__ float jac_s(float p, float alpha) {   // p^(2 - alpha), p > 0
+  if (MODE == kAlpha15) return sqrtf(p);
+  if (MODE == kAlpha2) return 1.f;
+  return pow_pos(p, 2.0f - alpha);
+}
+
+// Row-outer: 16 query vectors (R = 16 / G rows of one block) on 8 waves; wave w takes the
+// 16-chunk tiles w, w + 8, ...
+template <int D, int MODE>
+__global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16* __restrict__ kbt,
+                                                     int ncp, float* __restrict__ rho_out) {
+  constexpr int NW = 8, KS = D / 32, NDT = D / 16;
+  __shared__ float part[2][NW][16];
+  __shared__ float dqs[NW][16][D + 4];
+  const int G = a.Hq / a.Hkv;
+  const int R = 16 / G;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = a.T;
+  const int BH = a.B * a.Hkv;
+  const int ntile_r = (T + R - 1) / R;
+  const int w_id = gridDim.x - 1 - blockIdx.x;    // late (heavy) rows first
+  const int rt = w_id / BH, bk = w_id % BH;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int row0 = rt * R;
+  const int it = row0 / kChunk;
+  (void)ntile_r;
+  const int n = l16, r = n / G, g = n % G;
+  const int t = row0 + r;
+  const bool qok = t < T;
+  const size_t qi = (size_t)(b * a.Hq + kvh * G + g) * T + (qok ? t : 0);
+  const size_t rowi = (size_t)bk * T + (qok ? t : 0);
+  bf16x8 qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 qv = *reinterpret_cast<const bf16x8*>((const bf16*)a.q + qi * D + 32 * ks + 8 * lg);
+    qop[ks] = qok ? qv : bf16x8{};
+  }
+  const float gs = a.gamma * a.scale;
+  const float zscale = (a.alpha - 1.0f) * gs;
+  const float inv = 1.0f / (a.alpha - 1.0f), rG = 1.0f / (float)G;
+  const bool act = qok && it > 0;
+  const float tau = act ? a.tau[qi] : 0.f;
+  const float rz = act ? 1.0f / a.z[qi] : 0.f;
+  const bf16* sp = a.ssplit + (size_t)bk * split_bk_stride(a.nc, D);
+  const int ntile = (it + 15) / 16;
+  const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
+
+  // s and dp of the lane's 4 chunks of tile ct
+  auto sdp = [&](int ct, float (&s4)[4], float (&dp4)[4]) {
+    const floatx4 acc = route_scores<D>(sp, qop, ct, it, l16, lg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cc = 16 * ct + 4 * lg + i;
+      s4[i] = 0.f;
+      dp4[i] = 0.f;
+      if (act && cc < it) {
+        const float p = entmax_weight<MODE>(zscale * acc[i], tau, inv, rz);
+        if (p > 0.f) {
+          s4[i] = jac_s<MODE>(p, a.alpha);
+          const bool on = (a.mask[rowi * a.W + (cc >> 6)] >> (cc & 63)) & 1ull;
+          dp4[i] = on ? a.dwb[rowi * a.nc + cc] * rG : 0.f;
+        }
+      }
+    }
+  };
+  // ---- pass 1: sum s and sum s dp per query vector
+  float ss = 0.f, sd = 0.f;
+  for (int j = 0; j < nj; ++j) {
+    float s4[4], dp4[4];
+    sdp(wv + NW * j, s4, dp4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ss += s4[i];
+      sd = fmaf(s4[i], dp4[i], sd);
+    }
+  }
+  ss = rows_sum(ss);
+  sd = rows_sum(sd);
+  if (lg == 0) {
+    part[0][wv][l16] = ss;
+    part[1][wv][l16] = sd;
+  }
+  __syncthreads();
+  float sst = 0.f, sdt = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    sst += part[0][w][l16];
+    sdt += part[1][w][l16];
+  }
+  const float rho = sst > 0.f ? sdt / sst : 0.f;
+  if (wv == 0 && lg == 0 && qok) rho_out[qi] = rho;
+  // ---- pass 2: dx, and dq += gs * dX K_bar over pairs of tiles (k-slots i < 4: tile a,
+  // chunks 16 ta + 4 lg + i; i >= 4: tile b, chunks 16 tb + 4 lg + i - 4)
+  floatx4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bf16* kb = kbt + (size_t)bk * D * ncp;
+  for (int j = 0; j < nj; j += 2) {
+    const int ta = wv + NW * j, tb = wv + NW * (j + 1);
+    const bool hasb = j + 1 < nj;
+    bf16x8 xa;
+    {
+      float s4[4], dp4[4];
+      sdp(ta, s4, dp4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
+      if (hasb) {
+        sdp(tb, s4, dp4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)0.f;
+      }
+    }
+    const int cb = hasb ? tb : ta;                // any valid tile: its operand is times 0
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16* kr = kb + (size_t)(16 * dt + l16) * ncp;
+      typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(kr + 16 * ta + 4 * lg);
+      const bf16x4 y = *reinterpret_cast<const bf16x4*>(kr + 16 * cb + 4 * lg);
+      const bf16x8 bop = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+      acc[dt] = mma(xa, bop, acc[dt]);
+    }
+  }
+  // lane: C[4 lg + i][l16] = (query vector 4 lg + i, d = 16 dt + l16); sum the waves in LDS
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dqs[wv][4 * lg + i][16 * dt + l16] = acc[dt][i];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * D; idx += 512) {
+    const int nn = idx / D, d = idx % D;
+    const int rr = nn / G, gg = nn % G, tt = row0 + rr;
+    if (tt >= T) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += dqs[w][nn][d];
+    const size_t o = ((size_t)(b * a.Hq + kvh * G + gg) * T + tt) * D + d;
+    ((bf16*)a.dq)[o] = (bf16)(a.dq32[o] + v);
+  }
+}
+
+// Chunk-outer: one workgroup per (b, kv head, 16-chunk tile ct); 8 waves take spans of 32
+// query vectors (n = row * G + head) of the rows t >= 64 (16 ct + 1).  dK_bar (16 chunks x D)
+// of each wave is summed in LDS.
+template <int D, int MODE>
+__global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const float* __restrict__ rho) {
+  constexpr int NW = 8, KS = D / 32, NDT = D / 16;
+  constexpr int SB = 32 * 2 * D;
+  __shared__ __attribute__((aligned(16))) uint8_t lq[NW][SB];
+  __shared__ float red[16][D + 4];
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int T = a.T;
+  const int ct = blockIdx.x, bk = blockIdx.y;
+  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const float gs = a.gamma * a.scale;
+  const float zscale = (a.alpha - 1.0f) * gs;
+  const float inv = 1.0f / (a.alpha - 1.0f), rG = 1.0f / (float)G;
+  const int c = 16 * ct + l16;                    // this lane's chunk (B column)
+  const bool cok = c < a.nc;
+  // B operands: K_bar^T columns = chunks (hi and lo planes of the split summaries)
+  const bf16* sp = a.ssplit + (size_t)bk * split_bk_stride(a.nc, D);
+  bf16x8 khi[KS], klo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    khi[ks] = *reinterpret_cast<const bf16x8*>(sp + split_offset(c, 0, 32 * ks + 8 * lg, D));
+    klo[ks] = *reinterpret_cast<const bf16x8*>(sp + split_offset(c, 1, 32 * ks + 8 * lg, D));
+    if (!cok) { khi[ks] = bf16x8{}; klo[ks] = bf16x8{}; }
+  }
+  // rows that may route to this tile: t >= 64 (16 ct + 1); spans of 32 query vectors
+  const int t0 = kChunk * (16 * ct + 1);
+  const long long nq = t0 < T ? (long long)(T - t0) * G : 0;
+  const int nspan = (int)((nq + 31) / 32);
+  floatx4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  uint8_t* myq = lq[wv];
+  for (int s = wv; s < nspan; s += NW) {
+    // stage the span's 32 query rows in this wave's LDS tile (row m <- vector n0 + m)
+    const long long n0 = (long long)s * 32;
+    for (int i = lane; i < 32 * (D / 8); i += 64) {
+      const int m = i / (D / 8), d0 = (i % (D / 8)) * 8;
+      const long long nn = n0 + m;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (nn < nq) {
+        const int tt = t0 + (int)(nn / G), gg = (int)(nn % G);
+        x = *reinterpret_cast<const uint4*>((const bf16*)a.q + ((size_t)(b * a.Hq + kvh * G + gg) * T + tt) * D + d0);
+      }
+      *reinterpret_cast<uint4*>(myq + tile_off<D>(m, d0)) = x;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    // S = Q K_bar^T with span rows permuted (lane holds rows 8 lg + 4 h + i of column c)
+    floatx4 sv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+      sv[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = tile_row8<D>(myq, m, 32 * ks + 8 * lg);
+        sv[h] = mma(qa, khi[ks], sv[h]);
+        sv[h] = mma(qa, klo[ks], sv[h]);
+      }
+    }
+    bf16x8 xa;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 8 * lg + 4 * h + i;
+        const long long nn = n0 + m;
+        float dx = 0.f;
+        if (nn < nq && cok) {
+          const int tt = t0 + (int)(nn / G), gg = (int)(nn % G);
+          if (c < tt / kChunk) {
+            const size_t qi = (size_t)(b * a.Hq + kvh * G + gg) * T + tt;
+            const float p = entmax_weight<MODE>(zscale * sv[h][i], a.tau[qi], inv, 1.0f / a.z[qi]);
+            if (p > 0.f) {
+              const size_t ri = (size_t)bk * T + tt;
+              const bool on = (a.mask[ri * a.W + (c >> 6)] >> (c & 63)) & 1ull;
+              const float dp = on ? a.dwb[ri * a.nc + c] * rG : 0.f;
+              dx = gs * jac_s<MODE>(p, a.alpha) * (dp - rho[qi]);
+            }
+          }
+        }
+        xa[4 * h + i] = (bf16)dx;
+      }
+    // dK_bar (chunks x d) += dX^T Q: A = dX^T (row = chunk l16, k-slots = span rows),
+    // B = Q read transposed from the span tile
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma(xa, tile_tr8<D>(myq, 0, 16 * dt, lane), acc[dt]);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // sum the waves: C[4 lg + i][l16] = (chunk 16 ct + 4 lg + i, d = 16 dt + l16)
+  for (int w = 0; w < NW; ++w) {
+    if (wv == w) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float& dst = red[4 * lg + i][16 * dt + l16];
+          dst = (w == 0) ? acc[dt][i] : dst + acc[dt][i];
+        }
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < 16 * D; idx += 512) {
+    const int cc = 16 * ct + idx / D, d = idx % D;
+    if (cc < a.nc) a.dsumm[((size_t)bk * a.nc + cc) * D + d] = red[idx / D][d];
+  }
+}
+
+// ------------------------------------------------------------------------------ launcher
+int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delta, size_t* off_ub,
+                          size_t* off_kbt, size_t* off_rho, size_t* total) {
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const int nc = (T + kChunk - 1) / kChunk, W = (nc + 63) / 64, ncp = 32 * ((nc + 31) / 32);
+  size_t o = 0;
+  *off_delta = o;
+  o += al((size_t)B * Hq * T * 4);
+  *off_ub = o;
+  o += al((size_t)B * Hkv * nc * W * 8);
+  *off_kbt = o;
+  o += al((size_t)B * Hkv * D * ncp * 2);
+  *off_rho = o;
+  o += al((size_t)B * Hq * T * 4);
+  *total = o;
+  return 0;
+}
+
+template <int D>
+static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, hipStream_t s) {
+  size_t od, ou, ok, orho, tot;
+  backward_mfma_scratch(a.B, a.Hq, a.Hkv, a.T, a.D, &od, &ou, &ok, &orho, &tot);
+  float* delta = reinterpret_cast<float*>(scratch + od);
+  uint64_t* ub = reinterpret_cast<uint64_t*>(scratch + ou);
+  bf16* kbt = reinterpret_cast<bf16*>(scratch + ok);
+  float* rho = reinterpret_cast<float*>(scratch + orho);
+  const int G = a.Hq / a.Hkv;
+  const int BH = a.B * a.Hkv;
+  const int nblk = a.nc;                          // 64-row query blocks = chunks
+  const int ncp = 32 * ((a.nc + 31) / 32);
+  const size_t rows = (size_t)a.B * a.Hq * a.T;
+  k_bwd_delta<D><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a, delta);
+  k_bwd_union<<<dim3(nblk, BH), 64, 0, s>>>(a, ub, nblk);
+  k_bwd_kbart<<<dim3(64, BH), 256, 0, s>>>(a, kbt, ncp);
+  // dQ (Stage 2's part) and dw_bar
+  {
+    const int NW = G >= 2 ? 8 : 4;
+    const int R = NW * 16 / G;
+    const int nunits = nblk * BH;
+    dim3 grid(((nunits + kXcdsB - 1) / kXcdsB) * kXcdsB * (kChunk / R));
+    switch (G) {
+      case 16: k_bwd_dq_mfma<D, 8, 8><<<grid, 512, 0, s>>>(a, delta); break;
+      case 8: k_bwd_dq_mfma<D, 8, 16><<<grid, 512, 0, s>>>(a, delta); break;
+      case 4: k_bwd_dq_mfma<D, 8, 32><<<grid, 512, 0, s>>>(a, delta); break;
+      case 2: k_bwd_dq_mfma<D, 8, 64><<<grid, 512, 0, s>>>(a, delta); break;
+      default: k_bwd_dq_mfma<D, 4, 64><<<grid, 256, 0, s>>>(a, delta); break;
+    }
+  }
+  // dK (Stage 2's part) and dV
+  k_bwd_dkdv_mfma<D><<<dim3(a.nc, BH), 256, 0, s>>>(a, delta, ub, nblk);
+  // Stage 1: dq (final) and rho, then dK_bar
+  {
+    const int R = 16 / G;
+    dim3 grid((unsigned)(((a.T + R - 1) / R) * BH));
+    const int ntc = (a.nc + 15) / 16;
+    if (a.alpha == 1.5f) {
+      k_bwd_route_dq<D, kAlpha15><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dk<D, kAlpha15><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+    } else if (a.alpha == 2.0f) {
+      k_bwd_route_dq<D, kAlpha2><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dk<D, kAlpha2><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+    } else {
+      k_bwd_route_dq<D, kAlphaGeneral><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dk<D, kAlphaGeneral><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_mfma(const BackwardArgs& a, void* scratch, hipStream_t s) {
+  return a.D == 128 ? launch_backward_mfma_t<128>(a, (char*)scratch, s)
+                    : launch_backward_mfma_t<64>(a, (char*)scratch, s);
+}
+
+}  // namespace dash

@@ -19,8 +19,9 @@
 //                     dx = s (dp - rho); dq += gamma scale dx k_bar (final dq written);
 //                     d k_bar += gamma scale dx q by atomics.
 //   k_bwd_stage0      one wave per (b, kv head, chunk): Stage 0's softmax backwards,
-//                     dk = dk(Stage 2) + pi d k_bar + scale da head_cls (final dk and dv
-//                     written), and the chunk's part of d head_cls.
+//                     dk = dk(Stage 2) + pi d k_bar + scale da head_cls (final dk, and dv
+//                     from its fp32 accumulator when there is one), and the chunk's part of
+//                     d head_cls.  Also run after the MFMA kernels (backward_mfma.hip).
 //   k_bwd_reduce_hc   d head_cls summed over batch and chunks in a fixed order.
 #include "route_common.h"
 
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64) void k_bwd_stage0(BackwardArgs a) {
       for (int e = 0; e < E; ++e) {
         const size_t i = base + (size_t)j * D + lane * E + e;
         ((TIn*)a.dk)[i] = from_f32<TIn>(a.dk32[i]);
-        ((TIn*)a.dv)[i] = from_f32<TIn>(a.dv32[i]);
+        if (a.dv32 != nullptr) ((TIn*)a.dv)[i] = from_f32<TIn>(a.dv32[i]);
       }
 #pragma unroll
     for (int e = 0; e < E; ++e) dhp[lane * E + e] = 0.f;
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(64) void k_bwd_stage0(BackwardArgs a) {
       const size_t i = base + (size_t)j * D + lane * E + e;
       const float kv = to_f32(kc[(size_t)j * D + lane * E + e]);
       ((TIn*)a.dk)[i] = from_f32<TIn>(a.dk32[i] + pj * gv[e] + a.scale * daj * hcv[e]);
-      ((TIn*)a.dv)[i] = from_f32<TIn>(a.dv32[i]);
+      if (a.dv32 != nullptr) ((TIn*)a.dv)[i] = from_f32<TIn>(a.dv32[i]);
       dh[e] = fmaf(daj, kv, dh[e]);
     }
   }
@@ -295,6 +296,11 @@ static hipError_t launch_backward_valu_t(const BackwardArgs& a, hipStream_t s) {
     k_bwd_route_row<TIn, D, kAlpha2><<<dim3(a.T, a.Hkv, a.B), 64 * G, 0, s>>>(a);
   else
     k_bwd_route_row<TIn, D, kAlphaGeneral><<<dim3(a.T, a.Hkv, a.B), 64 * G, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename TIn, int D>
+static hipError_t launch_backward_stage0_t(const BackwardArgs& a, hipStream_t s) {
   k_bwd_stage0<TIn, D><<<dim3(a.nc, a.Hkv, a.B), 64, 0, s>>>(a);
   k_bwd_reduce_hc<<<a.Hkv, 128, 0, s>>>(a);
   return hipGetLastError();
@@ -304,6 +310,12 @@ hipError_t launch_backward_valu(const BackwardArgs& a, hipStream_t s) {
   if (a.dtype == 0)
     return a.D == 128 ? launch_backward_valu_t<bf16, 128>(a, s) : launch_backward_valu_t<bf16, 64>(a, s);
   return a.D == 128 ? launch_backward_valu_t<float, 128>(a, s) : launch_backward_valu_t<float, 64>(a, s);
+}
+
+hipError_t launch_backward_stage0(const BackwardArgs& a, hipStream_t s) {
+  if (a.dtype == 0)
+    return a.D == 128 ? launch_backward_stage0_t<bf16, 128>(a, s) : launch_backward_stage0_t<bf16, 64>(a, s);
+  return a.D == 128 ? launch_backward_stage0_t<float, 128>(a, s) : launch_backward_stage0_t<float, 64>(a, s);
 }
 
 }  // namespace dash

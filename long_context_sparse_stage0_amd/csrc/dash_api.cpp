@@ -374,7 +374,7 @@ namespace {
 
 struct BackwardLayout {
   PrefillLayout fwd;
-  size_t tau, z, dq32, dk32, dv32, dwb, dsumm, dhcp, total;
+  size_t tau, z, dq32, dk32, dv32, dwb, dsumm, dhcp, mscratch, total;
 };
 
 BackwardLayout backward_layout(const Dims& d) {
@@ -398,6 +398,12 @@ BackwardLayout backward_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
   L.dhcp = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
+  L.mscratch = off;          // bf16: the MFMA kernels' delta, block unions, K_bar^T, rho
+  if (d.dtype == DASH_BF16) {
+    size_t o1, o2, o3, o4, tot;
+    dash::backward_mfma_scratch(d.B, d.Hq, d.Hkv, d.T, d.D, &o1, &o2, &o3, &o4, &tot);
+    off += align256(tot);
+  }
   L.total = off;
   return L;
 }
@@ -479,12 +485,14 @@ int dash_prefill_backward(const dash_params* p, const void* q, const void* k, co
   ra.z_out = zn;
   e = d.dtype == DASH_BF16 ? dash::launch_route_mfma(ra, ss, s) : dash::launch_route_valu(ra, s);
   if (e != hipSuccess) return hip_fail(e, "stage 1 launch");
-  // accumulators that the kernels add into
-  if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dk32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
-      (e = fill_f32(reinterpret_cast<float*>(ws + L.dv32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
-      (e = fill_f32(reinterpret_cast<float*>(ws + L.dwb), (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess ||
-      (e = fill_f32(reinterpret_cast<float*>(ws + L.dsumm), (size_t)d.B * d.Hkv * d.nc * d.D, 0.f, s)) != hipSuccess)
-    return hip_fail(e, "clearing the gradient accumulators");
+  // accumulators that the generic (fp32) kernels add into
+  if (d.dtype != DASH_BF16) {
+    if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dk32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+        (e = fill_f32(reinterpret_cast<float*>(ws + L.dv32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+        (e = fill_f32(reinterpret_cast<float*>(ws + L.dwb), (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess ||
+        (e = fill_f32(reinterpret_cast<float*>(ws + L.dsumm), (size_t)d.B * d.Hkv * d.nc * d.D, 0.f, s)) != hipSuccess)
+      return hip_fail(e, "clearing the gradient accumulators");
+  }
   dash::BackwardArgs ba{};
   ba.q = q;
   ba.k = k;
@@ -522,7 +530,14 @@ int dash_prefill_backward(const dash_params* p, const void* q, const void* k, co
   ba.alpha = d.alpha;
   ba.sigma = d.sigma;
   ba.dtype = d.dtype;
-  if ((e = dash::launch_backward_valu(ba, s)) != hipSuccess) return hip_fail(e, "backward launch");
+  if (d.dtype == DASH_BF16) {
+    if ((e = dash::launch_backward_mfma(ba, ws + L.mscratch, s)) != hipSuccess)
+      return hip_fail(e, "backward launch");
+    ba.dv32 = nullptr;                 // dv is final already
+  } else {
+    if ((e = dash::launch_backward_valu(ba, s)) != hipSuccess) return hip_fail(e, "backward launch");
+  }
+  if ((e = dash::launch_backward_stage0(ba, s)) != hipSuccess) return hip_fail(e, "Stage 0 backward launch");
   return ok();
 }
 

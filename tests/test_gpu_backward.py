@@ -76,6 +76,8 @@ def test_backward_1k_fp32(dash):
     ("bf16", 4, 1.5, 1.0, 700, 128),      # ragged tail
     ("bf16", 16, 1.5, 1.0, 400, 128),     # the 128K workload's head ratio
     ("bf16", 2, 1.25, 0.5, 333, 64),
+    ("bf16", 1, 1.5, 1.0, 260, 64),       # no GQA (the 4-wave dQ instance)
+    ("bf16", 8, 2.0, 1.0, 530, 128),
     ("fp32", 2, 1.25, 0.5, 300, 64),      # the general-alpha Jacobian
     ("fp32", 8, 1.5, 2.0, 450, 128),
 ])
@@ -110,3 +112,53 @@ def test_backward_tiny_sequences(dash):
         _, ref = run_backward(dash, w)
         # no routing (T = 50), or one routed chunk whose entmax weight is always 1
         assert np.abs(ref["dhead_cls"]).max() < 1e-12
+
+
+def test_backward_bf16_dq_rows_and_dv_sum_at_8k(dash):
+    """The MFMA backward at T = 8192 (32/2 heads): dq on sampled rows against the oracle's
+    per-row backward (Stage 2 of each head, the GQA mean, the entmax Jacobian and the
+    Stage 1 scores of that row), and a property of the whole dv: the attention weights of
+    a row sum to one, so dv summed over the keys of a KV head equals dO summed over its
+    rows and query heads."""
+    from long_context_sparse_stage0_amd.workloads import CALIBRATED_AMP
+    w = Workload(name="bwd_8k", kind="prefill", B=1, Hq=32, Hkv=2, T=8192, D=128,
+                 dtype="bf16", seed=1500, needle_amp=CALIBRATED_AMP)
+    x = synth.prefill_inputs(w)
+    dout = _dout(x["q"].shape, "bf16", 15)
+    say("[backward] 8K, 32/2 heads, sampled dq rows and the dv sum")
+    q, k, v, hc = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "head_cls"))
+    kw = dict(enable_gqa=True)
+    out, lse = dash.prefill_train(q, k, v, hc, **kw)
+    dq, dk, dv, dhc = dash.prefill_backward(q, k, v, hc, out, to_dev(dout, "bf16"), lse, **kw)
+    torch.cuda.synchronize()
+    g_dq = dq.float().cpu().numpy()
+    g_dv = dv.float().cpu().numpy()
+    assert np.isfinite(g_dq).all() and np.isfinite(g_dv).all()
+    assert np.isfinite(dk.float().cpu().numpy()).all() and np.isfinite(dhc.cpu().numpy()).all()
+    # dv property
+    for kvh in range(2):
+        lhs = g_dv[0, kvh].astype(np.float64).sum(axis=0)
+        rhs = dout[0, 16 * kvh:16 * (kvh + 1)].astype(np.float64).sum(axis=(0, 1))
+        err = np.abs(lhs - rhs).max() / max(1.0, np.abs(rhs).max())
+        assert err <= 2e-2, f"dv sum, kv head {kvh}: {err:.3e}"
+    # dq on sampled rows: the oracle's backward of one row
+    scale = 1.0 / np.sqrt(w.D)
+    summ = F.chunk_summaries(x["k"], x["head_cls"], scale)
+    rows = [64, 127, 4095, 4096, 8191]
+    for t in rows:
+        for kvh in range(2):
+            qg = x["q"][0, 16 * kvh:16 * (kvh + 1), t].astype(np.float64)
+            wb, _, p = F.route_row(qg, summ[0, kvh], t, alpha=1.5, gamma=1.0, scale=scale)
+            dwb = np.zeros(t // 64)
+            ref = np.zeros((16, w.D))
+            for g in range(16):
+                dq_h, _, _, dwb_h = BW.attend_row_backward(
+                    qg[g], x["k"][0, kvh], x["v"][0, kvh], t, wb,
+                    dout[0, 16 * kvh + g, t], scale=scale)
+                ref[g] = dq_h
+                dwb += dwb_h
+            if t // 64 > 0:
+                dx = BW.entmax_backward(p, np.broadcast_to(dwb / 16, p.shape), 1.5)
+                ref += scale * (dx @ summ[0, kvh, :t // 64])
+            _check_grad(f"dq row {t} kv head {kvh}", g_dq[0, 16 * kvh:16 * (kvh + 1), t], ref,
+                        "bf16")
