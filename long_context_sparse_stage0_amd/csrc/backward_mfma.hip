@@ -15,21 +15,25 @@
 //                   row-major K tile by transposing LDS reads); the routed chunk's
 //                   dL/dw_bar = sigma / w_bar * (sum of dS over its keys and the row's heads)
 //                   is written by one lane per row.
-//   k_bwd_dkdv_mfma chunk-outer: one workgroup per (b, kv head, chunk), each of its 4 waves
-//                   owning 16 keys; it walks the 64-row query blocks whose rows route to the
-//                   chunk (plus its own block, causally) in spans of 32 query vectors staged in
-//                   LDS: S = Q K^T and dP = dO V^T with the span's rows permuted so that P and
-//                   dS land in the lanes as the A operands of dV += P^T dO and dK += dS^T Q.
+//   k_bwd_dkdv_mfma chunk-outer: one workgroup per (b, kv head, range of 64 query blocks,
+//                   chunk) with 8 waves, two per 16 keys; it walks the range's 64-row query
+//                   blocks whose rows route to the chunk (and its own block, causally) in
+//                   spans of 64 query vectors staged in LDS, each wave taking 32 of them: S = Q K^T and dP = dO V^T with the
+//                   span's rows permuted so that P and dS land in the lanes as the A operands of
+//                   dV += P^T dO and dK += dS^T Q, added into fp32 accumulators by atomics.
+//                   Workgroups are dispatched range by range, so the ones in flight share one
+//                   range's queries and output gradients through the caches.
 //   k_bwd_route_dq  Stage 1, row-outer (the forward router's work unit, 16 query vectors on
 //                   8 waves): pass 1 recomputes the scores (hi + lo planes) and each head's
 //                   weights from its saved tau, z, and reduces sum s and sum s dp into rho;
 //                   pass 2 recomputes them, forms dx and adds dq += gamma scale dx K_bar on
 //                   MFMA (dx straight from the score registers, K_bar from the [d][chunk]
 //                   plane); writes the final dq and rho.
-//   k_bwd_route_dk  Stage 1, chunk-outer: one workgroup per (b, kv head, 16 chunks); its
-//                   waves take spans of 32 query vectors of the later rows, recompute the
-//                   span's scores as S = Q K_bar^T (rows permuted as in k_bwd_dkdv_mfma), form
-//                   dx with the saved rho and add dK_bar += dX^T Q; waves are summed in LDS.
+//   k_bwd_route_dk  Stage 1, chunk-outer: one workgroup per (b, kv head, 16 chunks, slice of
+//                   8192 query vectors of the later rows); its waves take spans of 32 vectors,
+//                   recompute the span's scores as S = Q K_bar^T (rows permuted as in
+//                   k_bwd_dkdv_mfma), form dx with the saved rho and add dK_bar += dX^T Q;
+//                   waves are summed in LDS and added into dK_bar by atomics.
 // Stage 0 backwards and the head_cls reduction use the generic kernels (backward_valu.hip).
 #include <type_traits>
 
@@ -43,6 +47,8 @@ constexpr int kXcdsB = 8;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer descriptor dword 3 (bounds-checked)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kBwdRange = 64;            // query blocks per dK/dV workgroup range
+constexpr int kBwdSlice = 8192;          // query vectors per Stage 1 dK_bar workgroup
 
 __device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -371,37 +377,42 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const f
 }
 
 // ------------------------------------------------------------------------------ dK, dV
-// One workgroup per (b, kv head, chunk c); wave w owns keys c*64 + 16 w + [0, 16).
+// One workgroup per (b, kv head, block range, chunk c) with 8 waves: wave w owns keys
+// c*64 + 16 (w % 4) + [0, 16) and takes half w / 4 (32 vectors) of every 64-vector span.
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const float* __restrict__ delta,
+__global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const float* __restrict__ delta,
                                                        const uint64_t* __restrict__ ub, int nblk) {
-  constexpr int NW = 4, NT = 256;
+  constexpr int NT = 512, SPAN = 64;
   constexpr int KS = D / 32, NDT = D / 16;
-  constexpr int SB = 32 * 2 * D;                  // bytes of a 32-row span tile
-  constexpr int SEGR = D / 8, SEG = 32 * SEGR, PT = SEG / NT;
+  constexpr int SB = SPAN * 2 * D;                // bytes of a span tile
+  constexpr int SEGR = D / 8, SEG = SPAN * SEGR, PT = SEG / NT;
   static_assert(SEG % NT == 0, "span segments must divide over the threads");
   __shared__ __attribute__((aligned(16))) uint8_t lq[2][SB];
   __shared__ __attribute__((aligned(16))) uint8_t ldo[2][SB];
-  __shared__ float qinfo[2][4][32];               // lse2, delta, bias2, t (as float)
+  __shared__ float qinfo[2][4][SPAN];             // lse2, delta, bias2, t (as float)
   __shared__ uint16_t blist[kMaxRouted + 2];
   __shared__ int nbl_s;
 
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int kg = wv & 3, half_q = wv >> 2;        // key group, half of the span
   const int T = a.T;
-  const int c = blockIdx.x, bk = blockIdx.y;
+  const int c = blockIdx.x, rg = blockIdx.y, bk = blockIdx.z;
+  const int blo = kBwdRange * rg, bhi = min(nblk, blo + kBwdRange);   // this range's blocks
+  if (c >= bhi) return;                           // (whole workgroup)
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const float sl2 = a.scale * kLog2e;
 
-  // ---- query blocks whose rows route to chunk c: its own block first, then every later
-  // block whose union mask has bit c
+  // ---- query blocks of the range whose rows route to chunk c: its own block first (when
+  // in the range), then every later block whose union mask has bit c
   if (wv == 0) {
-    int cnt = 1;
-    if (lane == 0) blist[0] = (uint16_t)c;
-    for (int b0 = c + 1; b0 < nblk; b0 += 64) {
+    const bool own_in = c >= blo;
+    int cnt = own_in ? 1 : 0;
+    if (lane == 0 && own_in) blist[0] = (uint16_t)c;
+    for (int b0 = max(c + 1, blo); b0 < bhi; b0 += 64) {
       const int blk = b0 + lane;
-      const bool on = blk < nblk &&
+      const bool on = blk < bhi &&
                       ((ub[((size_t)bk * nblk + blk) * a.W + (c >> 6)] >> (c & 63)) & 1ull);
       const uint64_t m = __ballot(on);
       if (on) blist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)blk;
@@ -411,11 +422,12 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   }
   __syncthreads();
   const int nbl = nbl_s;
-  const int nspan_b = 2 * G;                      // 32-vector spans per 64-row block
-  const int nspan = nbl * nspan_b;
+  if (nbl == 0) return;                           // (whole workgroup)
+  const int nspan = nbl * G;                      // 64-vector spans (G per 64-row block)
 
   // ---- this wave's keys as B operands (columns = keys)
-  const int key = c * kChunk + 16 * wv + l16;
+  const int kloc = 16 * kg + l16;                 // key within the chunk
+  const int key = c * kChunk + kloc;
   const bool kok = key < T;
   bf16x8 kb[KS], vb[KS];
   {
@@ -429,11 +441,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
       vb[ks] = kok ? y : bf16x8{};
     }
   }
-  const int kloc = 16 * wv + l16;                 // key within the chunk
 
-  // ---- span loads: rows m < 32 of span s of block blk are query vectors n = 32 s' + m of
-  // the block (n = row * G + head); Q scaled by sm_scale * log2 e and rounded to bf16 as in
-  // the forward
+  // ---- span loads: row m < 64 of span s of block blk is query vector n = 64 s' + m of the
+  // block (n = row * G + head); Q scaled by sm_scale * log2 e and rounded to bf16 as in the
+  // forward
   int srow[PT], scol[PT];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
@@ -441,16 +452,19 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     srow[i] = seg / SEGR;
     scol[i] = (seg % SEGR) * 8;
   }
-  uint4 qreg[PT], oreg[PT];
-  float inf_next = 0.f;                           // this thread's qinfo entry (tid < 128)
+  // two register sets: the loads of spans s + 1 and s + 2 are in flight while span s computes
+  uint4 qreg[2][PT], oreg[2][PT];
+  float inf_next[2] = {0.f, 0.f};                 // this thread's qinfo entry (tid < 256)
+  const int lgG = __builtin_ctz(G);               // G is a power of two
   auto span_src = [&](int s, int m, int* tt) {    // global row index of span row m
-    const int blk = blist[s / nspan_b], sp = s % nspan_b;
-    const int nn = 32 * sp + m, rr = nn / G, gg = nn % G;
+    const int blk = blist[s >> lgG], sp = s & (G - 1);
+    const int nn = SPAN * sp + m, rr = nn >> lgG, gg = nn & (G - 1);
     const int tr = blk * kChunk + rr;
     *tt = tr;
     return (size_t)(b * a.Hq + kvh * G + gg) * T + (tr < T ? tr : 0);
   };
-  auto prefetch = [&](int s) {
+  auto prefetch = [&](int s, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       int tr;
@@ -461,14 +475,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
         x = __builtin_bit_cast(uint4, scale_bf16x8(qv, sl2));
         y = *reinterpret_cast<const uint4*>((const bf16*)a.dout + gi * D + scol[i]);
       }
-      qreg[i] = x;
-      oreg[i] = y;
+      qreg[S][i] = x;
+      oreg[S][i] = y;
     }
-    if (tid < 128) {
-      const int kind = tid >> 5, m = tid & 31;
+    if (tid < 4 * SPAN) {
+      const int kind = tid / SPAN, m = tid % SPAN;
       int tr;
       const size_t gi = span_src(s, m, &tr);
-      const int blk = blist[s / nspan_b];
+      const int blk = blist[s >> lgG];
       float v;
       if (kind == 0) v = tr < T ? a.lse[gi] * kLog2e : 0.f;
       else if (kind == 1) v = tr < T ? delta[gi] : 0.f;
@@ -481,16 +495,17 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
           v = on ? a.sigma * fast_log2(a.wbar[ri * a.nc + c]) : -INFINITY;
         }
       } else v = (float)tr;
-      inf_next = v;
+      inf_next[S] = v;
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto set_tag) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      *reinterpret_cast<uint4*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) = qreg[i];
-      *reinterpret_cast<uint4*>(&ldo[buf][tile_off<D>(srow[i], scol[i])]) = oreg[i];
+      *reinterpret_cast<uint4*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) = qreg[S][i];
+      *reinterpret_cast<uint4*>(&ldo[buf][tile_off<D>(srow[i], scol[i])]) = oreg[S][i];
     }
-    if (tid < 128) qinfo[buf][tid >> 5][tid & 31] = inf_next;
+    if (tid < 4 * SPAN) qinfo[buf][tid / SPAN][tid % SPAN] = inf_next[S];
   };
 
   floatx4 dk[NDT], dv[NDT];
@@ -500,21 +515,28 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (nspan > 0) prefetch(0);
-  for (int s = 0; s < nspan; ++s) {
-    const int buf = s & 1;
-    stash(buf);
-    const bool own = blist[s / nspan_b] == c;
+  const int r0 = 32 * half_q;                     // this wave's 32 rows of the span tile
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  prefetch(0, S0{});
+  if (1 < nspan) prefetch(1, S1{});
+  // span s: its registers (set s & 1) go to LDS buffer s & 1, which span s - 2 read before
+  // every wave passed the barrier of span s - 1; then the set is refilled with span s + 2
+  auto span_step = [&](int s, auto set_tag) {
+    constexpr int SS = decltype(set_tag)::value;
+    const int buf = SS;
+    stash(buf, set_tag);
+    const bool own = blist[s >> lgG] == c;
     __syncthreads();
-    if (s + 1 < nspan) prefetch(s + 1);
+    if (s + 2 < nspan) prefetch(s + 2, set_tag);
     const uint8_t* ql = lq[buf];
     const uint8_t* ol = ldo[buf];
-    // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- span row
-    // 8 (l16 / 4) + 4 h + l16 % 4, so lane (l16, lg) holds span rows 8 lg + 4 h + i
+    // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- tile row
+    // r0 + 8 (l16 / 4) + 4 h + l16 % 4, so lane (l16, lg) holds rows r0 + 8 lg + 4 h + i
     floatx4 sv[2], dpv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int m = 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+      const int m = r0 + 8 * (l16 >> 2) + 4 * h + (l16 & 3);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sv[h] = mma(tile_row8<D>(ql, m, 32 * ks + 8 * lg), kb[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sv[h]);
@@ -526,7 +548,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 8 * lg + 4 * h + i;
+        const int m = r0 + 8 * lg + 4 * h + i;
         float x = sv[h][i] + qinfo[buf][2][m] - qinfo[buf][0][m];
         if (own && kloc > (int)qinfo[buf][3][m] - c * kChunk) x = -INFINITY;
         if (!kok) x = -INFINITY;
@@ -537,21 +559,44 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     // dV += P^T dO, dK += dS^T Q (B operands: the span tiles read transposed)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      dv[dt] = mma(pa, tile_tr8<D>(ol, 0, 16 * dt, lane), dv[dt]);
-      dk[dt] = mma(dsa, tile_tr8<D>(ql, 0, 16 * dt, lane), dk[dt]);
+      dv[dt] = mma(pa, tile_tr8<D>(ol, r0, 16 * dt, lane), dv[dt]);
+      dk[dt] = mma(dsa, tile_tr8<D>(ql, r0, 16 * dt, lane), dk[dt]);
     }
+  };
+  for (int s = 0; s < nspan; s += 2) {
+    span_step(s, S0{});
+    if (s + 1 < nspan) span_step(s + 1, S1{});
   }
-  // lane holds rows (keys) 16 wv + 4 lg + i, column d = 16 dt + l16.  dK = s sum dS q
-  // = ln 2 * sum dS (q sm_scale log2 e).
+  // lane holds rows (keys) 16 kg + 4 lg + i, column d = 16 dt + l16.  dK = s sum dS q
+  // = ln 2 * sum dS (q sm_scale log2 e).  The second half's waves hand their sums to the
+  // first half's through LDS (the span tiles, free after the barrier), which add them into
+  // the fp32 accumulators.
+  __syncthreads();
+  float* xk = reinterpret_cast<float*>(&lq[0][0]);     // [4 key groups][64 lanes][NDT * 4]
+  float* xv = reinterpret_cast<float*>(&ldo[0][0]);
+  static_assert(4 * 64 * NDT * 4 * 4 <= 2 * SB, "hand-over fits the span tiles");
+  if (half_q == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xk[(kg * 64 + lane) * NDT * 4 + dt * 4 + i] = dk[dt][i];
+        xv[(kg * 64 + lane) * NDT * 4 + dt * 4 + i] = dv[dt][i];
+      }
+  }
+  __syncthreads();
+  if (half_q == 1) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int kk = c * kChunk + 16 * wv + 4 * lg + i;
+    const int kk = c * kChunk + 16 * kg + 4 * lg + i;
     if (kk >= T) continue;
     const size_t ro = ((size_t)bk * T + kk) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      a.dk32[ro + 16 * dt + l16] = kLn2 * dk[dt][i];
-      ((bf16*)a.dv)[ro + 16 * dt + l16] = (bf16)dv[dt][i];
+      const float ok = xk[(kg * 64 + lane) * NDT * 4 + dt * 4 + i];
+      const float ov = xv[(kg * 64 + lane) * NDT * 4 + dt * 4 + i];
+      atomicAdd(a.dk32 + ro + 16 * dt + l16, kLn2 * (dk[dt][i] + ok));
+      atomicAdd(a.dv32 + ro + 16 * dt + l16, dv[dt][i] + ov);
     }
   }
 }
@@ -723,9 +768,9 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
   }
 }
 
-// Chunk-outer: one workgroup per (b, kv head, 16-chunk tile ct); 8 waves take spans of 32
-// query vectors (n = row * G + head) of the rows t >= 64 (16 ct + 1).  dK_bar (16 chunks x D)
-// of each wave is summed in LDS.
+// Chunk-outer: one workgroup per (b, kv head, 16-chunk tile ct, slice of kBwdSlice query
+// vectors n = (t - t0) G + head of the rows t >= t0 = 64 (16 ct + 1)); 8 waves take spans of
+// 32 vectors.  dK_bar (16 chunks x D) of each wave is summed in LDS and added by atomics.
 template <int D, int MODE>
 __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const float* __restrict__ rho) {
   constexpr int NW = 8, KS = D / 32, NDT = D / 16;
@@ -736,12 +781,18 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int T = a.T;
-  const int ct = blockIdx.x, bk = blockIdx.y;
+  const int ct = blockIdx.x, sl = blockIdx.y, bk = blockIdx.z;
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const float gs = a.gamma * a.scale;
   const float zscale = (a.alpha - 1.0f) * gs;
   const float inv = 1.0f / (a.alpha - 1.0f), rG = 1.0f / (float)G;
   const int c = 16 * ct + l16;                    // this lane's chunk (B column)
+  // rows that may route to this tile: t >= 64 (16 ct + 1), as query vectors
+  // n = (t - t0) G + head; this workgroup takes n in [sl * kBwdSlice, + kBwdSlice)
+  const int t0 = kChunk * (16 * ct + 1);
+  const long long nq_all = t0 < a.T ? (long long)(a.T - t0) * G : 0;
+  const long long nlo = (long long)sl * kBwdSlice;
+  if (nlo >= nq_all) return;                      // (whole workgroup)
   const bool cok = c < a.nc;
   // B operands: K_bar^T columns = chunks (hi and lo planes of the split summaries)
   const bf16* sp = a.ssplit + (size_t)bk * split_bk_stride(a.nc, D);
@@ -752,17 +803,15 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
     klo[ks] = *reinterpret_cast<const bf16x8*>(sp + split_offset(c, 1, 32 * ks + 8 * lg, D));
     if (!cok) { khi[ks] = bf16x8{}; klo[ks] = bf16x8{}; }
   }
-  // rows that may route to this tile: t >= 64 (16 ct + 1); spans of 32 query vectors
-  const int t0 = kChunk * (16 * ct + 1);
-  const long long nq = t0 < T ? (long long)(T - t0) * G : 0;
-  const int nspan = (int)((nq + 31) / 32);
+  const long long nq = nq_all;
+  const int nspan = (int)((min(nq_all - nlo, (long long)kBwdSlice) + 31) / 32);
   floatx4 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   uint8_t* myq = lq[wv];
   for (int s = wv; s < nspan; s += NW) {
     // stage the span's 32 query rows in this wave's LDS tile (row m <- vector n0 + m)
-    const long long n0 = (long long)s * 32;
+    const long long n0 = nlo + (long long)s * 32;
     for (int i = lane; i < 32 * (D / 8); i += 64) {
       const int m = i / (D / 8), d0 = (i % (D / 8)) * 8;
       const long long nn = n0 + m;
@@ -832,7 +881,7 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
   }
   for (int idx = tid; idx < 16 * D; idx += 512) {
     const int cc = 16 * ct + idx / D, d = idx % D;
-    if (cc < a.nc) a.dsumm[((size_t)bk * a.nc + cc) * D + d] = red[idx / D][d];
+    if (cc < a.nc) atomicAdd(a.dsumm + ((size_t)bk * a.nc + cc) * D + d, red[idx / D][d]);
   }
 }
 
@@ -885,21 +934,22 @@ static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, h
     }
   }
   // dK (Stage 2's part) and dV
-  k_bwd_dkdv_mfma<D><<<dim3(a.nc, BH), 256, 0, s>>>(a, delta, ub, nblk);
+  k_bwd_dkdv_mfma<D><<<dim3(a.nc, (nblk + kBwdRange - 1) / kBwdRange, BH), 512, 0, s>>>(a, delta, ub, nblk);
   // Stage 1: dq (final) and rho, then dK_bar
   {
     const int R = 16 / G;
     dim3 grid((unsigned)(((a.T + R - 1) / R) * BH));
     const int ntc = (a.nc + 15) / 16;
+    const int nsl = (int)(((long long)a.T * G + kBwdSlice - 1) / kBwdSlice);
     if (a.alpha == 1.5f) {
       k_bwd_route_dq<D, kAlpha15><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
-      k_bwd_route_dk<D, kAlpha15><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+      k_bwd_route_dk<D, kAlpha15><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     } else if (a.alpha == 2.0f) {
       k_bwd_route_dq<D, kAlpha2><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
-      k_bwd_route_dk<D, kAlpha2><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+      k_bwd_route_dk<D, kAlpha2><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     } else {
       k_bwd_route_dq<D, kAlphaGeneral><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
-      k_bwd_route_dk<D, kAlphaGeneral><<<dim3(ntc, BH), 512, 0, s>>>(a, rho);
+      k_bwd_route_dk<D, kAlphaGeneral><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     }
   }
   return hipGetLastError();

@@ -485,12 +485,13 @@ int dash_prefill_backward(const dash_params* p, const void* q, const void* k, co
   ra.z_out = zn;
   e = d.dtype == DASH_BF16 ? dash::launch_route_mfma(ra, ss, s) : dash::launch_route_valu(ra, s);
   if (e != hipSuccess) return hip_fail(e, "stage 1 launch");
-  // accumulators that the generic (fp32) kernels add into
+  // accumulators that the kernels add into (the generic kernels also add into dw_bar)
+  if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dk32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+      (e = fill_f32(reinterpret_cast<float*>(ws + L.dv32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
+      (e = fill_f32(reinterpret_cast<float*>(ws + L.dsumm), (size_t)d.B * d.Hkv * d.nc * d.D, 0.f, s)) != hipSuccess)
+    return hip_fail(e, "clearing the gradient accumulators");
   if (d.dtype != DASH_BF16) {
-    if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dk32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
-        (e = fill_f32(reinterpret_cast<float*>(ws + L.dv32), (size_t)d.B * d.Hkv * d.T * d.D, 0.f, s)) != hipSuccess ||
-        (e = fill_f32(reinterpret_cast<float*>(ws + L.dwb), (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess ||
-        (e = fill_f32(reinterpret_cast<float*>(ws + L.dsumm), (size_t)d.B * d.Hkv * d.nc * d.D, 0.f, s)) != hipSuccess)
+    if ((e = fill_f32(reinterpret_cast<float*>(ws + L.dwb), (size_t)d.B * d.Hkv * d.T * d.nc, 0.f, s)) != hipSuccess)
       return hip_fail(e, "clearing the gradient accumulators");
   }
   dash::BackwardArgs ba{};
@@ -533,7 +534,6 @@ int dash_prefill_backward(const dash_params* p, const void* q, const void* k, co
   if (d.dtype == DASH_BF16) {
     if ((e = dash::launch_backward_mfma(ba, ws + L.mscratch, s)) != hipSuccess)
       return hip_fail(e, "backward launch");
-    ba.dv32 = nullptr;                 // dv is final already
   } else {
     if ((e = dash::launch_backward_valu(ba, s)) != hipSuccess) return hip_fail(e, "backward launch");
   }

@@ -158,8 +158,9 @@ hipError_t launch_backward_valu(const BackwardArgs& a, hipStream_t s);
 // Stage 0 backwards and the head_cls reduction (after either path); dv converted from dv32
 // unless dv32 is null
 hipError_t launch_backward_stage0(const BackwardArgs& a, hipStream_t s);
-// bf16 MFMA kernels for Stage 2 and Stage 1 backwards: dq written, dk32 and dv (final)
-// written, dwb at set bits, dsumm written; scratch of backward_mfma_scratch() bytes
+// bf16 MFMA kernels for Stage 2 and Stage 1 backwards: dq written, dwb written at set bits,
+// dk32, dv32 and dsumm added into (they must start at zero); scratch of
+// backward_mfma_scratch() bytes
 int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delta, size_t* off_ub,
                           size_t* off_kbt, size_t* off_rho, size_t* total);
 hipError_t launch_backward_mfma(const BackwardArgs& a, void* scratch, hipStream_t s);
