@@ -14,6 +14,7 @@ Prints ONE JSON line on stdout:
   topk_router  the same prefill with a top-k comparison router (k = entmax's mean active
              chunks per row) in place of entmax: Stage 1 and Stage 2 times;
   estimate_diagonal  the same prefill with the own chunk's partial summary in the entmax;
+  backward   dq, dk, dv and d head_cls through all three stages (dash_prefill_backward);
   cpu_baseline  the float64 oracle timed on host cores over a bounded sample of rows.
 Progress lines go to stderr.
 """
@@ -253,7 +254,41 @@ def bench_prefill(args, w, dash, torch):
                         "speedup_stage2_over_dense": dms / st[2]}
         log(f"dense causal {dms:.2f} ms ({res['dense']['tflops']:.0f} TFLOP/s)")
         del wsd
-    del q, k, v, out, ws, ab
+    if not args.no_backward:
+        # the backward pass (dash_prefill_train, then dash_prefill_backward) with a seeded
+        # dL/dout: dq, dk, dv and d head_cls through all three stages
+        del ws, ab
+        torch.cuda.empty_cache()
+        gen = torch.Generator(device=dev).manual_seed(20268000)
+        do = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        out_t, lse = dash.prefill_train(q, k, v, hc, alpha=w.alpha, gamma=w.gamma, enable_gqa=True)
+        pb = dash.make_params(B, Hq, Hkv, T, D, alpha=w.alpha, gamma=w.gamma, enable_gqa=True,
+                              dtype=torch.bfloat16)
+        wsb = dash.alloc_workspace(dash.workspace_size("backward", pb), dev)
+        bkw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=True, workspace=wsb)
+        dash.prefill_backward(q, k, v, hc, out_t, do, lse, **bkw)
+        torch.cuda.synchronize()
+        nb = max(1, min(args.steps, 3))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nb):
+            grads = dash.prefill_backward(q, k, v, hc, out_t, do, lse, **bkw)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / nb
+        finite = all(bool(torch.isfinite(g.float()).all()) for g in grads)
+        # Stage 2 backward work: the forward's QK^T recomputed plus dP, dQ, dK and dV on the
+        # same active (query, key) pairs, i.e. 2.5 times the forward's algorithmic flops
+        f2b = 2.5 * flops2
+        res["backward"] = {"ms_per_call": bms, "tokens_per_s": B * T / (bms / 1e3),
+                           "stage2_backward_algorithmic_flops": f2b,
+                           "stage2_backward_tflops_over_whole_call": f2b / (bms / 1e3) / 1e12,
+                           "workspace_gib": wsb.numel() / 2 ** 30, "gradients_finite": finite,
+                           "calls": nb}
+        log(f"backward {bms:.1f} ms per call ({f2b / (bms / 1e3) / 1e12:.0f} TFLOP/s of Stage 2 "
+            f"backward work over the whole call), gradients finite: {finite}")
+        del do, out_t, lse, wsb, grads
+    del q, k, v, out
     torch.cuda.empty_cache()
     return res
 
@@ -601,6 +636,8 @@ def main():
                     help="skip timing the top-k comparison router")
     ap.add_argument("--no-diag", action="store_true",
                     help="skip timing the prefill with estimate_diagonal")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall seconds of the CPU oracle's sampled rows")
     ap.add_argument("--cpu-workers", type=int, default=16,
@@ -651,6 +688,7 @@ def main():
         "dense": pre.get("dense"),
         "topk_router": pre.get("topk"),
         "estimate_diagonal": pre.get("diag"),
+        "backward": pre.get("backward"),
         "decode": dec,
     }
     print(json.dumps(line), flush=True)
