@@ -6,12 +6,12 @@
 // weighted key is the chunk's summary.  Once a chunk is complete its summary is frozen.
 //
 // Kernel shape: one 64-lane wave per (b, kv head, chunk).  A chunk of K is one
-// contiguous 64 x D block (16 KiB at D = 128 bf16), read row by row so that each row is
-// one fully coalesced 256-byte wave load; lane l owns columns [l*E, l*E + E), E = D/64.
-// The 64 partial dot products of a lane are reduced across lanes through a padded LDS
-// tile (lane j ends up with logit a_j), softmax runs across lanes, and the weighted sum
-// of the rows (still in registers) is accumulated per lane in fp32.  HBM-bound: K is
-// read once, fp32 summaries are written once.
+// contiguous 64 x D block (16 KiB at D = 128 bf16), read with 16-byte loads: a key row
+// spans D / EPS lanes (EPS elements of 16 bytes each), so one wave-wide load covers
+// 64 EPS / D consecutive rows and every lane issues 16-byte requests.  Logits are summed
+// across the lanes of a row by xor butterflies, the softmax and the weighted sum across
+// the row groups, all in registers in fp32.  HBM-bound: K is read once, fp32 summaries
+// are written once.
 #include "dash_internal.h"
 
 namespace dash {
@@ -27,10 +27,14 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
                                                float scale_log2,
                                                const int32_t* __restrict__ block_table,
                                                int bt_ld, int num_pages) {
-  constexpr int E = D / 64;
-  __shared__ float red[64][65];
-  __shared__ float pis[64];
+  constexpr int EPS = 16 / (int)sizeof(TIn);     // elements per 16-byte load
+  constexpr int LPR = D / EPS;                    // lanes per key row
+  constexpr int RPI = 64 / LPR;                   // key rows per wave-wide load
+  constexpr int NI = kChunk / RPI;                // loads per lane per chunk
+  static_assert(LPR <= 64 && 64 % LPR == 0, "a key row must split evenly over the lanes");
+  typedef TIn vec_t __attribute__((ext_vector_type(EPS)));
   const int lane = threadIdx.x;
+  const int cg = lane % LPR, rg = lane / LPR;     // column group, row group
   const int kvh = blockIdx.y, b = blockIdx.z;
   int lo = 0, hi = n_full;
   if (seq_lens != nullptr) {
@@ -40,9 +44,9 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
     lo = lo_b ? lo_b[b] : 0;
     if (lo < 0) lo = 0;
   }
-  float h[E];
+  float h[EPS];
 #pragma unroll
-  for (int e = 0; e < E; ++e) h[e] = to_f32(head_cls[kvh * D + lane * E + e]) * scale_log2;
+  for (int e = 0; e < EPS; ++e) h[e] = to_f32(head_cls[kvh * D + cg * EPS + e]) * scale_log2;
 
   for (int c = lo + blockIdx.x; c < hi; c += gridDim.x) {
     const TIn* kc;
@@ -53,47 +57,64 @@ __global__ __launch_bounds__(64) void k_stage0(const TIn* __restrict__ k,
     } else {
       kc = k + ((size_t)(b * Hkv + kvh) * T_stride + (size_t)c * kChunk) * D;
     }
-    float kr[64][E];
+    // lane (rg, cg) holds columns [cg EPS, + EPS) of rows i RPI + rg, one 16-byte load each
+    // (rows stay packed in the input type until they are used: half the registers for bf16)
+    vec_t kr[NI];
+    float lgt[NI];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
+    for (int i = 0; i < NI; ++i)
+      kr[i] = *reinterpret_cast<const vec_t*>(kc + (size_t)(i * RPI + rg) * D + cg * EPS);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        kr[j][e] = to_f32(kc[j * D + lane * E + e]);
-        part += h[e] * kr[j][e];
+      for (int e = 0; e < EPS; ++e) part = fmaf(h[e], to_f32(kr[i][e]), part);
+      lgt[i] = part;
+    }
+    // logits: sums over the LPR lanes of a row (xor butterflies stay inside the row group)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) lgt[i] += __shfl_xor(lgt[i], o, 64);
+    // softmax over the 64 keys: each lane holds rows i RPI + rg; combine the row groups
+    float mx = lgt[0];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) mx = fmaxf(mx, lgt[i]);
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      lgt[i] = fast_exp2(lgt[i] - mx);
+      sum += lgt[i];
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    const float rs = 1.0f / sum;
+    float acc[EPS];
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a = fmaf(lgt[i], to_f32(kr[i][e]), a);
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) a += __shfl_xor(a, o, 64);
+      acc[e] = a * rs;
+    }
+    if (rg == 0) {
+      float* o = summ + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * D + cg * EPS;
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) o[e] = acc[e];
+      if (ssplit != nullptr) {
+        bf16* sp = ssplit + (size_t)(b * Hkv + kvh) * split_bk_stride(nc_alloc, D);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+          const bf16 hv = (bf16)acc[e];
+          sp[split_offset(c, 0, cg * EPS + e, D)] = hv;
+          sp[split_offset(c, 1, cg * EPS + e, D)] = (bf16)(acc[e] - (float)hv);
+        }
       }
-      red[j][lane] = part;
     }
-    __syncthreads();
-    float a = 0.f;  // logit of key `lane`, in log2 units
-    for (int i = 0; i < 64; ++i) a += red[lane][i];
-    const float m = wave_max(a);
-    const float p = fast_exp2(a - m);
-    const float s = wave_sum(p);
-    pis[lane] = p / s;
-    __syncthreads();
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const float pj = pis[j];
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += pj * kr[j][e];
-    }
-    float* o = summ + ((size_t)(b * Hkv + kvh) * nc_alloc + c) * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = acc[e];
-    if (ssplit != nullptr) {
-      bf16* sp = ssplit + (size_t)(b * Hkv + kvh) * split_bk_stride(nc_alloc, D);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bf16 hi = (bf16)acc[e];
-        sp[split_offset(c, 0, lane * E + e, D)] = hi;
-        sp[split_offset(c, 1, lane * E + e, D)] = (bf16)(acc[e] - (float)hi);
-      }
-    }
-    __syncthreads();
   }
 }
 
