@@ -452,60 +452,81 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     srow[i] = seg / SEGR;
     scol[i] = (seg % SEGR) * 8;
   }
-  // two register sets: the loads of spans s + 1 and s + 2 are in flight while span s computes
+  // two register sets: the loads of spans s + 1 and s + 2 are in flight while span s
+  // computes.  They hold the loaded bits only; everything computed from them (Q's scale, the
+  // log2 e factor of lse, the prior bias) waits until the set is stashed two spans later,
+  // so no wave stalls on a load it has just issued.  Every thread issues the same loads
+  // without branches, through buffer descriptors over this (b, kv head)'s rows: a row past
+  // T gets an offset past the descriptor's range and reads as zero, and its bias is -inf,
+  // so its P and dS are exactly 0.  (Equal load counts on every path let the compiler wait
+  // for the older set only.)
+  constexpr int kOob = 0x7ffffff0;                // a byte offset past every range used here
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.q + (size_t)(b * a.Hq + kvh * G) * T * D), (short)0, G * T * D * 2,
+      kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.dout + (size_t)(b * a.Hq + kvh * G) * T * D), (short)0, G * T * D * 2,
+      kRsrcWord3);
+  // per-row information, one kind per wave of the first four: lse (0), delta (1), w_bar and
+  // the mask word's half that holds bit c (2), the row index (3, no load)
+  const int kindw = __builtin_amdgcn_readfirstlane(wv);
+  const float* ibase = kindw == 0 ? a.lse + (size_t)(b * a.Hq + kvh * G) * T
+                     : kindw == 1 ? delta + (size_t)(b * a.Hq + kvh * G) * T
+                                  : a.wbar + (size_t)bk * T * a.nc;
+  const int irange = kindw == 2 ? T * a.nc * 4 : (kindw < 2 ? G * T * 4 : 0);
+  const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc((void*)ibase, (short)0, irange, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.mask + (size_t)bk * T * a.W), (short)0, kindw == 2 ? T * a.W * 8 : 0, kRsrcWord3);
   uint4 qreg[2][PT], oreg[2][PT];
-  float inf_next[2] = {0.f, 0.f};                 // this thread's qinfo entry (tid < 256)
+  float inf_raw[2] = {0.f, 0.f};                  // lse / delta / w_bar of this thread's row
+  uint32_t inf_bits[2] = {0u, 0u};                // the mask half-word (kind 2)
+  int inf_row[2] = {0, 0};                        // the row index t
+  bool inf_own[2] = {false, false};               // the span's block is chunk c's own
   const int lgG = __builtin_ctz(G);               // G is a power of two
-  auto span_src = [&](int s, int m, int* tt) {    // global row index of span row m
-    const int blk = blist[s >> lgG], sp = s & (G - 1);
-    const int nn = SPAN * sp + m, rr = nn >> lgG, gg = nn & (G - 1);
-    const int tr = blk * kChunk + rr;
-    *tt = tr;
-    return (size_t)(b * a.Hq + kvh * G + gg) * T + (tr < T ? tr : 0);
-  };
-  auto prefetch = [&](int s, auto set_tag) {
+  // (a span index past the last one loads nothing: every offset is out of range)
+  auto prefetch = [&](int s_any, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
+    const bool live = s_any < nspan;
+    const int s = live ? s_any : 0;
+    const int blk = blist[s >> lgG], sp = s & (G - 1);
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      int tr;
-      const size_t gi = span_src(s, srow[i], &tr);
-      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-      if (tr < T) {
-        bf16x8 qv = *reinterpret_cast<const bf16x8*>((const bf16*)a.q + gi * D + scol[i]);
-        x = __builtin_bit_cast(uint4, scale_bf16x8(qv, sl2));
-        y = *reinterpret_cast<const uint4*>((const bf16*)a.dout + gi * D + scol[i]);
-      }
-      qreg[S][i] = x;
-      oreg[S][i] = y;
+      const int nn = SPAN * sp + srow[i], tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
+      const int off = live && tr < T ? (((gg * T + tr) * D + scol[i]) * 2) : kOob;
+      qreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+      oreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
     }
-    if (tid < 4 * SPAN) {
-      const int kind = tid / SPAN, m = tid % SPAN;
-      int tr;
-      const size_t gi = span_src(s, m, &tr);
-      const int blk = blist[s >> lgG];
-      float v;
-      if (kind == 0) v = tr < T ? a.lse[gi] * kLog2e : 0.f;
-      else if (kind == 1) v = tr < T ? delta[gi] : 0.f;
-      else if (kind == 2) {
-        if (tr >= T) v = -INFINITY;
-        else if (blk == c) v = 0.f;               // the block's own chunk: no prior
-        else {
-          const size_t ri = (size_t)bk * T + tr;
-          const bool on = (a.mask[ri * a.W + (c >> 6)] >> (c & 63)) & 1ull;
-          v = on ? a.sigma * fast_log2(a.wbar[ri * a.nc + c]) : -INFINITY;
-        }
-      } else v = (float)tr;
-      inf_next[S] = v;
-    }
+    const int m = tid % SPAN;
+    const int nn = SPAN * sp + m, tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
+    const bool ok = live && tr < T && tid < 3 * SPAN;
+    const int ioff = !ok ? kOob : (kindw == 2 ? (tr * a.nc + c) * 4 : (gg * T + tr) * 4);
+    const int moff = !ok ? kOob : (tr * a.W + (c >> 6)) * 8 + ((c & 63) >= 32 ? 4 : 0);
+    inf_raw[S] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(irs, ioff, 0, 0));
+    inf_bits[S] = __builtin_amdgcn_raw_buffer_load_b32(mrs, moff, 0, 0);
+    inf_row[S] = tr;
+    inf_own[S] = blk == c;
   };
   auto stash = [&](int buf, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      *reinterpret_cast<uint4*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) = qreg[S][i];
+      *reinterpret_cast<bf16x8*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) =
+          scale_bf16x8(__builtin_bit_cast(bf16x8, qreg[S][i]), sl2);
       *reinterpret_cast<uint4*>(&ldo[buf][tile_off<D>(srow[i], scol[i])]) = oreg[S][i];
     }
-    if (tid < 4 * SPAN) qinfo[buf][tid / SPAN][tid % SPAN] = inf_next[S];
+    if (tid < 4 * SPAN) {
+      const int kind = tid / SPAN;
+      const int tr = inf_row[S];
+      float v;
+      if (kind == 0) v = inf_raw[S] * kLog2e;
+      else if (kind == 1) v = inf_raw[S];
+      else if (kind == 2) {
+        if (tr >= T) v = -INFINITY;
+        else if (inf_own[S]) v = 0.f;             // the block's own chunk: no prior
+        else v = ((inf_bits[S] >> (c & 31)) & 1u) ? a.sigma * fast_log2(inf_raw[S]) : -INFINITY;
+      } else v = (float)tr;
+      qinfo[buf][kind][tid % SPAN] = v;
+    }
   };
 
   floatx4 dk[NDT], dv[NDT];
@@ -519,7 +540,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   prefetch(0, S0{});
-  if (1 < nspan) prefetch(1, S1{});
+  prefetch(1, S1{});
   // span s: its registers (set s & 1) go to LDS buffer s & 1, which span s - 2 read before
   // every wave passed the barrier of span s - 1; then the set is refilled with span s + 2
   auto span_step = [&](int s, auto set_tag) {
@@ -528,7 +549,8 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     stash(buf, set_tag);
     const bool own = blist[s >> lgG] == c;
     __syncthreads();
-    if (s + 2 < nspan) prefetch(s + 2, set_tag);
+    prefetch(s + 2, set_tag);
+    if (s >= nspan) return;                       // past the last span (whole workgroup)
     const uint8_t* ql = lq[buf];
     const uint8_t* ol = ldo[buf];
     // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- tile row
@@ -563,9 +585,11 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
       dk[dt] = mma(dsa, tile_tr8<D>(ql, r0, 16 * dt, lane), dk[dt]);
     }
   };
+  // both halves run every round (a span past the end only stashes and prefetches), so the
+  // loads in flight are the same on every path
   for (int s = 0; s < nspan; s += 2) {
     span_step(s, S0{});
-    if (s + 1 < nspan) span_step(s + 1, S1{});
+    span_step(s + 1, S1{});
   }
   // lane holds rows (keys) 16 kg + 4 lg + i, column d = 16 dt + l16.  dK = s sum dS q
   // = ln 2 * sum dS (q sm_scale log2 e).  The second half's waves hand their sums to the
