@@ -800,6 +800,7 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
   constexpr int NW = 8, KS = D / 32, NDT = D / 16;
   constexpr int SB = 32 * 2 * D;
   __shared__ __attribute__((aligned(16))) uint8_t lq[NW][SB];
+  __shared__ float info[NW][32][4];               // tau, z, rho, mask half-word per span row
   __shared__ float red[16][D + 4];
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -833,21 +834,89 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   uint8_t* myq = lq[wv];
-  for (int s = wv; s < nspan; s += NW) {
-    // stage the span's 32 query rows in this wave's LDS tile (row m <- vector n0 + m)
+  float* myinfo = &info[wv][0][0];
+
+  // Per-wave software pipeline over the wave's spans s = wv, wv + NW, ...: the next span's
+  // query rows, per-row thresholds, normalisers, rho, mask half-word and this lane's dL/dw_bar
+  // values are loaded (raw bits, through buffer descriptors; anything past the end or past the
+  // rows reads as zero) while the current span computes.  Query vector n of the slice is row
+  // t0 + n / G, head n % G (G a power of two).
+  constexpr int kOob = 0x7ffffff0;
+  constexpr int QPL = 32 * (D / 8) / 64;          // 16-byte query segments per lane per span
+  const int lgG = __builtin_ctz(G);
+  const size_t hbase = (size_t)(b * a.Hq + kvh * G) * T;   // first row of this kv head's heads
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)a.q + hbase * D), (short)0, G * T * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.tau + hbase), (short)0, G * T * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.z + hbase), (short)0, G * T * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc((void*)(rho + hbase), (short)0, G * T * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.mask + (size_t)bk * T * a.W), (short)0, T * a.W * 8, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.dwb + (size_t)bk * T * a.nc), (short)0, T * a.nc * 4, kRsrcWord3);
+  const int cb = 16 * ct;                         // the tile's chunks share one mask half-word
+  const int mhalf = (cb & 63) >= 32 ? 4 : 0;
+  uint4 qn[QPL];
+  float inf_n[3];
+  uint32_t mw_n;
+  float dw_n[8];
+  auto load_span = [&](int s) {
+    const bool live = s < nspan;
     const long long n0 = nlo + (long long)s * 32;
-    for (int i = lane; i < 32 * (D / 8); i += 64) {
-      const int m = i / (D / 8), d0 = (i % (D / 8)) * 8;
+#pragma unroll
+    for (int j = 0; j < QPL; ++j) {
+      const int i = lane + 64 * j, m = i / (D / 8), d0 = (i % (D / 8)) * 8;
       const long long nn = n0 + m;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (nn < nq) {
-        const int tt = t0 + (int)(nn / G), gg = (int)(nn % G);
-        x = *reinterpret_cast<const uint4*>((const bf16*)a.q + ((size_t)(b * a.Hq + kvh * G + gg) * T + tt) * D + d0);
-      }
-      *reinterpret_cast<uint4*>(myq + tile_off<D>(m, d0)) = x;
+      const bool ok = live && nn < nq;
+      const int tt = t0 + (int)(nn >> lgG), gg = (int)(nn & (G - 1));
+      qn[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            qrs, ok ? ((gg * T + tt) * D + d0) * 2 : kOob, 0, 0));
     }
+    {
+      const int m = lane & 31;
+      const long long nn = n0 + m;
+      const bool ok = live && nn < nq && lane < 32;
+      const int tt = t0 + (int)(nn >> lgG), gg = (int)(nn & (G - 1));
+      const int ro = ok ? (gg * T + tt) * 4 : kOob;
+      inf_n[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(trs, ro, 0, 0));
+      inf_n[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(zrs, ro, 0, 0));
+      inf_n[2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrs, ro, 0, 0));
+      mw_n = __builtin_amdgcn_raw_buffer_load_b32(mrs, ok ? (tt * a.W + (cb >> 6)) * 8 + mhalf : kOob, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long nn = n0 + 8 * lg + 4 * h + i;
+        const bool ok = live && nn < nq && cok;
+        const int tt = t0 + (int)(nn >> lgG);
+        dw_n[4 * h + i] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(wrs, ok ? (tt * a.nc + c) * 4 : kOob, 0, 0));
+      }
+  };
+
+  load_span(wv);
+  for (int s = wv; s < nspan; s += NW) {
+    // stash: the span's query rows in this wave's LDS tile (row m <- vector n0 + m) and its
+    // per-row values; this lane's dL/dw_bar values stay in registers
+#pragma unroll
+    for (int j = 0; j < QPL; ++j) {
+      const int i = lane + 64 * j, m = i / (D / 8), d0 = (i % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(myq + tile_off<D>(m, d0)) = qn[j];
+    }
+    if (lane < 32) {
+      myinfo[lane * 4 + 0] = inf_n[0];
+      myinfo[lane * 4 + 1] = inf_n[1];
+      myinfo[lane * 4 + 2] = inf_n[2];
+      myinfo[lane * 4 + 3] = __builtin_bit_cast(float, mw_n);
+    }
+    float dw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dw[e] = dw_n[e];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
+    load_span(s + NW);                            // the wave's next span (or nothing)
+    const long long n0 = nlo + (long long)s * 32;
     // S = Q K_bar^T with span rows permuted (lane holds rows 8 lg + 4 h + i of column c)
     floatx4 sv[2];
 #pragma unroll
@@ -870,15 +939,15 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
         const long long nn = n0 + m;
         float dx = 0.f;
         if (nn < nq && cok) {
-          const int tt = t0 + (int)(nn / G), gg = (int)(nn % G);
+          const int tt = t0 + (int)(nn >> lgG);
           if (c < tt / kChunk) {
-            const size_t qi = (size_t)(b * a.Hq + kvh * G + gg) * T + tt;
-            const float p = entmax_weight<MODE>(zscale * sv[h][i], a.tau[qi], inv, 1.0f / a.z[qi]);
+            const float tau = myinfo[m * 4 + 0], zz = myinfo[m * 4 + 1], rh = myinfo[m * 4 + 2];
+            const uint32_t mw = __builtin_bit_cast(uint32_t, myinfo[m * 4 + 3]);
+            const float p = entmax_weight<MODE>(zscale * sv[h][i], tau, inv, 1.0f / zz);
             if (p > 0.f) {
-              const size_t ri = (size_t)bk * T + tt;
-              const bool on = (a.mask[ri * a.W + (c >> 6)] >> (c & 63)) & 1ull;
-              const float dp = on ? a.dwb[ri * a.nc + c] * rG : 0.f;
-              dx = gs * jac_s<MODE>(p, a.alpha) * (dp - rho[qi]);
+              const bool on = (mw >> (c & 31)) & 1u;
+              const float dp = on ? dw[4 * h + i] * rG : 0.f;
+              dx = gs * jac_s<MODE>(p, a.alpha) * (dp - rh);
             }
           }
         }
