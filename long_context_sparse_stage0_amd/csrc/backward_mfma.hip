@@ -691,37 +691,91 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
   const bool act = qok && it > 0;
   const float tau = act ? a.tau[qi] : 0.f;
   const float rz = act ? 1.0f / a.z[qi] : 0.f;
-  const bf16* sp = a.ssplit + (size_t)bk * split_bk_stride(a.nc, D);
   const int ntile = (it + 15) / 16;
   const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
 
-  // s and dp of the lane's 4 chunks of tile ct
-  auto sdp = [&](int ct, float (&s4)[4], float (&dp4)[4]) {
-    const floatx4 acc = route_scores<D>(sp, qop, ct, it, l16, lg);
+  // A tile's loads (this wave's tiles wv, wv + NW, ...): the hi and lo summary operands of its
+  // 16 chunks, the mask half-word of the lane's row that holds them and the lane's four
+  // dL/dw_bar values, all as buffer loads issued together and without branches (a tile past
+  // the wave's last one, or a chunk at or past it, reads as zero), so the loads of the next
+  // tile are in flight while this one is evaluated.
+  constexpr int kOob = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.ssplit + (size_t)bk * split_bk_stride(a.nc, D)), (short)0,
+      (int)(split_bk_stride(a.nc, D) * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.mask + (size_t)bk * T * a.W), (short)0, T * a.W * 8, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.dwb + (size_t)bk * T * a.nc), (short)0, T * a.nc * 4, kRsrcWord3);
+  const int trow = qok ? t : 0;
+  struct TileLoads {
+    bf16x8 hi[KS], lo[KS];
+    uint32_t mw;
+    float dw[4];
+  };
+  auto load_tile = [&](int j, TileLoads& L) {
+    const int ct = wv + NW * j;
+    const bool live = j < nj;
+    const int crow = 16 * ct + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      L.hi[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                     srs, live ? split_offset(crow, 0, 32 * ks + 8 * lg, D) * 2 : kOob, 0, 0));
+      L.lo[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                     srs, live ? split_offset(crow, 1, 32 * ks + 8 * lg, D) * 2 : kOob, 0, 0));
+    }
+    const int c0 = 16 * ct + 4 * lg;              // the lane's chunks c0 .. c0 + 3
+    L.mw = __builtin_amdgcn_raw_buffer_load_b32(
+        mrs, live && act ? (trow * a.W + (c0 >> 6)) * 8 + ((c0 & 63) >= 32 ? 4 : 0) : kOob, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      L.dw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    wrs, live && act && c0 + i < it ? (trow * a.nc + c0 + i) * 4 : kOob, 0, 0));
+  };
+  // s and dp of the lane's 4 chunks of a loaded tile
+  auto eval_tile = [&](int j, const TileLoads& L, float (&s4)[4], float (&dp4)[4]) {
+    const int ct = wv + NW * j;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = mma(L.hi[ks], qop[ks], acc);
+      acc = mma(L.lo[ks], qop[ks], acc);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int cc = 16 * ct + 4 * lg + i;
       s4[i] = 0.f;
       dp4[i] = 0.f;
-      if (act && cc < it) {
+      if (act && j < nj && cc < it) {
         const float p = entmax_weight<MODE>(zscale * acc[i], tau, inv, rz);
         if (p > 0.f) {
           s4[i] = jac_s<MODE>(p, a.alpha);
-          const bool on = (a.mask[rowi * a.W + (cc >> 6)] >> (cc & 63)) & 1ull;
-          dp4[i] = on ? a.dwb[rowi * a.nc + cc] * rG : 0.f;
+          dp4[i] = ((L.mw >> (cc & 31)) & 1u) ? L.dw[i] * rG : 0.f;
         }
       }
     }
   };
   // ---- pass 1: sum s and sum s dp per query vector
   float ss = 0.f, sd = 0.f;
-  for (int j = 0; j < nj; ++j) {
-    float s4[4], dp4[4];
-    sdp(wv + NW * j, s4, dp4);
+  {
+    TileLoads A, B;
+    load_tile(0, A);
+    for (int j = 0; j < nj; j += 2) {
+      float s4[4], dp4[4];
+      load_tile(j + 1, B);
+      eval_tile(j, A, s4, dp4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ss += s4[i];
-      sd = fmaf(s4[i], dp4[i], sd);
+      for (int i = 0; i < 4; ++i) {
+        ss += s4[i];
+        sd = fmaf(s4[i], dp4[i], sd);
+      }
+      load_tile(j + 2, A);
+      eval_tile(j + 1, B, s4, dp4);               // zeros past the last tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ss += s4[i];
+        sd = fmaf(s4[i], dp4[i], sd);
+      }
     }
   }
   ss = rows_sum(ss);
@@ -745,33 +799,38 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bf16* kb = kbt + (size_t)bk * D * ncp;
-  for (int j = 0; j < nj; j += 2) {
-    const int ta = wv + NW * j, tb = wv + NW * (j + 1);
-    const bool hasb = j + 1 < nj;
-    bf16x8 xa;
-    {
+  {
+    TileLoads A, B;
+    load_tile(0, A);
+    for (int j = 0; j < nj; j += 2) {
+      const int ta = wv + NW * j, tb = wv + NW * (j + 1);
+      const bool hasb = j + 1 < nj;
+      const int cb = hasb ? tb : ta;              // any valid tile: its operand is times 0
+      // the pair's K_bar operands, loaded before the tiles are evaluated
+      typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 kx[NDT], ky[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16* kr = kb + (size_t)(16 * dt + l16) * ncp;
+        kx[dt] = *reinterpret_cast<const bf16x4*>(kr + 16 * ta + 4 * lg);
+        ky[dt] = *reinterpret_cast<const bf16x4*>(kr + 16 * cb + 4 * lg);
+      }
+      bf16x8 xa;
       float s4[4], dp4[4];
-      sdp(ta, s4, dp4);
+      load_tile(j + 1, B);
+      eval_tile(j, A, s4, dp4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
-      if (hasb) {
-        sdp(tb, s4, dp4);
+      load_tile(j + 2, A);
+      eval_tile(j + 1, B, s4, dp4);               // zeros past the last tile
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
-      } else {
+      for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)0.f;
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 bop = {kx[dt][0], kx[dt][1], kx[dt][2], kx[dt][3],
+                            ky[dt][0], ky[dt][1], ky[dt][2], ky[dt][3]};
+        acc[dt] = mma(xa, bop, acc[dt]);
       }
-    }
-    const int cb = hasb ? tb : ta;                // any valid tile: its operand is times 0
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16* kr = kb + (size_t)(16 * dt + l16) * ncp;
-      typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 x = *reinterpret_cast<const bf16x4*>(kr + 16 * ta + 4 * lg);
-      const bf16x4 y = *reinterpret_cast<const bf16x4*>(kr + 16 * cb + 4 * lg);
-      const bf16x8 bop = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-      acc[dt] = mma(xa, bop, acc[dt]);
     }
   }
   // lane: C[4 lg + i][l16] = (query vector 4 lg + i, d = 16 dt + l16); sum the waves in LDS
