@@ -21,6 +21,7 @@
 //                   spans of 64 query vectors staged in LDS, each wave taking 32 of them: S = Q K^T and dP = dO V^T with the
 //                   span's rows permuted so that P and dS land in the lanes as the A operands of
 //                   dV += P^T dO and dK += dS^T Q, added into fp32 accumulators by atomics.
+//                   A span's loads are raw, branch-free buffer loads issued two spans ahead.
 //                   Workgroups are dispatched range by range, so the ones in flight share one
 //                   range's queries and output gradients through the caches.
 //   k_bwd_route_dq  Stage 1, row-outer (the forward router's work unit, 16 query vectors on
@@ -28,12 +29,14 @@
 //                   weights from its saved tau, z, and reduces sum s and sum s dp into rho;
 //                   pass 2 recomputes them, forms dx and adds dq += gamma scale dx K_bar on
 //                   MFMA (dx straight from the score registers, K_bar from the [d][chunk]
-//                   plane); writes the final dq and rho.
+//                   plane); writes the final dq and rho.  A tile's operand, mask and dL/dw_bar
+//                   loads are issued one tile ahead.
 //   k_bwd_route_dk  Stage 1, chunk-outer: one workgroup per (b, kv head, 16 chunks, slice of
 //                   8192 query vectors of the later rows); its waves take spans of 32 vectors,
 //                   recompute the span's scores as S = Q K_bar^T (rows permuted as in
 //                   k_bwd_dkdv_mfma), form dx with the saved rho and add dK_bar += dX^T Q;
-//                   waves are summed in LDS and added into dK_bar by atomics.
+//                   waves are summed in LDS and added into dK_bar by atomics.  Each wave
+//                   loads its next span while the current one computes.
 // Stage 0 backwards and the head_cls reduction use the generic kernels (backward_valu.hip).
 #include <type_traits>
 
@@ -626,26 +629,6 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
 }
 
 // ------------------------------------------------------------------------------ Stage 1
-// Scores of this lane's column (query vector) against 16 chunks 16 ct + l16 (A rows) on the
-// hi and lo planes, as in the forward router: C[4 lg + i][l16] = chunk 16 ct + 4 lg + i.
-template <int D>
-__device__ __forceinline__ floatx4 route_scores(const bf16* sp, const bf16x8 (&qop)[D / 32], int ct,
-                                                int it, int l16, int lg) {
-  constexpr int KS = D / 32;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int crow = 16 * ct + l16;
-  const bool cok = crow < it;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8 hi = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 0, 32 * ks + 8 * lg, D));
-    bf16x8 lo = *reinterpret_cast<const bf16x8*>(sp + split_offset(crow, 1, 32 * ks + 8 * lg, D));
-    if (!cok) { hi = bf16x8{}; lo = bf16x8{}; }
-    acc = mma(hi, qop[ks], acc);
-    acc = mma(lo, qop[ks], acc);
-  }
-  return acc;
-}
-
 template <int MODE>
 __device__ __forceinline__ float jac_s(float p, float alpha) {   // p^(2 - alpha), p > 0
   if (MODE == kAlpha15) return sqrtf(p);
