@@ -14,6 +14,10 @@ Run once under each of four rocprofv3 passes (one counter group per pass), then 
         -- python3 -m long_context_sparse_stage0_amd.traffic run
     python3 -m long_context_sparse_stage0_amd.traffic summarize <out>/traffic
 
+`backward` runs the 128K backward pass three times (for a kernel-trace run), and
+`ktable <stats.csv> <out.md> <title> <command> [note]` writes a rocprofv3 kernel-stats CSV
+as a markdown table of the library's kernels.
+
 `run` launches, on the 128K prefill workload, the full prefill once (to build the mask and
 the weights), then Stage 2 alone three times; then, on the 64K decode workload, the bulk
 summary append and kDecodeSteps decode steps; and, as the last dispatch, a plain
@@ -303,10 +307,68 @@ def report(base, factors):
     return doc
 
 
+def backward():
+    """The 128K backward pass: dash_prefill_train once, then dash_prefill_backward three times
+    with a seeded dL/dout (for a kernel-trace run)."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from long_context_sparse_stage0_amd import dash, synth
+    from long_context_sparse_stage0_amd.workloads import PREFILL_128K_GQA as w
+    dash.load()
+    x = synth.prefill_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, hc = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev)
+                   for n in ("q", "k", "v", "head_cls"))
+    del x
+    g = torch.Generator(device="cpu").manual_seed(7)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+    kw = dict(alpha=w.alpha, gamma=w.gamma, enable_gqa=True)
+    out, lse = dash.prefill_train(q, k, v, hc, **kw)
+    p = dash.make_params(w.B, w.Hq, w.Hkv, w.T, w.D, alpha=w.alpha, gamma=w.gamma,
+                         enable_gqa=True, dtype=torch.bfloat16)
+    ws = dash.alloc_workspace(dash.workspace_size("backward", p), dev)
+    for _ in range(3):
+        dash.prefill_backward(q, k, v, hc, out, do, lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    print("backward done", flush=True)
+
+
+def ktable(stats_csv, out_md, title, command, note=""):
+    """Write a rocprofv3 kernel-stats CSV (library kernels only) as a markdown table."""
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if "dash::" not in r["Name"] and "_ZN4dash" not in r["Name"]:
+                continue
+            rows.append((float(r["TotalDurationNs"]), r["Name"], int(r["Calls"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(reverse=True)
+    lines = [f"# {title}", "", "Command (repo root; `cd /tmp && export TMPDIR=/tmp` first, then back "
+             "to the repo):", "", f"    {command}", "",
+             f"Per-kernel statistics from `{os.path.basename(stats_csv)}` (library kernels only, by "
+             "total time; torch helper kernels omitted), written by", "",
+             f"    python3 -m long_context_sparse_stage0_amd.traffic ktable <csv> <md> ...", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| kernel | calls | mean (us) | min (us) | max (us) | total (ms) |",
+              "|---|---|---|---|---|---|"]
+    for tot, name, calls, avg, mn, mx in rows:
+        nm = name.replace("void ", "").replace("dash::", "").replace("|", "/")
+        lines.append(f"| `{nm[:110]}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | "
+                     f"{mx / 1e3:.1f} | {tot / 1e6:.2f} |")
+    lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
+    elif len(sys.argv) >= 2 and sys.argv[1] == "backward":
+        backward()
     elif len(sys.argv) >= 3 and sys.argv[1] == "summarize":
         summarize(sys.argv[2])
+    elif len(sys.argv) >= 6 and sys.argv[1] == "ktable":
+        ktable(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
