@@ -38,6 +38,7 @@
 //                   waves are summed in LDS and added into dK_bar by atomics.  Each wave
 //                   loads its next span while the current one computes.
 // Stage 0 backwards and the head_cls reduction use the generic kernels (backward_valu.hip).
+#include <algorithm>
 #include <type_traits>
 
 #include "route_common.h"
@@ -379,20 +380,36 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const f
   }
 }
 
+// Q scaled by sm_scale * log2 e and rounded to bf16, exactly as the forward's Stage 2 uses it,
+// for the dK/dV kernel's direct-to-LDS span loads (which cannot scale on the way).
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_qscale(BackwardArgs a, bf16* __restrict__ qsc) {
+  const float sl2 = a.scale * kLog2e;
+  const size_t n8 = (size_t)a.B * a.Hq * a.T * D / 8;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const bf16x8 v = reinterpret_cast<const bf16x8*>(a.q)[i];
+    reinterpret_cast<bf16x8*>(qsc)[i] = scale_bf16x8(v, sl2);
+  }
+}
+
 // ------------------------------------------------------------------------------ dK, dV
 // One workgroup per (b, kv head, block range, chunk c) with 8 waves: wave w owns keys
 // c*64 + 16 (w % 4) + [0, 16) and takes half w / 4 (32 vectors) of every 64-vector span.
 template <int D>
 __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const float* __restrict__ delta,
-                                                       const uint64_t* __restrict__ ub, int nblk) {
-  constexpr int NT = 512, SPAN = 64;
+                                                       const uint64_t* __restrict__ ub, int nblk,
+                                                       const bf16* __restrict__ qsc) {
+  constexpr int NT = 512, SPAN = 64, NBUF = 4;
   constexpr int KS = D / 32, NDT = D / 16;
   constexpr int SB = SPAN * 2 * D;                // bytes of a span tile
-  constexpr int SEGR = D / 8, SEG = SPAN * SEGR, PT = SEG / NT;
-  static_assert(SEG % NT == 0, "span segments must divide over the threads");
-  __shared__ __attribute__((aligned(16))) uint8_t lq[2][SB];
-  __shared__ __attribute__((aligned(16))) uint8_t ldo[2][SB];
-  __shared__ float qinfo[2][4][SPAN];             // lse2, delta, bias2, t (as float)
+  constexpr int NBLK = SB / 1024 / 8;             // 1 KiB LDS blocks per wave and tile
+  static_assert(NBLK >= 1 && SB % (1024 * 8) == 0, "a span tile must split into 1 KiB blocks per wave");
+  // the ring's slots are separate arrays, so that the compiler can tell the slot a load is
+  // filling from the slot being read and does not wait for the former before the latter
+  // (each slot holds the Q tile, then the dO tile)
+  __shared__ __attribute__((aligned(16))) uint8_t rs0[2 * SB], rs1[2 * SB], rs2[2 * SB], rs3[2 * SB];
+  __shared__ float qinfo[NBUF][4][SPAN];          // lse2, delta, bias2, t (as float)
   __shared__ uint16_t blist[kMaxRouted + 2];
   __shared__ int nbl_s;
 
@@ -445,33 +462,22 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     }
   }
 
-  // ---- span loads: row m < 64 of span s of block blk is query vector n = 64 s' + m of the
-  // block (n = row * G + head); Q scaled by sm_scale * log2 e and rounded to bf16 as in the
-  // forward
-  int srow[PT], scol[PT];
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int seg = tid + i * NT;
-    srow[i] = seg / SEGR;
-    scol[i] = (seg % SEGR) * 8;
-  }
-  // two register sets: the loads of spans s + 1 and s + 2 are in flight while span s
-  // computes.  They hold the loaded bits only; everything computed from them (Q's scale, the
-  // log2 e factor of lse, the prior bias) waits until the set is stashed two spans later,
-  // so no wave stalls on a load it has just issued.  Every thread issues the same loads
-  // without branches, through buffer descriptors over this (b, kv head)'s rows: a row past
-  // T gets an offset past the descriptor's range and reads as zero, and its bias is -inf,
-  // so its P and dS are exactly 0.  (Equal load counts on every path let the compiler wait
-  // for the older set only.)
-  constexpr int kOob = 0x7ffffff0;                // a byte offset past every range used here
+  // ---- span tiles: row m < 64 of span s of block blk is query vector n = 64 s' + m of the
+  // block (n = row * G + head).  The Q and dO tiles go from memory straight into a ring of
+  // NBUF LDS slots (buffer loads with an LDS destination: lane i of a load fills the 16
+  // bytes at the slot's 1 KiB block base + 16 i, so each lane fetches the global 16 bytes
+  // that the swizzled layout puts there); Q comes pre-scaled by sm_scale * log2 e and rounded
+  // to bf16 as in the forward (k_bwd_qscale).  Spans s + 1 .. s + NBUF - 2 are in flight
+  // while span s computes.  The per-row values (lse, delta, the prior bias and the row) go
+  // through registers, raw, one set per slot, and are turned into qinfo when the slot is
+  // stashed.  Every load is unconditional: a row past T or a span past the end gets an
+  // offset past its descriptor's range and reads as zero.
+  constexpr int kOob = 0x7ffffff0;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const bf16*)a.q + (size_t)(b * a.Hq + kvh * G) * T * D), (short)0, G * T * D * 2,
-      kRsrcWord3);
+      (void*)(qsc + (size_t)(b * a.Hq + kvh * G) * T * D), (short)0, G * T * D * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const bf16*)a.dout + (size_t)(b * a.Hq + kvh * G) * T * D), (short)0, G * T * D * 2,
       kRsrcWord3);
-  // per-row information, one kind per wave of the first four: lse (0), delta (1), w_bar and
-  // the mask word's half that holds bit c (2), the row index (3, no load)
   const int kindw = __builtin_amdgcn_readfirstlane(wv);
   const float* ibase = kindw == 0 ? a.lse + (size_t)(b * a.Hq + kvh * G) * T
                      : kindw == 1 ? delta + (size_t)(b * a.Hq + kvh * G) * T
@@ -480,25 +486,39 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc((void*)ibase, (short)0, irange, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.mask + (size_t)bk * T * a.W), (short)0, kindw == 2 ? T * a.W * 8 : 0, kRsrcWord3);
-  uint4 qreg[2][PT], oreg[2][PT];
-  float inf_raw[2] = {0.f, 0.f};                  // lse / delta / w_bar of this thread's row
-  uint32_t inf_bits[2] = {0u, 0u};                // the mask half-word (kind 2)
-  int inf_row[2] = {0, 0};                        // the row index t
-  bool inf_own[2] = {false, false};               // the span's block is chunk c's own
+  // this lane's tile position in each of the wave's NBLK blocks: row and first element
+  int drow[NBLK], dcol[NBLK];
+#pragma unroll
+  for (int j = 0; j < NBLK; ++j) {
+    const int byte = (wv * NBLK + j) * 1024 + 16 * lane;
+    drow[j] = byte / (2 * D);
+    dcol[j] = 8 * (((byte % (2 * D)) >> 4) ^ swz<D>(drow[j]));
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto qslot = [&](auto set_tag) -> uint8_t* {
+    constexpr int S = decltype(set_tag)::value;
+    if constexpr (S == 0) return rs0; else if constexpr (S == 1) return rs1;
+    else if constexpr (S == 2) return rs2; else return rs3;
+  };
+  auto oslot = [&](auto set_tag) -> uint8_t* { return qslot(set_tag) + SB; };
+  float inf_raw[NBUF];                            // lse / delta / w_bar of this thread's row
+  uint32_t inf_bits[NBUF];                        // the mask half-word (kind 2)
+  int inf_row[NBUF];                              // the row index t
+  bool inf_own[NBUF];                             // the span's block is chunk c's own
   const int lgG = __builtin_ctz(G);               // G is a power of two
-  // (a span index past the last one loads nothing: every offset is out of range)
   auto prefetch = [&](int s_any, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
     const bool live = s_any < nspan;
     const int s = live ? s_any : 0;
     const int blk = blist[s >> lgG], sp = s & (G - 1);
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int nn = SPAN * sp + srow[i], tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
-      const int off = live && tr < T ? (((gg * T + tr) * D + scol[i]) * 2) : kOob;
-      qreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-      oreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
+    for (int j = 0; j < NBLK; ++j) {
+      const int nn = SPAN * sp + drow[j], tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
+      const int off = live && tr < T ? (((gg * T + tr) * D + dcol[j]) * 2) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(qslot(set_tag) + (wv * NBLK + j) * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(oslot(set_tag) + (wv * NBLK + j) * 1024), 16, off, 0, 0, 0);
     }
+    asm volatile("" ::: "memory");                // the row values are issued after the tiles
     const int m = tid % SPAN;
     const int nn = SPAN * sp + m, tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
     const bool ok = live && tr < T && tid < 3 * SPAN;
@@ -509,14 +529,16 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     inf_row[S] = tr;
     inf_own[S] = blk == c;
   };
-  auto stash = [&](int buf, auto set_tag) {
+  // every span issues 2 NBLK tile loads and 2 row-value loads per wave, in that order; before
+  // slot S is used, every wave waits until at most the NBUF - 2 younger spans' loads are in
+  // flight, i.e. this span's tiles have landed in LDS, and the workgroup meets at a barrier
+  constexpr int kLoadsPerSpan = 2 * NBLK + 2;
+  constexpr int kWaitN = (NBUF - 2) * kLoadsPerSpan;
+  static_assert(kWaitN < 64, "vmcnt holds 6 bits");
+  auto stash = [&](auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      *reinterpret_cast<bf16x8*>(&lq[buf][tile_off<D>(srow[i], scol[i])]) =
-          scale_bf16x8(__builtin_bit_cast(bf16x8, qreg[S][i]), sl2);
-      *reinterpret_cast<uint4*>(&ldo[buf][tile_off<D>(srow[i], scol[i])]) = oreg[S][i];
-    }
+    // s_waitcnt vmcnt(kWaitN) with expcnt and lgkmcnt left free (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt((kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8));
     if (tid < 4 * SPAN) {
       const int kind = tid / SPAN;
       const int tr = inf_row[S];
@@ -528,8 +550,16 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
         else if (inf_own[S]) v = 0.f;             // the block's own chunk: no prior
         else v = ((inf_bits[S] >> (c & 31)) & 1u) ? a.sigma * fast_log2(inf_raw[S]) : -INFINITY;
       } else v = (float)tr;
-      qinfo[buf][kind][tid % SPAN] = v;
+      qinfo[S][kind][tid % SPAN] = v;
     }
+  };
+  // a barrier without the fence of __syncthreads (whose release would wait for every load in
+  // flight, the ring's included): LDS writes are waited for explicitly, and the compiler may
+  // not move memory operations across it
+  auto ring_barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   floatx4 dk[NDT], dv[NDT];
@@ -539,23 +569,36 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     dv[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // the ring starts as zeros, so every value a masked row ever reads is finite
+  for (int i = tid; i < 2 * SB / 16; i += NT) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(rs0)[i] = z;
+    reinterpret_cast<uint4*>(rs1)[i] = z;
+    reinterpret_cast<uint4*>(rs2)[i] = z;
+    reinterpret_cast<uint4*>(rs3)[i] = z;
+  }
+  __syncthreads();
+
   const int r0 = 32 * half_q;                     // this wave's 32 rows of the span tile
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   prefetch(0, S0{});
   prefetch(1, S1{});
-  // span s: its registers (set s & 1) go to LDS buffer s & 1, which span s - 2 read before
-  // every wave passed the barrier of span s - 1; then the set is refilled with span s + 2
-  auto span_step = [&](int s, auto set_tag) {
+  prefetch(2, S2{});
+  // span s: slot s % NBUF, whose loads went out NBUF - 1 spans earlier; then the slot that
+  // span s - 1 used (every wave finished it before this barrier) is refilled with s + 3
+  auto span_step = [&](int s, auto set_tag, auto next_tag) {
     constexpr int SS = decltype(set_tag)::value;
     const int buf = SS;
-    stash(buf, set_tag);
-    const bool own = blist[s >> lgG] == c;
-    __syncthreads();
-    prefetch(s + 2, set_tag);
+    stash(set_tag);
+    const bool own = blist[(s < nspan ? s : 0) >> lgG] == c;
+    ring_barrier();
+    prefetch(s + NBUF - 1, next_tag);
     if (s >= nspan) return;                       // past the last span (whole workgroup)
-    const uint8_t* ql = lq[buf];
-    const uint8_t* ol = ldo[buf];
+    const uint8_t* ql = qslot(set_tag);
+    const uint8_t* ol = oslot(set_tag);
     // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- tile row
     // r0 + 8 (l16 / 4) + 4 h + l16 % 4, so lane (l16, lg) holds rows r0 + 8 lg + 4 h + i
     floatx4 sv[2], dpv[2];
@@ -588,27 +631,39 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
       dk[dt] = mma(dsa, tile_tr8<D>(ql, r0, 16 * dt, lane), dk[dt]);
     }
   };
-  // both halves run every round (a span past the end only stashes and prefetches), so the
+  // all four steps run every round (a span past the end only stashes and prefetches), so the
   // loads in flight are the same on every path
-  for (int s = 0; s < nspan; s += 2) {
-    span_step(s, S0{});
-    span_step(s + 1, S1{});
+  for (int s = 0; s < nspan; s += NBUF) {
+    span_step(s, S0{}, S3{});
+    span_step(s + 1, S1{}, S0{});
+    span_step(s + 2, S2{}, S1{});
+    span_step(s + 3, S3{}, S2{});
   }
   // lane holds rows (keys) 16 kg + 4 lg + i, column d = 16 dt + l16.  dK = s sum dS q
   // = ln 2 * sum dS (q sm_scale log2 e).  The second half's waves hand their sums to the
-  // first half's through LDS (the span tiles, free after the barrier), which add them into
-  // the fp32 accumulators.
+  // first half's through LDS (the span tiles, free once the ring's last loads, past the
+  // end, have landed), which add them into the fp32 accumulators.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  float* xk = reinterpret_cast<float*>(&lq[0][0]);     // [4 key groups][64 lanes][NDT * 4]
-  float* xv = reinterpret_cast<float*>(&ldo[0][0]);
-  static_assert(4 * 64 * NDT * 4 * 4 <= 2 * SB, "hand-over fits the span tiles");
+  // [4 key groups][64 lanes][NDT / 2 * 4] floats per tile: d tiles dt < NDT / 2 in slot 0,
+  // the others in slot 1 (dK in the Q tiles, dV in the dO tiles)
+  constexpr int HD = NDT / 2;
+  static_assert(4 * 64 * HD * 4 * 4 <= SB, "hand-over fits two slots");
+  auto xk = [&](int dt, int i) -> float& {
+    float* base = reinterpret_cast<float*>(dt < HD ? rs0 : rs1);
+    return base[(kg * 64 + lane) * HD * 4 + (dt % HD) * 4 + i];
+  };
+  auto xv = [&](int dt, int i) -> float& {
+    float* base = reinterpret_cast<float*>(dt < HD ? rs0 + SB : rs1 + SB);
+    return base[(kg * 64 + lane) * HD * 4 + (dt % HD) * 4 + i];
+  };
   if (half_q == 1) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xk[(kg * 64 + lane) * NDT * 4 + dt * 4 + i] = dk[dt][i];
-        xv[(kg * 64 + lane) * NDT * 4 + dt * 4 + i] = dv[dt][i];
+        xk(dt, i) = dk[dt][i];
+        xv(dt, i) = dv[dt][i];
       }
   }
   __syncthreads();
@@ -620,8 +675,8 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     const size_t ro = ((size_t)bk * T + kk) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const float ok = xk[(kg * 64 + lane) * NDT * 4 + dt * 4 + i];
-      const float ov = xv[(kg * 64 + lane) * NDT * 4 + dt * 4 + i];
+      const float ok = xk(dt, i);
+      const float ov = xv(dt, i);
       atomicAdd(a.dk32 + ro + 16 * dt + l16, kLn2 * (dk[dt][i] + ok));
       atomicAdd(a.dv32 + ro + 16 * dt + l16, dv[dt][i] + ov);
     }
@@ -1022,7 +1077,7 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
 
 // ------------------------------------------------------------------------------ launcher
 int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delta, size_t* off_ub,
-                          size_t* off_kbt, size_t* off_rho, size_t* total) {
+                          size_t* off_kbt, size_t* off_rho, size_t* off_qsc, size_t* total) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const int nc = (T + kChunk - 1) / kChunk, W = (nc + 63) / 64, ncp = 32 * ((nc + 31) / 32);
   size_t o = 0;
@@ -1034,14 +1089,17 @@ int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delt
   o += al((size_t)B * Hkv * D * ncp * 2);
   *off_rho = o;
   o += al((size_t)B * Hq * T * 4);
+  *off_qsc = o;                                   // Q pre-scaled for the dK/dV span loads
+  o += al((size_t)B * Hq * T * D * 2);
   *total = o;
   return 0;
 }
 
 template <int D>
 static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, hipStream_t s) {
-  size_t od, ou, ok, orho, tot;
-  backward_mfma_scratch(a.B, a.Hq, a.Hkv, a.T, a.D, &od, &ou, &ok, &orho, &tot);
+  size_t od, ou, ok, orho, oqs, tot;
+  backward_mfma_scratch(a.B, a.Hq, a.Hkv, a.T, a.D, &od, &ou, &ok, &orho, &oqs, &tot);
+  bf16* qsc = reinterpret_cast<bf16*>(scratch + oqs);
   float* delta = reinterpret_cast<float*>(scratch + od);
   uint64_t* ub = reinterpret_cast<uint64_t*>(scratch + ou);
   bf16* kbt = reinterpret_cast<bf16*>(scratch + ok);
@@ -1068,8 +1126,13 @@ static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, h
       default: k_bwd_dq_mfma<D, 4, 64><<<grid, 256, 0, s>>>(a, delta); break;
     }
   }
-  // dK (Stage 2's part) and dV
-  k_bwd_dkdv_mfma<D><<<dim3(a.nc, (nblk + kBwdRange - 1) / kBwdRange, BH), 512, 0, s>>>(a, delta, ub, nblk);
+  // dK (Stage 2's part) and dV, from Q pre-scaled as the forward used it
+  {
+    const size_t n8 = rows * D / 8;
+    const unsigned gq = (unsigned)std::min<size_t>((n8 + 255) / 256, 8192);
+    k_bwd_qscale<D><<<gq, 256, 0, s>>>(a, qsc);
+  }
+  k_bwd_dkdv_mfma<D><<<dim3(a.nc, (nblk + kBwdRange - 1) / kBwdRange, BH), 512, 0, s>>>(a, delta, ub, nblk, qsc);
   // Stage 1: dq (final) and rho, then dK_bar
   {
     const int R = 16 / G;
