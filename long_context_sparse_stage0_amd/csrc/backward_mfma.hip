@@ -263,9 +263,18 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const f
     goff[i] = (row * D + ch * 8) * 2;
     loff[i] = tile_off<D>(row, ch * 8);
   }
-  uint4 kreg[PT], vreg[PT];
-  auto prefetch = [&](int c_any) {
-    const int c = __builtin_amdgcn_readfirstlane(c_any);
+  // three register sets: the K/V tiles and the routing weight of visits v + 1 and v + 2 are
+  // in flight while visit v computes; every load is unconditional (a visit past the last
+  // reads the first visit's chunk with offsets past the range, as zeros), so the compiler's
+  // waits are exact
+  constexpr int kOob = 0x7ffffff0;
+  uint4 kreg[3][PT], vreg[3][PT];
+  float wnext[3];
+  bool onnext[3];
+  auto prefetch = [&](int v_any, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    const bool live = v_any < nvis;
+    const int c = __builtin_amdgcn_readfirstlane((int)visit[live ? v_any : 0]);
     const int nbytes = min(T - c * kChunk, kChunk) * D * 2;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (size_t)c * kChunk * D), (short)0, nbytes, kRsrcWord3);
@@ -273,29 +282,35 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const f
         (void*)(vbase + (size_t)c * kChunk * D), (short)0, nbytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, goff[i], 0, 0));
-      vreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, goff[i], 0, 0));
+      const int off = live ? goff[i] : kOob;
+      kreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+      vreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
+    onnext[S] = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
+    wnext[S] = a.wbar[((size_t)bk * T + (qok ? t : T - 1)) * a.nc + c];
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      *reinterpret_cast<uint4*>(&lds_k[buf][loff[i]]) = kreg[i];
-      *reinterpret_cast<uint4*>(&lds_v[buf][loff[i]]) = vreg[i];
+      *reinterpret_cast<uint4*>(&lds_k[buf][loff[i]]) = kreg[S][i];
+      *reinterpret_cast<uint4*>(&lds_v[buf][loff[i]]) = vreg[S][i];
     }
   };
-  float wnext = 1.f;
-  bool onnext = false;
-  auto fetch_weight = [&](int c) {
-    onnext = (rowbits[r][c >> 6] >> (c & 63)) & 1ull;
-    wnext = a.wbar[((size_t)bk * T + (qok ? t : T - 1)) * a.nc + c];
+  // a barrier without the fence of __syncthreads, whose release would wait for every load in
+  // flight: this wave's LDS writes are waited for explicitly, and the compiler may not move
+  // memory operations across it
+  auto tile_barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   floatx4 dq[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dq[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto visit_chunk = [&](int buf, int c, float bias2, float wb, auto diag_tag) {
+  auto visit_chunk = [&](int buf, int c, float bias2, float wb, auto diag_tag) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     asm volatile("" ::: "memory");
     if (!DIAG && __builtin_amdgcn_ballot_w64(bias2 != -INFINITY) == 0ull) return;
@@ -350,27 +365,36 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_dq_mfma(BackwardArgs a, const f
     }
   };
 
-  prefetch(visit[0]);
-  stash(0);
-  __syncthreads();
-  if (1 < nvis) {
-    prefetch(visit[1]);
-    fetch_weight(visit[1]);
-  }
+  // visit v: its tiles, loaded into register set v % 3, go to LDS slot v & 1 (which visit
+  // v - 2 read before every wave passed visit v - 1's barrier); then the set is refilled with
+  // visit v + 3.  Visit 0, the diagonal, is peeled; the later ones go three per round.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  prefetch(0, S0{});
+  prefetch(1, S1{});
+  prefetch(2, S2{});
+  stash(0, S0{});
+  tile_barrier();
+  prefetch(3, S0{});
   visit_chunk(0, it, 0.f, 0.f, std::true_type{});
-  for (int v = 1; v < nvis; ++v) {
+  auto step = [&](int v, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
     const int buf = v & 1;
-    stash(buf);
-    const int c = visit[v];
-    const float wb = wnext;
-    const float bias2 = onnext ? a.sigma * fast_log2(wnext) : -INFINITY;
-    __syncthreads();
-    if (v + 1 < nvis) {
-      prefetch(visit[v + 1]);
-      fetch_weight(visit[v + 1]);
-    }
-    visit_chunk(buf, c, bias2, wb, std::false_type{});
+    stash(buf, set_tag);
+    const int c = visit[v < nvis ? v : 0];
+    const float wb = wnext[S];
+    const float bias2 = onnext[S] ? a.sigma * fast_log2(wnext[S]) : -INFINITY;
+    tile_barrier();
+    prefetch(v + 3, set_tag);
+    if (v < nvis) visit_chunk(buf, c, bias2, wb, std::false_type{});
+  };
+  for (int v = 1; v < nvis; v += 3) {
+    step(v, S1{});
+    step(v + 1, S2{});
+    step(v + 2, S0{});
   }
+  __builtin_amdgcn_s_waitcnt(0);                  // the prefetches past the last visit
   if (qok) {
     float* dst = a.dq32 + qi * D;
 #pragma unroll
