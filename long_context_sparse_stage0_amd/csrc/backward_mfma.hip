@@ -621,6 +621,9 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     ring_barrier();
     prefetch(s + NBUF - 1, next_tag);
     if (s >= nspan) return;                       // past the last span (whole workgroup)
+    // a wave none of whose 32 rows of the span routes to chunk c has P = dS = 0 there and
+    // adds exactly nothing: it skips the span (the block's own chunk is never skipped)
+    if (__builtin_amdgcn_ballot_w64(qinfo[buf][2][r0 + (lane & 31)] != -INFINITY) == 0ull) return;
     const uint8_t* ql = qslot(set_tag);
     const uint8_t* ol = oslot(set_tag);
     // S = Q K^T, dP = dO V^T over two halves; half h, A row l16 <- tile row
