@@ -434,8 +434,10 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   // (each slot holds the Q tile, then the dO tile)
   __shared__ __attribute__((aligned(16))) uint8_t rs0[2 * SB], rs1[2 * SB], rs2[2 * SB], rs3[2 * SB];
   __shared__ float qinfo[NBUF][4][SPAN];          // lse2, delta, bias2, t (as float)
-  __shared__ uint16_t blist[kMaxRouted + 2];
-  __shared__ int nbl_s;
+  __shared__ uint16_t blist[kBwdRange];          // candidate blocks (own first)
+  __shared__ uint32_t spanbits[kBwdRange];        // per candidate block: its live spans
+  __shared__ uint16_t slist[kBwdRange * 16];      // live spans: block << 4 | span
+  __shared__ int nbl_s, nspan_s;
 
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -467,7 +469,40 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   __syncthreads();
   const int nbl = nbl_s;
   if (nbl == 0) return;                           // (whole workgroup)
-  const int nspan = nbl * G;                      // 64-vector spans (G per 64-row block)
+  // ---- live spans: a span is 64 / G rows of a block (times its G heads); it is walked only
+  // if one of its rows routes to chunk c (every span of the own block is, causally).  Lane l
+  // of a wave reads row l's mask word of a candidate block; waves take the blocks in turn.
+  const int rps = kChunk / G;                     // rows per span
+  for (int i = wv; i < nbl; i += NT / 64) {
+    const int blk = blist[i], tt = blk * kChunk + lane;
+    bool on = tt < T;
+    if (on && blk != c) on = (a.mask[((size_t)bk * T + tt) * a.W + (c >> 6)] >> (c & 63)) & 1ull;
+    const uint64_t rows = __ballot(on);
+    uint32_t sb = 0u;
+    for (int sp = 0; sp < G; ++sp)
+      if ((rows >> (sp * rps)) & (rps == 64 ? ~0ull : ((1ull << rps) - 1ull))) sb |= 1u << sp;
+    if (lane == 0) spanbits[i] = sb;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const uint32_t sb = lane < nbl ? spanbits[lane] : 0u;
+    const int nmine = __popc(sb);
+    int incl = nmine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    int at = incl - nmine;
+    if (lane < nbl) {
+      const uint16_t hb = (uint16_t)(blist[lane] << 4);
+      for (uint32_t m = sb; m; m &= m - 1) slist[at++] = (uint16_t)(hb | __builtin_ctz(m));
+    }
+    if (lane == 63) nspan_s = incl;
+  }
+  __syncthreads();
+  const int nspan = nspan_s;                      // live 64-vector spans
+  if (nspan == 0) return;                         // (whole workgroup, before any load)
 
   // ---- this wave's keys as B operands (columns = keys)
   const int kloc = 16 * kg + l16;                 // key within the chunk
@@ -533,8 +568,8 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
   auto prefetch = [&](int s_any, auto set_tag) {
     constexpr int S = decltype(set_tag)::value;
     const bool live = s_any < nspan;
-    const int s = live ? s_any : 0;
-    const int blk = blist[s >> lgG], sp = s & (G - 1);
+    const int ent = slist[live ? s_any : 0];
+    const int blk = ent >> 4, sp = ent & 15;
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
       const int nn = SPAN * sp + drow[j], tr = blk * kChunk + (nn >> lgG), gg = nn & (G - 1);
@@ -617,7 +652,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv_mfma(BackwardArgs a, const flo
     constexpr int SS = decltype(set_tag)::value;
     const int buf = SS;
     stash(set_tag);
-    const bool own = blist[(s < nspan ? s : 0) >> lgG] == c;
+    const bool own = (slist[s < nspan ? s : 0] >> 4) == c;
     ring_barrier();
     prefetch(s + NBUF - 1, next_tag);
     if (s >= nspan) return;                       // past the last span (whole workgroup)
