@@ -20,9 +20,9 @@
 // Every step is a valid lower bound (Newton from the left on a convex function, or a
 // point where F is still positive), so the iteration is monotone and each pass that does
 // not finish drops at least one element.
-// For alpha = 1.5 and at least kEntmaxModelMinN entries, the second point comes from a
-// Gaussian model of the first pass's moments instead (see gauss_sq_tail_offset); it is used
-// only after a pass confirms F >= 0 there, so the same invariants hold.
+// For alpha = 1.5 and at least kEntmaxModelMinN entries, the starting point comes from a
+// Gaussian model of the entries' moments instead (see gauss_sq_tail_offset); it is used only
+// after a pass confirms F >= 0 there, so the same invariants hold.
 #pragma once
 #include "dash_internal.h"
 
@@ -81,28 +81,47 @@ constexpr float kEntmaxModelTarget = 1.25f;
 template <int MODE, int NR, class Red>
 __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, const Red& red,
                                   float* zsum) {
-  float m = -INFINITY;
+  // alpha = 1.5 with many entries starts from a point given by the moments of all entries
+  // (gauss_sq_tail_offset), gathered with the max; the first pass checks it is still a lower
+  // bound of tau*, else the solver resumes at the tangent of F there, which lies at or below
+  // tau* (F is convex), or at max - 1
+  const bool model = MODE == kAlpha15 && n >= kEntmaxModelMinN;
+  float m = -INFINITY, sy = 0.f, syy = 0.f;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) m = fmaxf(m, y[r]);
+  for (int r = 0; r < NR; ++r) {
+    m = fmaxf(m, y[r]);
+    if (model) {
+      const float v = y[r] > -INFINITY ? y[r] : 0.f;   // absent entries are -inf
+      sy += v;
+      syy = fmaf(v, v, syy);
+    }
+  }
   m = red.max(m);
   float tau = m - 1.0f;
   const float inv = 1.0f / (alpha - 1.0f);
   const float hi = m - ((MODE == kAlpha15) ? rsqrtf((float)n)
                                             : (MODE == kAlpha2 ? 1.0f / (float)n
                                                                : pow_pos((float)n, 1.0f - alpha)));
-  // alpha = 1.5 with many entries: after the first pass, a point from the support's moments
-  // (gauss_sq_tail_offset); the next pass checks it is still a lower bound of tau*, else the
-  // solver resumes at the tangent of F there, which lies at or below tau* (F is convex)
-  const bool model = MODE == kAlpha15 && n >= kEntmaxModelMinN;
   bool probe = false;
   float lo = tau;
+  if (model) {
+    const float nf = (float)n;
+    const float mean = red.sum(sy) / nf;
+    const float var = fmaxf(fmaf(-mean, mean, red.sum(syy) / nf), 0.f);
+    const float est = mean + gauss_sq_tail_offset(nf * var, kEntmaxModelTarget) * sqrtf(var);
+    if (est > tau) {                              // false for a NaN estimate
+      tau = fminf(est, hi);
+      probe = true;
+    }
+  }
   for (int it = 0; it < 96; ++it) {
-    float cnt = 0.f, s1 = 0.f, s2 = 0.f, mn = INFINITY;
+    float s1 = 0.f, s2 = 0.f, mn = INFINITY;
+    int icnt = 0;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const float d = y[r] - tau;
       if (d > 0.f) {
-        cnt += 1.f;
+        ++icnt;
         mn = fminf(mn, d);
         if (MODE == kAlpha15) {
           s1 += d;
@@ -116,7 +135,7 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
         }
       }
     }
-    cnt = red.sum(cnt);
+    const float cnt = red.sum((float)icnt);
     s1 = red.sum(s1);
     if (MODE != kAlpha2) s2 = red.sum(s2);
     mn = red.min(mn);
@@ -143,18 +162,7 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
           break;
         }
       }
-      float nt = fminf(tau + fmaxf(F / (2.0f * s1), mn), hi);
-      if (model && it == 0) {
-        const float mean = s1 / cnt, var = fmaxf(fmaf(-mean, mean, s2 / cnt), 0.f);
-        const float est =
-            tau + mean + gauss_sq_tail_offset(cnt * var, kEntmaxModelTarget) * sqrtf(var);
-        if (est > nt) {                       // false for a NaN estimate
-          lo = nt;
-          nt = fminf(est, hi);
-          probe = true;
-        }
-      }
-      tau = nt;
+      tau = fminf(tau + fmaxf(F / (2.0f * s1), mn), hi);
     } else {
       const float F = s2 - 1.0f;
       const float step = F / (inv * s1);
