@@ -8,7 +8,8 @@
 // Kernels (launch order):
 //   k_bwd_delta     Delta = <dO, O> per (b, head, row).
 //   k_bwd_union     per (b, kv head, 64-row block) the OR of its rows' mask words.
-//   k_bwd_kbart     the fp32 summaries as a bf16 [d][chunk] plane (Stage 1's dq operand).
+//   k_bwd_ksplit    the summaries split into bf16 hi and lo rows, chunk-major (Stage 1's
+//                   operands, gathered by chunk).
 //   k_bwd_dq_mfma   query-outer, the forward's work unit and union walk: per visit
 //                   S^T = K Q^T seeded with bias - lse (so the MFMA returns log2 P),
 //                   dP^T = V dO^T, dS = P (dP - Delta), dQ^T += K^T dS^T (K^T read from the
@@ -25,12 +26,13 @@
 //                   Workgroups are dispatched range by range, so the ones in flight share one
 //                   range's queries and output gradients through the caches.
 //   k_bwd_route_dq  Stage 1, row-outer (the forward router's work unit, 16 query vectors on
-//                   8 waves): pass 1 recomputes the scores (hi + lo planes) and each head's
-//                   weights from its saved tau, z, and reduces sum s and sum s dp into rho;
-//                   pass 2 recomputes them, forms dx and adds dq += gamma scale dx K_bar on
-//                   MFMA (dx straight from the score registers, K_bar from the [d][chunk]
-//                   plane); writes the final dq and rho.  A tile's operand, mask and dL/dw_bar
-//                   loads are issued one tile ahead.
+//                   8 waves), over the chunks routed to its rows only (listed in LDS): pass 1
+//                   recomputes the scores (hi + lo rows) and each head's weights from its saved
+//                   tau, z, and reduces sum s and sum s dp into rho; pass 2 recomputes them,
+//                   forms dx and adds dq += gamma scale dx K_bar on MFMA (dx straight from the
+//                   score registers, K_bar's operand the hi rows transposed through LDS);
+//                   writes the final dq and rho.  A tile's operand and dL/dw_bar loads are
+//                   issued one tile ahead.
 //   k_bwd_route_dk  Stage 1, chunk-outer: one workgroup per (b, kv head, 16 chunks, slice of
 //                   8192 query vectors of the later rows); its waves take spans of 32 vectors,
 //                   recompute the span's scores as S = Q K_bar^T (rows permuted as in
@@ -53,6 +55,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kBwdRange = 64;            // query blocks per dK/dV workgroup range
 constexpr int kBwdSlice = 8192;          // query vectors per Stage 1 dK_bar workgroup
+constexpr int kRouteDqWaves = 8;         // waves per Stage 1 dq workgroup
 
 __device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -155,15 +158,19 @@ __global__ void k_bwd_union(BackwardArgs a, uint64_t* __restrict__ ub, int nblk)
   }
 }
 
-// kbt[bk][d][c] = bf16(summ[bk][c][d]) for the complete chunks, zero past them (up to ncp)
-__global__ void k_bwd_kbart(BackwardArgs a, bf16* __restrict__ kbt, int ncp) {
+// kcm[bk][c][p][d]: the summaries of the complete chunks split as Stage 0 splits them
+// (p = 0: bf16(k_bar), p = 1: bf16(k_bar - that)), chunk-major, so that a gathered chunk's
+// hi and lo rows are whole cache lines
+__global__ void k_bwd_ksplit(BackwardArgs a, bf16* __restrict__ kcm) {
   const int bk = blockIdx.y;
-  const int nfull = a.T / kChunk;
-  const size_t n = (size_t)a.D * ncp;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int d = (int)(i / ncp), c = (int)(i % ncp);
-    const float v = c < nfull ? a.summ[((size_t)bk * a.nc + c) * a.D + d] : 0.f;
-    kbt[(size_t)bk * n + i] = (bf16)v;
+  const int n = (a.T / kChunk) * a.D;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int c = i / a.D, d = i % a.D;
+    const float v = a.summ[((size_t)bk * a.nc + c) * a.D + d];
+    const bf16 h = (bf16)v;
+    bf16* o = kcm + ((size_t)bk * a.nc + c) * 2 * a.D;
+    o[d] = h;
+    o[a.D + d] = (bf16)(v - (float)h);
   }
 }
 
@@ -753,32 +760,71 @@ __device__ __forceinline__ float jac_s(float p, float alpha) {   // p^(2 - alpha
   return pow_pos(p, 2.0f - alpha);
 }
 
-// Row-outer: 16 query vectors (R = 16 / G rows of one block) on 8 waves; wave w takes the
-// 16-chunk tiles w, w + 8, ...
-template <int D, int MODE>
-__global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16* __restrict__ kbt,
-                                                     int ncp, float* __restrict__ rho_out) {
-  constexpr int NW = 8, KS = D / 32, NDT = D / 16;
+// Row-outer: 16 query vectors (R = 16 / G rows of one block) on 8 waves.  Both passes run
+// over the chunks routed to any of the R rows only, listed in LDS from the union of their mask
+// words: a head's entmax support lies inside its row's routed set, so s and dx vanish outside
+// it.  Wave w takes the 16-entry list tiles w, w + 8, ...
+template <int D, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void k_bwd_route_dq(BackwardArgs a, const bf16* __restrict__ kcm,
+                                                         float* __restrict__ rho_out) {
+  constexpr int NT = NW * 64, KS = D / 32, NDT = D / 16;
+  constexpr int MAXW = kMaxRouted / 64;           // mask words of the chunks before a row
+  constexpr int XT = 32 * 2 * D;                  // bytes of a wave's 32-row transpose tile
+  constexpr int DQS = NW * 16 * (D + 4) * 4;      // bytes of the waves' partial dq
+  constexpr int UB = DQS > NW * XT ? DQS : NW * XT;
   __shared__ float part[2][NW][16];
-  __shared__ float dqs[NW][16][D + 4];
+  __shared__ uint64_t rowbits[16][MAXW];
+  __shared__ int woff[MAXW + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t clist[kMaxRouted + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ubuf[UB];   // transpose tiles, then dq parts
   const int G = a.Hq / a.Hkv;
   const int R = 16 / G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int T = a.T;
   const int BH = a.B * a.Hkv;
-  const int ntile_r = (T + R - 1) / R;
   const int w_id = gridDim.x - 1 - blockIdx.x;    // late (heavy) rows first
   const int rt = w_id / BH, bk = w_id % BH;
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int row0 = rt * R;
-  const int it = row0 / kChunk;
-  (void)ntile_r;
+  const int it = row0 / kChunk;                   // the same for all R rows (R divides 64)
+
+  // ---- the list of chunks routed to any of the rows (ascending)
+  const int nwr = (it + 63) / 64;
+  for (int idx = tid; idx < R * nwr; idx += NT) {
+    const int rr = idx / nwr, w = idx % nwr;
+    const int tt = row0 + rr;
+    uint64_t m = tt < T ? a.mask[((size_t)bk * T + tt) * a.W + w] : 0ull;
+    if (w == nwr - 1 && (it & 63) != 0) m &= (1ull << (it & 63)) - 1;
+    rowbits[rr][w] = m;
+  }
+  __syncthreads();
+  uint64_t un = 0;
+  if (tid < nwr) {
+    for (int rr = 0; rr < R; ++rr) un |= rowbits[rr][tid];
+    woff[tid + 1] = __popcll(un);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    woff[0] = 0;
+    for (int w = 0; w < nwr; ++w) woff[w + 1] += woff[w];
+  }
+  __syncthreads();
+  const int ncl = woff[nwr];
+  if (tid < nwr) {
+    int o = woff[tid];
+    while (un) {
+      clist[o++] = (uint16_t)(64 * tid + __builtin_ctzll(un));
+      un &= un - 1;
+    }
+  }
+  if (tid < 16) clist[ncl + tid] = 0;             // the last tile's tail: chunk 0, weight 0
+  __syncthreads();
+
   const int n = l16, r = n / G, g = n % G;
   const int t = row0 + r;
   const bool qok = t < T;
   const size_t qi = (size_t)(b * a.Hq + kvh * G + g) * T + (qok ? t : 0);
-  const size_t rowi = (size_t)bk * T + (qok ? t : 0);
   bf16x8 qop[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -791,49 +837,47 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
   const bool act = qok && it > 0;
   const float tau = act ? a.tau[qi] : 0.f;
   const float rz = act ? 1.0f / a.z[qi] : 0.f;
-  const int ntile = (it + 15) / 16;
+  const int ntile = (ncl + 15) / 16;
   const int nj = ntile > wv ? (ntile - wv + NW - 1) / NW : 0;
 
-  // A tile's loads (this wave's tiles wv, wv + NW, ...): the hi and lo summary operands of its
-  // 16 chunks, the mask half-word of the lane's row that holds them and the lane's four
-  // dL/dw_bar values, all as buffer loads issued together and without branches (a tile past
-  // the wave's last one, or a chunk at or past it, reads as zero), so the loads of the next
-  // tile are in flight while this one is evaluated.
+  // A tile's loads (this wave's tiles wv, wv + NW, ...): the hi and lo summary rows of its 16
+  // listed chunks from the chunk-major split copy, and the lane's four dL/dw_bar values, all as
+  // buffer loads issued together and without branches (a tile past the wave's last one reads
+  // as zero), so the loads of the next tile are in flight while this one is evaluated.
   constexpr int kOob = 0x7ffffff0;
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.ssplit + (size_t)bk * split_bk_stride(a.nc, D)), (short)0,
-      (int)(split_bk_stride(a.nc, D) * 2), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.mask + (size_t)bk * T * a.W), (short)0, T * a.W * 8, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kcm + (size_t)bk * a.nc * 2 * D), (short)0, a.nc * 2 * D * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.dwb + (size_t)bk * T * a.nc), (short)0, T * a.nc * 4, kRsrcWord3);
   const int trow = qok ? t : 0;
   struct TileLoads {
     bf16x8 hi[KS], lo[KS];
-    uint32_t mw;
+    uint32_t cc[2];                               // the lane's four chunk ids, 16 bits each
     float dw[4];
   };
-  auto load_tile = [&](int j, TileLoads& L) {
+  auto chunk_of = [](const TileLoads& L, int i) { return (int)((L.cc[i >> 1] >> (16 * (i & 1))) & 0xffffu); };
+  auto load_tile = [&](int j, TileLoads& L) __attribute__((always_inline)) {
     const int ct = wv + NW * j;
     const bool live = j < nj;
-    const int crow = 16 * ct + l16;
+    const int crow = clist[live ? 16 * ct + l16 : 0];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       L.hi[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                     srs, live ? split_offset(crow, 0, 32 * ks + 8 * lg, D) * 2 : kOob, 0, 0));
+                     crs, live ? (2 * crow * D + 32 * ks + 8 * lg) * 2 : kOob, 0, 0));
       L.lo[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                     srs, live ? split_offset(crow, 1, 32 * ks + 8 * lg, D) * 2 : kOob, 0, 0));
+                     crs, live ? ((2 * crow + 1) * D + 32 * ks + 8 * lg) * 2 : kOob, 0, 0));
     }
-    const int c0 = 16 * ct + 4 * lg;              // the lane's chunks c0 .. c0 + 3
-    L.mw = __builtin_amdgcn_raw_buffer_load_b32(
-        mrs, live && act ? (trow * a.W + (c0 >> 6)) * 8 + ((c0 & 63) >= 32 ? 4 : 0) : kOob, 0, 0);
+    const int p0 = 16 * ct + 4 * lg;              // the lane's list entries p0 .. p0 + 3
+    const uint2 cc = *reinterpret_cast<const uint2*>(&clist[live ? p0 : 0]);
+    L.cc[0] = cc.x;
+    L.cc[1] = cc.y;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       L.dw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                    wrs, live && act && c0 + i < it ? (trow * a.nc + c0 + i) * 4 : kOob, 0, 0));
+                    wrs, live && act && p0 + i < ncl ? (trow * a.nc + chunk_of(L, i)) * 4 : kOob, 0, 0));
   };
-  // s and dp of the lane's 4 chunks of a loaded tile
-  auto eval_tile = [&](int j, const TileLoads& L, float (&s4)[4], float (&dp4)[4]) {
+  // s and dp of the lane's 4 list entries of a loaded tile
+  auto eval_tile = [&](int j, const TileLoads& L, float (&s4)[4], float (&dp4)[4]) __attribute__((always_inline)) {
     const int ct = wv + NW * j;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -843,14 +887,14 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int cc = 16 * ct + 4 * lg + i;
       s4[i] = 0.f;
       dp4[i] = 0.f;
-      if (act && j < nj && cc < it) {
+      if (act && j < nj && 16 * ct + 4 * lg + i < ncl) {
         const float p = entmax_weight<MODE>(zscale * acc[i], tau, inv, rz);
         if (p > 0.f) {
+          const int c = chunk_of(L, i);
           s4[i] = jac_s<MODE>(p, a.alpha);
-          dp4[i] = ((L.mw >> (cc & 31)) & 1u) ? L.dw[i] * rG : 0.f;
+          dp4[i] = ((rowbits[r][c >> 6] >> (c & 63)) & 1ull) ? L.dw[i] * rG : 0.f;
         }
       }
     }
@@ -893,53 +937,49 @@ __global__ __launch_bounds__(512) void k_bwd_route_dq(BackwardArgs a, const bf16
   }
   const float rho = sst > 0.f ? sdt / sst : 0.f;
   if (wv == 0 && lg == 0 && qok) rho_out[qi] = rho;
-  // ---- pass 2: dx, and dq += gs * dX K_bar over pairs of tiles (k-slots i < 4: tile a,
-  // chunks 16 ta + 4 lg + i; i >= 4: tile b, chunks 16 tb + 4 lg + i - 4)
+  // ---- pass 2: dx, and dq += gs * dX K_bar over pairs of tiles (k-slots i < 4: tile j, list
+  // entries 16 ta + 4 lg + i; i >= 4: tile j + 1, entries 16 tb + 4 lg + i - 4).  K_bar's operand
+  // is the pair's hi rows, already in registers for the scores, written into this wave's LDS
+  // tile in that k-slot order (entry p of tile j at row 8 (p >> 2) + (p & 3), of tile j + 1 four
+  // rows further) and read back transposed.
   floatx4 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bf16* kb = kbt + (size_t)bk * D * ncp;
+  uint8_t* xt = ubuf + wv * XT;
+  const int xrow = 8 * (l16 >> 2) + (l16 & 3);
   {
     TileLoads A, B;
     load_tile(0, A);
     for (int j = 0; j < nj; j += 2) {
-      const int ta = wv + NW * j, tb = wv + NW * (j + 1);
-      const bool hasb = j + 1 < nj;
-      const int cb = hasb ? tb : ta;              // any valid tile: its operand is times 0
-      // the pair's K_bar operands, loaded before the tiles are evaluated
-      typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 kx[NDT], ky[NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16* kr = kb + (size_t)(16 * dt + l16) * ncp;
-        kx[dt] = *reinterpret_cast<const bf16x4*>(kr + 16 * ta + 4 * lg);
-        ky[dt] = *reinterpret_cast<const bf16x4*>(kr + 16 * cb + 4 * lg);
-      }
       bf16x8 xa;
       float s4[4], dp4[4];
       load_tile(j + 1, B);
       eval_tile(j, A, s4, dp4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<bf16x8*>(xt + tile_off<D>(xrow, 32 * ks + 8 * lg)) = A.hi[ks];
       load_tile(j + 2, A);
       eval_tile(j + 1, B, s4, dp4);               // zeros past the last tile
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[4 + i] = (bf16)(gs * s4[i] * (dp4[i] - rho));
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 bop = {kx[dt][0], kx[dt][1], kx[dt][2], kx[dt][3],
-                            ky[dt][0], ky[dt][1], ky[dt][2], ky[dt][3]};
-        acc[dt] = mma(xa, bop, acc[dt]);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<bf16x8*>(xt + tile_off<D>(xrow + 4, 32 * ks + 8 * lg)) = B.hi[ks];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma(xa, tile_tr8<D>(xt, 0, 16 * dt, lane), acc[dt]);
     }
   }
+  __syncthreads();                                // every wave is done with its transpose tile
   // lane: C[4 lg + i][l16] = (query vector 4 lg + i, d = 16 dt + l16); sum the waves in LDS
+  float (*dqs)[16][D + 4] = reinterpret_cast<float (*)[16][D + 4]>(ubuf);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dqs[wv][4 * lg + i][16 * dt + l16] = acc[dt][i];
   __syncthreads();
-  for (int idx = tid; idx < 16 * D; idx += 512) {
+  for (int idx = tid; idx < 16 * D; idx += NT) {
     const int nn = idx / D, d = idx % D;
     const int rr = nn / G, gg = nn % G, tt = row0 + rr;
     if (tt >= T) continue;
@@ -1139,16 +1179,16 @@ __global__ __launch_bounds__(512) void k_bwd_route_dk(BackwardArgs a, const floa
 
 // ------------------------------------------------------------------------------ launcher
 int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delta, size_t* off_ub,
-                          size_t* off_kbt, size_t* off_rho, size_t* off_qsc, size_t* total) {
+                          size_t* off_kcm, size_t* off_rho, size_t* off_qsc, size_t* total) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const int nc = (T + kChunk - 1) / kChunk, W = (nc + 63) / 64, ncp = 32 * ((nc + 31) / 32);
+  const int nc = (T + kChunk - 1) / kChunk, W = (nc + 63) / 64;
   size_t o = 0;
   *off_delta = o;
   o += al((size_t)B * Hq * T * 4);
   *off_ub = o;
   o += al((size_t)B * Hkv * nc * W * 8);
-  *off_kbt = o;
-  o += al((size_t)B * Hkv * D * ncp * 2);
+  *off_kcm = o;                                   // chunk-major split summaries
+  o += al((size_t)B * Hkv * nc * 2 * D * 2);
   *off_rho = o;
   o += al((size_t)B * Hq * T * 4);
   *off_qsc = o;                                   // Q pre-scaled for the dK/dV span loads
@@ -1164,16 +1204,15 @@ static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, h
   bf16* qsc = reinterpret_cast<bf16*>(scratch + oqs);
   float* delta = reinterpret_cast<float*>(scratch + od);
   uint64_t* ub = reinterpret_cast<uint64_t*>(scratch + ou);
-  bf16* kbt = reinterpret_cast<bf16*>(scratch + ok);
+  bf16* kcm = reinterpret_cast<bf16*>(scratch + ok);
   float* rho = reinterpret_cast<float*>(scratch + orho);
   const int G = a.Hq / a.Hkv;
   const int BH = a.B * a.Hkv;
   const int nblk = a.nc;                          // 64-row query blocks = chunks
-  const int ncp = 32 * ((a.nc + 31) / 32);
   const size_t rows = (size_t)a.B * a.Hq * a.T;
   k_bwd_delta<D><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a, delta);
   k_bwd_union<<<dim3(nblk, BH), 64, 0, s>>>(a, ub, nblk);
-  k_bwd_kbart<<<dim3(64, BH), 256, 0, s>>>(a, kbt, ncp);
+  k_bwd_ksplit<<<dim3(64, BH), 256, 0, s>>>(a, kcm);
   // dQ (Stage 2's part) and dw_bar
   {
     const int NW = G >= 2 ? 8 : 4;
@@ -1202,13 +1241,13 @@ static hipError_t launch_backward_mfma_t(const BackwardArgs& a, char* scratch, h
     const int ntc = (a.nc + 15) / 16;
     const int nsl = (int)(((long long)a.T * G + kBwdSlice - 1) / kBwdSlice);
     if (a.alpha == 1.5f) {
-      k_bwd_route_dq<D, kAlpha15><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dq<D, kAlpha15, kRouteDqWaves><<<grid, kRouteDqWaves * 64, 0, s>>>(a, kcm, rho);
       k_bwd_route_dk<D, kAlpha15><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     } else if (a.alpha == 2.0f) {
-      k_bwd_route_dq<D, kAlpha2><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dq<D, kAlpha2, kRouteDqWaves><<<grid, kRouteDqWaves * 64, 0, s>>>(a, kcm, rho);
       k_bwd_route_dk<D, kAlpha2><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     } else {
-      k_bwd_route_dq<D, kAlphaGeneral><<<grid, 512, 0, s>>>(a, kbt, ncp, rho);
+      k_bwd_route_dq<D, kAlphaGeneral, kRouteDqWaves><<<grid, kRouteDqWaves * 64, 0, s>>>(a, kcm, rho);
       k_bwd_route_dk<D, kAlphaGeneral><<<dim3(ntc, nsl, BH), 512, 0, s>>>(a, rho);
     }
   }

@@ -162,7 +162,7 @@ hipError_t launch_backward_stage0(const BackwardArgs& a, hipStream_t s);
 // dk32, dv32 and dsumm added into (they must start at zero); scratch of
 // backward_mfma_scratch() bytes
 int backward_mfma_scratch(int B, int Hq, int Hkv, int T, int D, size_t* off_delta, size_t* off_ub,
-                          size_t* off_kbt, size_t* off_rho, size_t* off_qsc, size_t* total);
+                          size_t* off_kcm, size_t* off_rho, size_t* off_qsc, size_t* total);
 hipError_t launch_backward_mfma(const BackwardArgs& a, void* scratch, hipStream_t s);
 
 // summ_split (nullable, bf16 inputs only): bf16 hi and lo planes of the fp32 summaries
