@@ -967,6 +967,8 @@ __global__ __launch_bounds__(NW * 64) void k_bwd_route_dq(BackwardArgs a, const 
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         *reinterpret_cast<bf16x8*>(xt + tile_off<D>(xrow + 4, 32 * ks + 8 * lg)) = B.hi[ks];
+      // the transposing reads are not ordered behind the wave's outstanding LDS writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma(xa, tile_tr8<D>(xt, 0, 16 * dt, lane), acc[dt]);
     }

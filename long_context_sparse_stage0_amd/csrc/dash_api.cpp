@@ -398,7 +398,7 @@ BackwardLayout backward_layout(const Dims& d) {
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
   L.dhcp = off;
   off += align256((size_t)d.B * d.Hkv * d.nc * d.D * 4);
-  L.mscratch = off;          // bf16: the MFMA kernels' delta, block unions, K_bar^T, rho, scaled Q
+  L.mscratch = off;          // bf16: the MFMA kernels' delta, block unions, split K_bar, rho, scaled Q
   if (d.dtype == DASH_BF16) {
     size_t o1, o2, o3, o4, o5, tot;
     dash::backward_mfma_scratch(d.B, d.Hq, d.Hkv, d.T, d.D, &o1, &o2, &o3, &o4, &o5, &tot);

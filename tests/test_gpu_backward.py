@@ -61,10 +61,10 @@ def run_backward(dash, w, *, alpha=None, sigma=1.0, seed=1):
     assert torch.equal(out, plain), "the training forward must equal dash_prefill"
     ref = BW.prefill_backward(x["q"], x["k"], x["v"], x["head_cls"], dout, alpha=alpha,
                               gamma=w.gamma, sigma=sigma)
-    errs = {n: _check_grad(n, g.float().cpu().numpy(), ref[n], w.dtype)
-            for n, g in (("dq", dq), ("dk", dk), ("dv", dv), ("dhead_cls", dhc))}
+    got = {n: g.float().cpu().numpy() for n, g in (("dq", dq), ("dk", dk), ("dv", dv), ("dhead_cls", dhc))}
+    errs = {n: _check_grad(n, got[n], ref[n], w.dtype) for n in got}
     say("[backward]   " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
-    return x, ref
+    return x, ref, got
 
 
 def test_backward_1k_fp32(dash):
@@ -85,9 +85,43 @@ def test_backward_small(dash, dtype, G, alpha, sigma, T, D):
     w = Workload(name=f"bwd_{dtype}_g{G}", kind="prefill", B=2 if dtype == "bf16" else 1,
                  Hq=2 * G, Hkv=2, T=T, D=D, dtype=dtype, alpha=alpha, seed=1200 + G,
                  needle_amp=1.0)
-    _, ref = run_backward(dash, w, sigma=sigma, seed=G)
+    _, ref, _ = run_backward(dash, w, sigma=sigma, seed=G)
     # the routing gradient is really exercised: it reaches Stage 0's classifier query
     assert np.abs(ref["dhead_cls"]).max() > 1e-3
+
+
+def test_backward_routing_part_of_dq(dash):
+    """Stage 1's part of dq, gamma scale dx K_bar with dx the entmax Jacobian applied to
+    dL/dw_bar / G (the gradient that flows back through the router), is only a few percent
+    of dq at gamma = sigma = 1, inside the bf16 bar of the whole dq.  Here gamma = 4 and
+    sigma = 4 make it about a sixth of dq's norm, and dq's error is also measured against the
+    norm of the oracle's Stage 1 part alone: the bf16 path's whole-dq error (about 3.5e-3 of
+    |dq| in norm) is about 2% of that part, so a bar of 0.1 rejects a Stage 1 part that is
+    wrong by more than a tenth of its norm."""
+    G, T, D, gamma, sigma = 16, 400, 128, 4.0, 4.0
+    w = Workload(name="bwd_route_part", kind="prefill", B=1, Hq=2 * G, Hkv=2, T=T, D=D,
+                 dtype="bf16", gamma=gamma, seed=1600, needle_amp=1.0)
+    x, ref, got = run_backward(dash, w, sigma=sigma, seed=16)
+    scale = 1.0 / np.sqrt(D)
+    summ = F.chunk_summaries(x["k"], x["head_cls"], scale)
+    route = np.zeros_like(ref["dq"])
+    for kvh in range(2):
+        for t in range(64, T):
+            qg = x["q"][0, G * kvh:G * (kvh + 1), t].astype(np.float64)
+            _, _, p = F.route_row(qg, summ[0, kvh], t, alpha=1.5, gamma=gamma, scale=scale)
+            dp = np.broadcast_to(ref["dw_bar"][0, kvh, t, :t // 64] / G, p.shape)
+            dx = BW.entmax_backward(p, dp, 1.5)
+            route[0, G * kvh:G * (kvh + 1), t] = gamma * scale * (dx @ summ[0, kvh, :t // 64])
+    share = np.linalg.norm(route) / np.linalg.norm(ref["dq"])
+    rel = np.linalg.norm(got["dq"] - ref["dq"]) / np.linalg.norm(route)
+    say(f"[backward]   Stage 1 part {share:.3f} of |dq|; |dq error| / |Stage 1 part| {rel:.3e}")
+    assert share > 0.1, "the Stage 1 part is too small here to be checked"
+    assert rel <= 0.1, f"dq error {rel:.3e} of the Stage 1 part's norm"
+    # dk's part through the summaries (Stage 0's softmax backward of dL/dK_bar), the same way
+    dk_route, _ = BW.chunk_summaries_backward(x["k"], x["head_cls"], scale, ref["dsumm"])
+    rel_k = np.linalg.norm(got["dk"] - ref["dk"]) / np.linalg.norm(dk_route)
+    say(f"[backward]   |dk error| / |dk part through the summaries| {rel_k:.3e}")
+    assert rel_k <= 0.1, f"dk error {rel_k:.3e} of its part through the summaries"
 
 
 def test_backward_sparsemax_away_from_ties(dash):
@@ -109,7 +143,7 @@ def test_backward_tiny_sequences(dash):
     for T in (50, 100):
         w = Workload(name=f"bwd_tiny{T}", kind="prefill", B=1, Hq=4, Hkv=2, T=T, D=64,
                      dtype="fp32", seed=1400 + T, needle_amp=1.0)
-        _, ref = run_backward(dash, w)
+        _, ref, _ = run_backward(dash, w)
         # no routing (T = 50), or one routed chunk whose entmax weight is always 1
         assert np.abs(ref["dhead_cls"]).max() < 1e-12
 
