@@ -8,6 +8,7 @@ it does not know that feature, which is harmless.
 """
 from __future__ import annotations
 
+import ctypes
 import glob
 import os
 import shutil
@@ -68,6 +69,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # resolve every symbol now: a kernel whose host-side launch stub the compiler dropped
+    # links fine but cannot be loaded
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"the built library does not load: {e}") from None
     os.replace(tmp, LIB)
     return LIB
 

@@ -27,8 +27,8 @@
 // accumulator starts at bias - m, so the MFMA returns the base-2 exponent itself, and the
 // column sums of the bf16 probabilities come from one more MFMA with an all-ones operand.
 // Visits go in rounds of two behind one workgroup barrier: the K/V tiles of a round's two
-// chunks are register-prefetched during the previous round and stored into two of four LDS
-// slots (the pair the round before last used).
+// chunks are loaded straight into two of four LDS slots (the pair the round before last
+// used) during the previous round.
 //
 // LDS layout: rows are unpadded and the 16-byte chunks of a row are XOR-swizzled by row bits
 // (kswz, vswz) so that every quarter wave of an operand read or a tile store touches 16
@@ -97,17 +97,22 @@ void k_attend_mfma(AttendArgs a) {
   constexpr int VP = 64 * 2;          // V^T row pitch in LDS (bytes), chunks swizzled
   constexpr int KBYTES = 64 * KP, VBYTES = D * VP;
   constexpr int KSEG = 64 * D / 8, VSEG = D * 8;       // 16-byte segments per tile
-  // each thread moves KPT K segments and VPT V^T segments per chunk; with fewer K segments
-  // than threads, the first KSEG threads move K and the others V^T (one segment each)
-  constexpr bool SPLIT = KSEG < NT;
-  static_assert(SPLIT ? (KSEG + VSEG == NT) : (KSEG % NT == 0 && VSEG % NT == 0),
-                "tile loads must cover every thread evenly");
-  constexpr int KPT = SPLIT ? 1 : KSEG / NT, VPT = SPLIT ? 0 : VSEG / NT;
-  constexpr int VPTA = VPT > 0 ? VPT : 1;
+  // A chunk's K and V^T tiles go straight into LDS (buffer loads with an LDS destination): one
+  // such load of a wave fills 1 KiB, lane i the 16 bytes at offset 16 i, so each lane fetches
+  // the global 16 bytes that the swizzled layout puts there; NKI and NVI loads per wave cover
+  // the two tiles.
+  constexpr int NKI = KBYTES / 1024 / NW, NVI = VBYTES / 1024 / NW;
+  static_assert(NKI * NW * 1024 == KBYTES && NVI * NW * 1024 == VBYTES,
+                "tile loads must cover every wave evenly");
+  constexpr int SLOT = KBYTES + VBYTES;           // K tile, then V^T tile
   constexpr int MAXW = (kMaxRouted + 1 + 63) / 64;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[4][KBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[4][VBYTES];
+  // four tile slots as separate arrays, so that the compiler can tell the slots being filled
+  // from the ones being read and waits for the loads only where a slot is taken up
+  __shared__ __attribute__((aligned(16))) uint8_t ls0[SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ls1[SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ls2[SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ls3[SLOT];
   __shared__ uint64_t rowbits[RMAX][MAXW];
   __shared__ uint16_t visit[kMaxRouted + 2];
   __shared__ int woff[MAXW + 1];
@@ -204,26 +209,32 @@ void k_attend_mfma(AttendArgs a) {
     }
   }
 
-  // ---- global -> register prefetch of one chunk's K and V^T tiles through buffer
-  // descriptors rebased per chunk (scalar arithmetic only; each thread's byte offsets are
-  // fixed).  A K descriptor's range ends at the last key, so rows past the end of the
-  // sequence read as zeros; they only occur in the diagonal chunk, where they are masked.
+  // ---- global -> LDS prefetch of one chunk's K and V^T tiles through buffer descriptors
+  // rebased per chunk (scalar arithmetic only; each lane's byte offsets are fixed).  A K
+  // descriptor's range ends at the last key, so rows past the end of the sequence read as
+  // zeros; they only occur in the diagonal chunk, where they are masked.
   const bf16* kbase = (const bf16*)a.k + (size_t)bk * a.Tk * D;
   const bf16* vtbase = (const bf16*)a.vt + (size_t)bk * a.nc * D * 64;
-  // this thread's K half (wave-uniform) in the split layout
-  const bool kpart = !SPLIT || __builtin_amdgcn_readfirstlane(tid) < KSEG;
-  const int vseg0 = SPLIT ? tid - KSEG : tid;
-  int koff[KPT], voff[VPTA];
+  int kdo[NKI], vdo[NVI];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int seg = tid + i * NT;
-    koff[i] = (seg / (D / 8) * D + (seg % (D / 8)) * 8) * 2;
+  for (int j = 0; j < NKI; ++j) {
+    const int byte = (wv * NKI + j) * 1024 + 16 * lane;
+    const int row = byte / KP, ch = ((byte % KP) >> 4) ^ kswz<D>(row);
+    kdo[j] = row * KP + ch * 16;
   }
 #pragma unroll
-  for (int i = 0; i < VPTA; ++i) voff[i] = (vseg0 + i * NT) * 16;
-  uint4 kreg[2][KPT], vreg[2][VPTA];
-  auto prefetch = [&](int c_any, auto set_tag) {
-    constexpr int S = decltype(set_tag)::value;
+  for (int j = 0; j < NVI; ++j) {
+    const int byte = (wv * NVI + j) * 1024 + 16 * lane;
+    const int row = byte / VP, ch = ((byte % VP) >> 4) ^ vswz(row);
+    vdo[j] = row * VP + ch * 16;
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto slot = [&](auto slot_tag) -> uint8_t* {
+    constexpr int S = decltype(slot_tag)::value;
+    if constexpr (S == 0) return ls0; else if constexpr (S == 1) return ls1;
+    else if constexpr (S == 2) return ls2; else return ls3;
+  };
+  auto prefetch = [&](int c_any, auto slot_tag) {
     const int c = __builtin_amdgcn_readfirstlane(c_any);
     const int keys_left = a.Tk - c * kChunk;            // > 0 for every visited chunk
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -231,36 +242,13 @@ void k_attend_mfma(AttendArgs a) {
         kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vtbase + (size_t)c * D * 64), (short)0, D * 64 * 2, kBufferRsrcWord3);
-    if (SPLIT) {
-      kreg[S][0] = __builtin_bit_cast(uint4, kpart ? __builtin_amdgcn_raw_buffer_load_b128(kr, koff[0], 0, 0)
-                                                   : __builtin_amdgcn_raw_buffer_load_b128(vr, voff[0], 0, 0));
-      return;
-    }
+    uint8_t* base = slot(slot_tag);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      kreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0));
+    for (int j = 0; j < NKI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(base + (wv * NKI + j) * 1024), 16, (unsigned)kdo[j], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      vreg[S][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0));
-  };
-  auto stash_v = [&](int buf, int seg, const uint4& val) {
-    const int row = seg / 8, ch = seg % 8;
-    *reinterpret_cast<uint4*>(&lds_v[buf][row * VP + (ch ^ vswz(row)) * 16]) = val;
-  };
-  auto stash = [&](int buf, auto set_tag) {
-    constexpr int S = decltype(set_tag)::value;
-    if (SPLIT && !kpart) {
-      stash_v(buf, vseg0, kreg[S][0]);
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int seg = tid + i * NT;
-      const int row = seg / (D / 8), ch = seg % (D / 8);
-      *reinterpret_cast<uint4*>(&lds_k[buf][row * KP + (ch ^ kswz<D>(row)) * 16]) = kreg[S][i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) stash_v(buf, vseg0 + i * NT, vreg[S][i]);
+    for (int j = 0; j < NVI; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(base + KBYTES + (wv * NVI + j) * 1024), 16, (unsigned)vdo[j], 0, 0, 0);
   };
   // routing weight and mask bit of this lane's rows for routed chunk c, in set S (the first
   // or second visit of a round); the weight is loaded one round ahead and only turned into a
@@ -304,7 +292,7 @@ void k_attend_mfma(AttendArgs a) {
 
   // the work of one visit on the tile in LDS slot buf; DIAG: the query block's own chunk
   // (always the first visit)
-  auto visit_chunk = [&](int buf, const float (&bias)[QT], auto diag_tag) {
+  auto visit_chunk = [&](const uint8_t* sl, const float (&bias)[QT], auto diag_tag) {
     constexpr bool DIAG = decltype(diag_tag)::value;
     asm volatile("" ::: "memory");      // keep each visit's LDS reads inside it
     // a wave none of whose rows has this routed chunk adds exactly nothing (p = 0, no
@@ -315,8 +303,8 @@ void k_attend_mfma(AttendArgs a) {
       for (int qt = 0; qt < QT; ++qt) any = any || bias[qt] != -INFINITY;
       if (__builtin_amdgcn_ballot_w64(any) == 0ull) return;
     }
-    const uint8_t* kl = lds_k[buf];
-    const uint8_t* vl = lds_v[buf];
+    const uint8_t* kl = sl;
+    const uint8_t* vl = sl + KBYTES;
 
     // S^T for 64 keys: tile kt = 2 p + half
     floatx4 sc[QT][4];
@@ -422,53 +410,56 @@ void k_attend_mfma(AttendArgs a) {
     }
   };
 
-  // rounds of two visits behind one barrier: visits 2r and 2r + 1 use LDS slots 2(r & 1) and
-  // 2(r & 1) + 1, which round r - 2 used; every wave finished that round before the barrier
-  // of round r - 1.  Visit 0 is the diagonal chunk.
+  // rounds of two visits behind one barrier: visits 2r and 2r + 1 use the LDS slots of pair
+  // r & 1 (slots 0, 1 or 2, 3), whose loads went out during round r - 1 into the pair that
+  // round r - 2 used; every wave finished that round before the barrier of round r - 1.
+  // Visit 0 is the diagonal chunk.  The rounds are unrolled by pair so that each one's slots
+  // are known at compile time.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   prefetch(visit[0], S0{});
   if (1 < nvis) {
     prefetch(visit[1], S1{});
     fetch_weight(visit[1], S1{});
   }
-  auto round = [&](int r, auto first_tag) {
+  auto round = [&](int r, auto first_tag, auto pair_tag) {
     constexpr bool FIRST = decltype(first_tag)::value;   // round 0: visit 0 is the diagonal
+    constexpr int P = decltype(pair_tag)::value;
+    using A0 = std::integral_constant<int, 2 * P>;
+    using A1 = std::integral_constant<int, 2 * P + 1>;
+    using N0 = std::integral_constant<int, 2 - 2 * P>;
+    using N1 = std::integral_constant<int, 3 - 2 * P>;
     const int v0 = 2 * r, v1 = 2 * r + 1;
     const bool has1 = v1 < nvis;
-    const int b0 = 2 * (r & 1), b1 = b0 + 1;
-    stash(b0, S0{});
-    if (has1) stash(b1, S1{});
     float bias[2][QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       bias[0][qt] = (FIRST || DENSE) ? 0.f : (onnext[0][qt] ? a.sigma * fast_log2(wnext[0][qt]) : -INFINITY);
       bias[1][qt] = DENSE ? 0.f : (onnext[1][qt] ? a.sigma * fast_log2(wnext[1][qt]) : -INFINITY);
     }
+    // this round's tiles and weights are the only loads in flight: wait for them (vmcnt(0),
+    // gfx9 encoding), then meet, so every wave's share of the tiles is in LDS
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     __syncthreads();
     if (v0 + 2 < nvis) {
-      prefetch(visit[v0 + 2], S0{});
+      prefetch(visit[v0 + 2], N0{});
       fetch_weight(visit[v0 + 2], S0{});
     }
     if (v1 + 2 < nvis) {
-      prefetch(visit[v1 + 2], S1{});
+      prefetch(visit[v1 + 2], N1{});
       fetch_weight(visit[v1 + 2], S1{});
     }
-    if (FIRST) {
-      visit_chunk(b0, bias[0], std::true_type{});
-      if (has1) visit_chunk(b1, bias[1], std::false_type{});
-    } else {
-#pragma nounroll
-      for (int h = 0; h < (has1 ? 2 : 1); ++h) {
-        float bh[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) bh[qt] = h ? bias[1][qt] : bias[0][qt];
-        visit_chunk(b0 + h, bh, std::false_type{});
-      }
-    }
+    if (FIRST) visit_chunk(slot(A0{}), bias[0], std::true_type{});
+    else visit_chunk(slot(A0{}), bias[0], std::false_type{});
+    if (has1) visit_chunk(slot(A1{}), bias[1], std::false_type{});
   };
-  round(0, std::true_type{});
-  for (int r = 1; 2 * r < nvis; ++r) round(r, std::false_type{});
+  round(0, std::true_type{}, std::integral_constant<int, 0>{});
+  for (int r = 1; 2 * r < nvis; r += 2) {
+    round(r, std::false_type{}, std::integral_constant<int, 1>{});
+    if (2 * (r + 1) < nvis) round(r + 1, std::false_type{}, std::integral_constant<int, 0>{});
+  }
 
   // ---- normalise and write
 #pragma unroll
