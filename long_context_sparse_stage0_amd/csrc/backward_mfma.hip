@@ -81,11 +81,15 @@ __device__ __forceinline__ float heads_sum(float v, int G) {
   return v;
 }
 
-// XOR swizzle of the 16-byte chunk index inside a row of a [row][D] bf16 LDS tile (the
-// forward's K-tile swizzle): a quarter wave's 16-byte operand reads hit distinct slots.
+// XOR swizzle of the 16-byte chunk index inside a row of a [row][D] bf16 LDS tile.  With
+// D = 128 (16 chunks per row) row bits 4, 0, 1 and 3 go to chunk bits 0, 1, 2 and 3: the
+// 16 rows of a quarter wave's 16-byte operand read differ in row bits 0, 1, 3 and 4, so they
+// hit 16 distinct slots, and the 32 lanes of a half wave's transposing 8-byte read
+// (ds_read_b64_tr_b16: rows r + 8 lg + k, chunk bit 0 from the column) hit 32 distinct
+// 8-byte slots, the column bit landing on chunk bit 0 and the rows on bits 1 to 3.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if (D == 128) return (row & 3) | (((row >> 3) & 3) << 2);
+  if (D == 128) return ((row >> 4) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
   return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
 }
 template <int D>
