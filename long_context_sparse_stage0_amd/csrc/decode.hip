@@ -16,8 +16,10 @@
 //   k_decode_attend  split-K: the active chunks of (b, kv head) plus the partial diagonal
 //                    chunk form a list; all lists are cut into segments of one common
 //                    size, as many as keep every workgroup slot of the GPU busy in one
-//                    round, so that long and short lists are balanced; each of a
-//                    workgroup's 4 waves takes every fourth item of its segment.  S^T = K Q^T with K rows
+//                    round, so that long and short lists are balanced; the work unit is
+//                    a 32-key half item, so a segment splits over the workgroup's 4 waves
+//                    to within half an item (waves 2i and 2i + 1 take the two halves of
+//                    every second item, starting at item i).  S^T = K Q^T with K rows
 //                    loaded straight from global as MFMA operands, V staged through
 //                    wave-private LDS in [d][key] order for the V^T P^T product; the waves'
 //                    (max, sum, O) partials are merged in LDS and written once per
@@ -384,8 +386,8 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   constexpr int KS = D / 32, NDT = D / 16;
   constexpr int VP = D + 16;                      // V row pitch in LDS (bf16 elements)
   constexpr int SEGR = D / 8;                     // 16-byte segments per V row
-  constexpr int VL = 64 * SEGR / 64;              // segments per lane per tile
-  __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][64 * VP];
+  constexpr int VL = 32 * SEGR / 64;              // segments per lane per half tile
+  __shared__ __attribute__((aligned(16))) bf16 vts[kAttWaves][32 * VP];
   __shared__ float mrg_ml[kAttWaves][2][16];
 
   const int G = a.Hq / a.Hkv;
@@ -449,12 +451,16 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
   const int per = smap[3];
   const int lo = seg * per;
   const int nitems = min(per, ntot - lo);
-  // wave wv takes items lo + wv + kAttWaves j; lane j of myc holds the chunk of item j
-  const int nmy = max(0, (nitems - wv + kAttWaves - 1) / kAttWaves);
-  const int32_t* myl = lst + 1 + lo + wv;
-  const int myc = lane < nmy ? myl[kAttWaves * lane] : it;
+  // The work unit is a 32-key half of an item, so that the segment's work splits over the
+  // waves to within half an item: wave wv takes half hp = wv & 1 (keys 32 hp .. 32 hp + 31)
+  // of the items lo + wv / 2 + 2 j; lane j of myc holds the chunk of its item j.
+  static_assert(kAttWaves == 4, "two waves per half-item column");
+  const int hp = wv & 1;
+  const int nmy = max(0, (nitems - (wv >> 1) + 1) / 2);
+  const int32_t* myl = lst + 1 + lo + (wv >> 1);
+  const int myc = lane < nmy ? myl[2 * lane] : it;
   auto chunk_of = [&](int j) {
-    return j < 64 ? __builtin_amdgcn_readlane(myc, j) : myl[kAttWaves * j];
+    return j < 64 ? __builtin_amdgcn_readlane(myc, j) : myl[2 * j];
   };
   // paged caches: the page of each of those chunks (-1 past the list)
   const int32_t* btab = a.block_table ? a.block_table + (size_t)b * a.bt_ld : nullptr;
@@ -483,17 +489,19 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // registers for one item: K operands (A of S^T) and this lane's V segments, fetched
-  // through buffer descriptors whose range ends at the item's last valid key (t on the
-  // diagonal), so keys past it read as zeros without branches
-  bf16x8 kop[4][KS];
+  // registers for one half-item: K operands (A of S^T, key tiles 2 hp and 2 hp + 1) and
+  // this lane's V segments of the half, fetched through buffer descriptors whose range ends
+  // at the item's last valid key (t on the diagonal), so keys past it read as zeros without
+  // branches
+  bf16x8 kop[2][KS];
   uint4 vseg[VL];
-  int koff[4];
+  int koff[2];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int key = 32 * (kt >> 1) + 8 * (l16 >> 2) + 4 * (kt & 1) + (l16 & 3);
-    koff[kt] = (key * D + 8 * lg) * 2;
+  for (int h = 0; h < 2; ++h) {
+    const int key = 32 * hp + 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+    koff[h] = (key * D + 8 * lg) * 2;
   }
+  const int voff0 = 32 * hp * SEGR * 16;          // byte offset of the half's first V row
   // a chunk's K and V rows: contiguous caches index by chunk, paged ones by page; a page id
   // outside the pool gives an empty range, so its keys and values read as zeros
   auto load_item = [&](int j) {
@@ -514,15 +522,15 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)vp, (short)0, nkeys * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kop[kt][ks] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[kt] + 64 * ks, 0, 0));
+        kop[h][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, koff[h] + 64 * ks, 0, 0));
 #pragma unroll
     for (int i = 0; i < VL; ++i)
       vseg[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, (i * 64 + lane) * 16, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff0 + (i * 64 + lane) * 16, 0, 0));
   };
 
   if (nmy > 0) load_item(0);
@@ -534,7 +542,7 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     const int c = chunk_of(j);
     const bool diag = c == it;
     const int kmax = diag ? t : c * kChunk + 63;
-    // V rows -> LDS (row-major, padded)
+    // the half's V rows -> LDS (row-major, padded)
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
       const int sg = i * 64 + lane;
@@ -544,13 +552,13 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     // wait for these stores before the transposing LDS reads below: unlike ordinary LDS
     // reads they are not ordered behind the wave's outstanding LDS writes
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // S^T = K Q^T
-    floatx4 s[4];
+    // S^T = K Q^T over the half's 32 keys
+    floatx4 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      s[h] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kt] = mfma16(kop[kt][ks], qop[ks], s[kt]);
+      for (int ks = 0; ks < KS; ++ks) s[h] = mfma16(kop[h][ks], qop[ks], s[h]);
     }
     const float bias = j < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mybias), j))
                               : (diag ? 0.f : a.sigma * fast_log2(a.wbar[(size_t)bk * a.wbar_ld + c]));
@@ -559,32 +567,32 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
     // online softmax against the reference max m, which is only raised (with the rescale
     // of O and l) when a lane's partial probability sum exceeds kSumCap; keys past the
     // query are masked on the diagonal item only
-    float x[16];
+    float x[8];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) x[4 * kt + jj] = s[kt][jj];
+      for (int jj = 0; jj < 4; ++jj) x[4 * h + jj] = s[h][jj];
     if (diag) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int key = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1) + jj;
-          if (c * kChunk + key > kmax) x[4 * kt + jj] = -INFINITY;
+          const int key = 32 * hp + 8 * lg + 4 * h + jj;
+          if (c * kChunk + key > kmax) x[4 * h + jj] = -INFINITY;
         }
     }
     float off = bias - m;
     float ps = 0.f;
-    float pr[16];
+    float pr[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       pr[i] = fast_exp2(fmaf(x[i], sl2, off));
       ps += pr[i];
     }
     if (__builtin_amdgcn_ballot_w64(!(ps <= kSumCap)) != 0ull) {
       float mx = x[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
       mx = xg_max(mx);
       const float mn = fmaxf(m, fmaf(mx, sl2, bias));
       const float corr = fast_exp2(m - mn);
@@ -595,26 +603,19 @@ void k_decode_attend(AttendArgs a, float* __restrict__ pml, float* __restrict__ 
       off = bias - mn;
       ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 8; ++i) {
         pr[i] = fast_exp2(fmaf(x[i], sl2, off));
         ps += pr[i];
       }
     }
     lsum += ps;
-    bf16x8 pop[2];
+    // P^T operand of the half (k-slot i <-> key 32 hp + 8 lg + i)
+    bf16x8 pop;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int i = 0; i < 8; ++i) pop[i] = (bf16)pr[i];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        pop[p][jj] = (bf16)pr[8 * p + jj];
-        pop[p][4 + jj] = (bf16)pr[8 * p + 4 + jj];
-      }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        o[dt] = mfma16(vt_operand(vl, VP, 32 * p + 8 * lg, 16 * dt, l16), pop[p], o[dt]);
-    }
+    for (int dt = 0; dt < NDT; ++dt)
+      o[dt] = mfma16(vt_operand(vl, VP, 8 * lg, 16 * dt, l16), pop, o[dt]);
     asm volatile("" ::: "memory");  // the next item's stores stay after these reads
   }
   // merge the waves' partials: (m, l) per query column, then O rescaled and summed in LDS
