@@ -195,3 +195,29 @@ def test_prior_strength_is_a_power_of_the_multiplicity(sigma):
     wt = wt * e[: t + 1]
     ref = (wt[:, None] * v[: t + 1]).sum(0) / wt.sum()
     np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_zero_fraction_counts_routed_pairs_only():
+    """zero_fraction: the share of (row, kv head, chunk c < t // 64) entries whose weight is
+    exactly 0.  Hand-built weights with a known answer: row 0 routes nothing, row 64 routes
+    chunk 0 only, row 200 routes chunks 0..2; the own chunk and everything past it (set to 0
+    here on purpose) must not be counted."""
+    rows = np.array([0, 64, 200])
+    wb = np.full((1, 2, 3, 5), 0.25)
+    wb[0, 0, 1, 0] = 0.0          # row 64, head 0: its one routed chunk is inactive
+    wb[0, 1, 2, 1] = 0.0          # row 200, head 1: chunk 1 inactive
+    wb[0, 0, 2, 3:] = 0.0         # row 200: own chunk 3 and chunk 4 are outside the count
+    wb[0, :, 0, :] = 0.0          # row 0 routes no chunk at all
+    # routed entries: 2 heads x (1 + 3) = 8, of which 2 are zero
+    assert O.zero_fraction(wb, rows) == pytest.approx(2 / 8, abs=0)
+    # every routed entry zero -> 1; no routed entry at all -> 0
+    assert O.zero_fraction(np.zeros_like(wb), rows) == 1.0
+    assert O.zero_fraction(wb[:, :, :1], rows[:1]) == 0.0
+    # brute force over random sparsity patterns, counted a different way
+    rng = np.random.default_rng(3)
+    t = np.sort(rng.choice(np.arange(1024), size=40, replace=False))
+    w = rng.random((2, 3, t.size, 16)) * (rng.random((2, 3, t.size, 16)) < 0.6)
+    routed = np.arange(16)[None, :] < (t // 64)[:, None]           # [rows, chunks]
+    zeros = ((w == 0.0) & routed[None, None]).sum()
+    total = routed.sum() * 2 * 3
+    assert O.zero_fraction(w, t) == pytest.approx(zeros / total, rel=0, abs=1e-15)
