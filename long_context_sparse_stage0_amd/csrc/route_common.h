@@ -42,6 +42,19 @@ struct WaveReduce {
   __device__ __forceinline__ float max(float v) const { return wave_max(v); }
 };
 
+// smallest unsigned value over the wave (DPP steps inside each 16-lane row, then the row
+// swaps); used on the bit patterns of non-negative floats, which order like the floats
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = ::min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = ::min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = ::min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = ::min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = ::min(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return ::min(b[0], b[1]);
+}
+
 // Start point from the first pass's moments (own design, alpha = 1.5).  With the scores
 // modelled as Gaussian with the mean and variance v of the current support (n entries),
 // sum_c [y_c - tau]_+^2 at tau = mean + a sqrt(v) is n v g(a), g(a) = E[(Z - a)_+^2]
@@ -115,30 +128,45 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
     }
   }
   for (int it = 0; it < 96; ++it) {
-    float s1 = 0.f, s2 = 0.f, mn = INFINITY;
-    int icnt = 0;
+    float s1 = 0.f, s2 = 0.f, mn = INFINITY, cnt;
+    if constexpr (MODE == kAlpha15 || MODE == kAlpha2) {
+      // branch-free: entries outside the support add +0 (and fma(0, 0, s2) = s2), the
+      // count is the popcount of the wave's comparison mask, and the support's smallest
+      // excess is an unsigned min over the bit patterns (positive floats order like them)
+      uint32_t mnb = 0x7f800000u;                   // +inf
+      int cw = 0;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float d = y[r] - tau;
-      if (d > 0.f) {
-        ++icnt;
-        mn = fminf(mn, d);
-        if (MODE == kAlpha15) {
-          s1 += d;
-          s2 = fmaf(d, d, s2);
-        } else if (MODE == kAlpha2) {
-          s1 += d;
-        } else {
+      for (int r = 0; r < NR; ++r) {
+        const float d = y[r] - tau;
+        const bool in = d > 0.f;
+        cw += __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
+        const float dp = in ? d : 0.f;
+        s1 += dp;
+        if (MODE == kAlpha15) s2 = fmaf(dp, dp, s2);
+        mnb = ::min(mnb, in ? __float_as_uint(d) : 0x7f800000u);
+      }
+      cnt = (float)cw;
+      s1 = red.sum(s1);
+      if (MODE == kAlpha15) s2 = red.sum(s2);
+      mn = __uint_as_float(wave_umin(mnb));
+    } else {
+      int icnt = 0;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float d = y[r] - tau;
+        if (d > 0.f) {
+          ++icnt;
+          mn = fminf(mn, d);
           const float dp1 = pow_pos(d, inv - 1.0f);  // d^(p-1)
           s1 += dp1;                                 // for F'
           s2 = fmaf(dp1, d, s2);                     // d^p, for F
         }
       }
+      cnt = red.sum((float)icnt);
+      s1 = red.sum(s1);
+      s2 = red.sum(s2);
+      mn = red.min(mn);
     }
-    const float cnt = red.sum((float)icnt);
-    s1 = red.sum(s1);
-    if (MODE != kAlpha2) s2 = red.sum(s2);
-    mn = red.min(mn);
     if (MODE == kAlpha2) {
       const float delta = (s1 - 1.0f) / cnt;
       if (delta < mn) {
