@@ -269,10 +269,21 @@ __global__ __launch_bounds__(1024) void k_decode_route(RouteArgs a) {
     float z;
     const float tau = entmax_threshold<MODE, NRU>(y, nent, a.alpha, WaveReduce(), &z);
     const float rz = 1.0f / z, inv = 1.0f / (a.alpha - 1.0f);
+    // every slot is stored (LDS columns up to 64 NRU <= kMaxRouted exist); the GQA sum reads
+    // only chunks below i_t, so the own chunk's estimate_diagonal entry is never used
 #pragma unroll
     for (int r = 0; r < NRU; ++r) {
       const int c = lane + 64 * r;
-      if (c < it) sc[wv * ld + c] = entmax_weight<MODE>(y[r], tau, inv, rz);
+      float wgt;
+      if constexpr (MODE == kAlpha15) {
+        const float d = fmaxf(y[r] - tau, 0.f);
+        wgt = (d * d) * rz;
+      } else if constexpr (MODE == kAlpha2) {
+        wgt = fmaxf(y[r] - tau, 0.f) * rz;
+      } else {
+        wgt = entmax_weight<MODE>(y[r], tau, inv, rz);
+      }
+      sc[wv * ld + c] = wgt;
     }
     }
   };

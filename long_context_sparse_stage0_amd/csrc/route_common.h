@@ -202,7 +202,14 @@ __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, cons
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const float d = y[r] - tau;
-    if (d > 0.f) z += (MODE == kAlpha15) ? d * d : (MODE == kAlpha2 ? d : pow_pos(d, inv));
+    if constexpr (MODE == kAlpha15) {
+      const float dp = d > 0.f ? d : 0.f;        // +0 outside the support
+      z += dp * dp;
+    } else if constexpr (MODE == kAlpha2) {
+      z += d > 0.f ? d : 0.f;
+    } else {
+      if (d > 0.f) z += pow_pos(d, inv);
+    }
   }
   *zsum = red.sum(z);
   return tau;
