@@ -91,6 +91,8 @@ constexpr float kEntmaxModelTarget = 1.25f;
 
 // y[NR]: this lane's scores ((alpha-1)-scaled), -inf for absent entries.
 // Returns tau; *zsum receives sum_c [y_c - tau]_+^(1/(alpha-1)) (the normaliser).
+// Called with every lane of the wave active: the reductions and the support count (a popcount
+// of the wave's comparison mask) span all 64 lanes.
 template <int MODE, int NR, class Red>
 __device__ float entmax_threshold(const float (&y)[NR], int n, float alpha, const Red& red,
                                   float* zsum) {
