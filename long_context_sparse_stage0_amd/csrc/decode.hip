@@ -78,30 +78,33 @@ __global__ __launch_bounds__(256) void k_decode_scores(RouteArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv;
-  const int t = a.seq_lens[b] - 1;
-  const bool valid = t >= 0 && t < a.tcap;
-  const int it = valid ? t / kChunk : 0;
   const int ct = blockIdx.x * 4 + wv;              // this wave's tile of 16 chunks
-  if (16 * ct >= it) return;                       // (whole wave)
+  // the sequence length, the queries and the tile's summary rows are loaded together: no
+  // address depends on the length (rows are clamped to the cache), only which results count
+  const int slen = a.seq_lens[b];
   bf16x8 qop[KS];
+  const bool qok = l16 < G;
   {
-    const bool qok = l16 < G;
     const bf16* qp = (const bf16*)a.q + ((size_t)b * a.Hq + kvh * G + (qok ? l16 : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
-      qop[ks] = qok ? v : bf16x8{};
-    }
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks + 8 * lg);
   }
   const int crow = 16 * ct + l16;
-  const bool cok = crow < it;
-  const float* srow = a.summ + ((size_t)bk * a.nc_alloc + (cok ? crow : 0)) * D;
+  const float* srow = a.summ + ((size_t)bk * a.nc_alloc + min(crow, a.nc_alloc - 1)) * D;
   float4 xr[2 * KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     xr[2 * ks] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg);
     xr[2 * ks + 1] = *reinterpret_cast<const float4*>(srow + 32 * ks + 8 * lg + 4);
   }
+  const int t = slen - 1;
+  const bool valid = t >= 0 && t < a.tcap;
+  const int it = valid ? t / kChunk : 0;
+  if (16 * ct >= it) return;                       // (whole wave)
+  const bool cok = crow < it;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    if (!qok) qop[ks] = bf16x8{};
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
